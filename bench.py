@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of one sigmoid-routed int4 x Q8_0 MoE layer on one MI355X.
+
+Default workload: GLM-5.2-shaped decode at batch 1 (1 token per step, hidden
+6144, 256 routed experts, top-8, one shared expert, intermediate 2048). A
+step is one full coli_moe_forward: Q8_0(x), router + top-k, bucketing,
+gate/up + SwiGLU + requant, down, weighted combine. Every step uses a new
+seeded token and the next of R layer replicas (distinct seeded weights), so
+the 256 MB Infinity Cache never serves a previous step's weights.
+
+Prints one JSON line (see the fields below). Options: --config picks another
+workload (0 tiny, 1 decode, 2 MTP verify T=3, 3 prefill T=512); --gpus must
+be 1 (this build runs on one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="time budget of the oracle CPU-baseline sample (0 = skip)")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the layer is not sharded "
+                                   "across GPUs (use --gpus 1)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import coli_synth as cs
+    import int4_quantized_moe_sigmoid_amd as C
+
+    torch.cuda.set_device(0)
+    cfg = cs.CONFIGS[args.config]
+    if cfg.n_layers > 1:
+        print(json.dumps({"error": "the layer-stack workload has its own script path; "
+                                   "use --config 0..3"}))
+        sys.exit(2)
+    T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho)
+    R = max(1, args.replicas)
+    n_steps, n_warm = args.steps, args.warmup
+    n_inputs = n_steps + n_warm
+
+    t_setup = time.time()
+    pack = lambda w, qv, sv: C.coli_pack_int4(w, qv, sv)
+    layers = []
+    for r in range(R):
+        wr, b, q, s = cs.build_layer(cfg, r, "cuda", pack)
+        layers.append(C.LayerWeights(lc, wr, b, q, s))
+        print(f"[bench] replica {r} packed ({(q.numel() + 4 * s.numel()) / 1e9:.2f} GB)",
+              file=sys.stderr, flush=True)
+    # distinct seeded inputs for every step, RMS-normalised on the GPU when the
+    # workload's input is normalised
+    xs = []
+    for i in range(n_inputs):
+        raw = cs.activations(cfg, i % R, "cuda", n_tok=T, first_tok=(i // R) * T)
+        if cfg.rmsnorm_input:
+            xn = torch.empty_like(raw)
+            C.coli_rmsnorm(raw, xn, 1e-5)
+            raw = xn
+        xs.append(raw)
+    ys = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in range(2)]
+    ws = torch.empty(C.coli_moe_workspace_bytes(lc, T), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    def step(i):
+        C.coli_moe_forward(layers[i % R], xs[i], ys[i & 1], ws)
+
+    for i in range(n_warm):
+        step(n_steps + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / n_steps
+    tok_s = T * n_steps / elapsed
+
+    # bytes that must cross HBM per step: unique experts' packed weights + scales,
+    # the router weight, activations in and out
+    lay = C.coli_moe_workspace_layout(lc, T, 0)
+    eb = 3 * I * H // 2 + 4 * (2 * I + H)
+
+    # ---- per-kernel durations with HIP events on the same stream -------------
+    kern = {}
+    unique_counts = []
+    if not args.no_profile:
+        names = None
+        nev = 16
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
+        for e in evs:
+            e.record()
+        torch.cuda.synchronize()
+        handles = [e.cuda_event for e in evs]
+        sums = {}
+        n_prof = n_steps
+        counts_view = ws[lay.counts:lay.counts + 4 * (E + S)].view(torch.int32)
+        for i in range(n_prof):
+            names = C.coli_moe_forward_profiled(layers[i % R], xs[i], ys[i & 1], ws, handles)
+            torch.cuda.synchronize()
+            for j in range(len(names) - 1):
+                sums[names[j]] = sums.get(names[j], 0.0) + evs[j].elapsed_time(evs[j + 1])
+            unique_counts.append(int((counts_view[:E] > 0).sum().item()) + S)
+        kern = {k: v / n_prof for k, v in sums.items()}
+    uniq_avg = float(np.mean(unique_counts)) if unique_counts else float(min(E, T * K) + S)
+
+    gate_up_bytes = uniq_avg * (2 * I * H // 2 + 4 * 2 * I) + T * (H + H // 8) + \
+        T * (K + S) * (I + I // 8)
+    down_bytes = uniq_avg * (I * H // 2 + 4 * H) + T * (K + S) * (I + I // 8 + 4 * H)
+    step_bytes = uniq_avg * eb + 4 * E * H + 4 * E + 8 * T * H
+    weight_gbps = uniq_avg * eb / (ms_per_step * 1e-3) / 1e9
+
+    roofline = None
+    if "gateup" in kern:
+        ms = kern["gateup"]
+        ach = gate_up_bytes / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "kernel": "k_gateup_gemv", "bytes_per_launch": int(gate_up_bytes),
+                    "avg_launch_us": round(ms * 1e3, 2)}
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(cfg, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE-layer tokens/s; decode int4 expert-weight GB/s as % of HBM peak",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": n_warm, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int4xint8 (int32 block dots, f64 scales)",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights packed by coli_pack_int4)",
+        "config": {"workload": cfg.name, "tokens_per_step": T, "hidden": H, "inter": I,
+                   "n_experts": E, "top_k": K, "n_shared": S, "weight_replicas": R,
+                   "parallelism": "none (1 GPU)"},
+        "expert_weight_gbps": round(weight_gbps, 1),
+        "expert_weight_frac_hbm": round(weight_gbps / HBM_PEAK_GBPS, 4),
+        "unique_experts_per_step": round(uniq_avg, 2),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle (plain C++ CPU reference, fp64) on a bounded sample of the
+    same workload: tokens of replica 0, one forward per token, until the time
+    budget is spent. Expert fp32 weights are drawn by coli_synth (on the GPU for
+    speed; the draw is bit-identical to the CPU draw) and packed by the oracle."""
+    import numpy as np
+    import torch
+
+    import coli_synth as cs
+    import oracle
+
+    H, I = cfg.hidden, cfg.inter
+    wr, b = cs.router(cfg, 0, "cpu")
+    wr, b = wr.numpy(), b.numpy()
+    OL = oracle.OracleLayer(H, I, cfg.n_experts, cfg.top_k, cfg.n_shared, cfg.norm_topk,
+                            cfg.rho, wr, b, {})
+    timed = 0.0
+    n_tok = 0
+    while timed < budget_s and n_tok < 4096:
+        x = cs.activations(cfg, 0, "cpu", n_tok=cfg.n_tok, first_tok=n_tok).numpy()
+        if cfg.rmsnorm_input:
+            x = oracle.rmsnorm(x, float(np.float32(1e-5)))
+        idx, _, _ = oracle.route(x, wr, b, cfg.top_k, cfg.norm_topk, cfg.rho)
+        need = set(int(e) for e in np.unique(idx)) | ({cfg.n_experts} if cfg.n_shared else set())
+        for e in sorted(need - set(OL.experts)):
+            OL.add_expert(e, oracle.pack_expert(*[cs.expert_matrix(cfg, 0, e, m, "cuda").cpu().numpy()
+                                                  for m in ("gate", "up", "down")]))
+        t0 = time.perf_counter()
+        OL.forward(x)
+        timed += time.perf_counter() - t0
+        n_tok += cfg.n_tok
+    return {"value": round(n_tok / timed, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n_tok} tokens of {cfg.name}, replica 0, one oracle forward per "
+                      f"{cfg.n_tok} token(s), {timed:.1f} s timed"}
+
+
+if __name__ == "__main__":
+    main()

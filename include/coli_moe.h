@@ -1,0 +1,204 @@
+/*
+ * coli_moe.h — C ABI of the MI355X (gfx950) library for one sigmoid-routed
+ * Mixture-of-Experts layer with symmetric int4 expert weights and Q8_0 int8
+ * activations.
+ *
+ * The operation comes from the pages on the colibri engine for GLM-5.2:
+ *  - wmrh.cn, "GLM-5.2-colibri-int4架构解析MoE专家混合与INT4量化原理",
+ *    section "GLM-5.2的MoE实现": 256 routed experts, 1 shared expert, 8
+ *    experts per token, hidden size 6144, expert intermediate size 2048;
+ *    section "MoE的工作原理": every token gets router scores, the 8
+ *    highest-scoring experts run and their outputs are summed weighted by
+ *    score; section "量化流程": weights go FP8 -> F32 -> int4 with np.rint
+ *    (chosen to agree with the engine's lrintf), one F32 scale per weight
+ *    row, 4-bit values packed into U8; section "路由策略定制": the knobs
+ *    topk_method, routed_scaling_factor and norm_topk_prob.
+ *  - "Colibri：在笔记本上跑744B参数的AI模型", feature list (关键特性): a
+ *    DeepSeek-V3-style sigmoid router with a shared expert; an integer dot
+ *    kernel over Q8_0-style int8 activations.
+ *  - hn mirror (hn.213312.xyz) of the project summary, feature list: in a
+ *    batch an expert needed by several positions is read once and shared.
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers owned by the caller, row-major and
+ *    contiguous, 16-byte aligned (else COLI_E_ALIGN). The library never
+ *    allocates, frees or keeps them.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *    Every call only enqueues work on that stream: it neither allocates nor
+ *    synchronises, and results are ready when the stream reaches them.
+ *  - Calls return COLI_OK (0) or a negative code; arguments are checked on
+ *    the host before anything is launched, so a rejected call has no effect.
+ *    A call with zero rows/tokens is a no-op and may pass NULL data pointers
+ *    (shape and config arguments are still checked).
+ *    COLI_E_HIP reports a launch failure from the HIP runtime.
+ *  - The library keeps no state between calls; concurrent calls are safe
+ *    when they use different workspaces (calls sharing one workspace must be
+ *    ordered, e.g. on one stream).
+ */
+#ifndef COLI_MOE_H
+#define COLI_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COLI_API __attribute__((visibility("default")))
+
+#define COLI_OK 0
+#define COLI_E_INVAL (-1)       /* null pointer, bad size, dim % 32 != 0, K > E, K > 16 ... */
+#define COLI_E_ALIGN (-2)       /* a pointer is not 16-byte aligned */
+#define COLI_E_WORKSPACE (-3)   /* ws_bytes smaller than coli_moe_workspace_bytes() */
+#define COLI_E_HIP (-4)         /* the HIP runtime rejected a launch */
+#define COLI_E_UNSUPPORTED (-5) /* a size beyond the compiled limits */
+
+/* coli_moe_forward flags */
+#define COLI_FWD_ACCUM 1u      /* y += layer(x) (residual add in fp32) instead of y = layer(x) */
+#define COLI_FWD_DEBUG_TAPS 2u /* also store per-block int32 dots of the gate rows in ws */
+
+/* Layer shape and routing knobs (the knob names follow the model's
+ * config.json fields named on the wmrh.cn page, section 路由策略定制). */
+typedef struct coli_moe_cfg {
+    int32_t hidden;       /* H, multiple of 32, <= 8192 */
+    int32_t inter;        /* I, expert intermediate size, multiple of 32, <= 8192 */
+    int32_t n_experts;    /* E routed experts, 1..1024 */
+    int32_t top_k;        /* K experts per token, 1..min(E, 16) */
+    int32_t n_shared;     /* 0 or 1 shared expert (stored after the routed ones) */
+    int32_t norm_topk;    /* norm_topk_prob: 1 = divide the K gate values by their sum */
+    float routed_scale;   /* routed_scaling_factor rho, applied after normalisation */
+    int32_t reserved;     /* must be 0 */
+} coli_moe_cfg;
+
+/* Weights of one layer (all device memory, owned by the caller).
+ *  w_router      [E, H] fp32 router weight (kept in F32, not quantised)
+ *  bias          [E] fp32 correction bias: added to the sigmoid score for
+ *                expert selection only; the gate value is the unbiased score
+ *  experts_q     E + n_shared contiguous expert blobs of 3*I*H/2 bytes, blob e =
+ *                [gate I x H/2 | up I x H/2 | down H x I/2], rows = output
+ *                channels, byte j of a row = code(2j) | code(2j+1) << 4 with
+ *                4-bit two's complement codes in -7..7 (coli_pack_int4 format);
+ *                the shared expert is blob E. One blob is the unit the engine
+ *                reads with a single pread (devtrends.cc page, section
+ *                引擎是如何工作的).
+ *  experts_scale E + n_shared blobs of 2*I + H fp32 row scales:
+ *                [gate I | up I | down H].
+ */
+typedef struct coli_moe_weights {
+    coli_moe_cfg cfg;
+    const float* w_router;
+    const float* bias;
+    const uint8_t* experts_q;
+    const float* experts_scale;
+} coli_moe_weights;
+
+/* Where the intermediates of one forward live inside the workspace (byte
+ * offsets from ws). Slot s indexes the (token, expert) assignments in
+ * expert-bucketed order; tokens of one expert occupy consecutive slots in
+ * ascending token order, experts in ascending id order, the shared expert last.
+ *   qx     [T, H] int8 Q8_0 codes of x, each group of 8 stored as
+ *          (e0,e2,e4,e6,e1,e3,e5,e7)
+ *   dx     [T, H/32] fp32 block scales of x
+ *   logits [T, E] fp64 router logits
+ *   topk_idx [T, K] int32, topk_w [T, K] fp32
+ *   counts [E + S] int32 tokens per expert, offs [E + S + 1] int32 first slot
+ *   slot_of [T, K + S] int32 slot of (t, k) (k == K: shared expert)
+ *   slot_tok [T*(K+S)] int32 token of each slot
+ *   qh     [T*(K+S), I] int8 Q8_0 codes of the SwiGLU output h (same 8-group order)
+ *   dh     [T*(K+S), I/32] fp32
+ *   ye     [T*(K+S), H] fp32 expert outputs (only written when T is above the
+ *          decode path's token limit)
+ *   tap    [T*(K+S), tap_rows, H/32] int32 gate-row block dots of rows
+ *          r = i * tap_stride (COLI_FWD_DEBUG_TAPS only)
+ */
+typedef struct coli_moe_ws_layout {
+    size_t total;
+    size_t qx, dx, logits, topk_idx, topk_w, counts, offs, slot_of, slot_tok, qh, dh, ye, tap;
+    int64_t n_slots, tap_rows, tap_stride;
+    size_t reserved[4];
+} coli_moe_ws_layout;
+
+/* Message for a return code (static string, never NULL). */
+COLI_API const char* coli_strerror(int code);
+
+/* Pack an fp32 matrix [rows, cols] into symmetric int4 (wmrh.cn page,
+ * section 量化流程): per row s = fp32(max|w|/7); code = clamp(rint(w/s), -7, 7)
+ * with round-half-to-even and IEEE division; s == 0 gives code 0; byte j of
+ * a row = code(2j) & 0xF | (code(2j+1) & 0xF) << 4.
+ *   w [rows, cols] fp32 (in), q [rows, cols/2] u8 (out), scale [rows] fp32 (out).
+ * cols must be a positive multiple of 32, rows >= 0 (0: no-op).
+ * Result is bit-exact with the plain definition above. */
+COLI_API int coli_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q,
+                            float* scale, void* stream);
+
+/* Q8_0 quantisation of activations ("Colibri：在笔记本上跑744B参数的AI模型",
+ * 关键特性: Q8_0-style int8 activations): per block of 32 consecutive
+ * elements d = fp32(max|x|/127), q = clamp(rint(x/d), -127, 127), d == 0
+ * gives q = 0.
+ *   x [n_tok, dim] fp32 (in), q [n_tok, dim] int8 (out, plain element order),
+ *   d [n_tok, dim/32] fp32 (out). dim must be a positive multiple of 32. */
+COLI_API int coli_quant_q8(const float* x, int64_t n_tok, int64_t dim, int8_t* q, float* d,
+                           void* stream);
+
+/* Bytes of workspace that coli_moe_route / coli_moe_forward need for up to
+ * max_tok tokens with the given flags; 0 if cfg is invalid. */
+COLI_API size_t coli_moe_workspace_bytes(const coli_moe_cfg* cfg, int64_t max_tok,
+                                         uint32_t flags);
+
+/* Offsets of the intermediates inside a workspace for n_tok tokens. */
+COLI_API int coli_moe_workspace_layout(const coli_moe_cfg* cfg, int64_t n_tok, uint32_t flags,
+                                       coli_moe_ws_layout* out);
+
+/* Sigmoid router with correction bias and top-k (wmrh.cn page, sections
+ * MoE的工作原理 and 路由策略定制; Colibri page, 关键特性):
+ *   l = x . w_router^T (accumulated in fp64), s = 1/(1+exp(-l)), c = s + bias;
+ *   the K largest c in descending order, ties to the lower expert index;
+ *   w_k = s[e_k], divided by sum_k s[e_k] when cfg->norm_topk, times
+ *   cfg->routed_scale, rounded to fp32.
+ *   x [n_tok, H] fp32, w_router [E, H], bias [E] (in); topk_idx [n_tok, K]
+ *   int32 and topk_w [n_tok, K] fp32 (out); ws: workspace of at least
+ *   coli_moe_workspace_bytes(cfg, n_tok, 0) bytes. */
+COLI_API int coli_moe_route(const float* x, const float* w_router, const float* bias,
+                            int64_t n_tok, const coli_moe_cfg* cfg, int32_t* topk_idx,
+                            float* topk_w, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer on n_tok tokens (pages as above):
+ *   route (as coli_moe_route); q_x, d_x = Q8_0(x);
+ *   for every selected expert e of token t and for the shared expert:
+ *     g_r = fp32(s_gate[r] * sum_b d_x,b * I_b) with I_b the exact int32 dot
+ *           of block b of gate row r with q_x (sum in fp64), u_r likewise,
+ *     h_r = fp32(silu(g_r) * u_r), silu(z) = z/(1+exp(-z)) in fp64,
+ *     q_h, d_h = Q8_0(h),
+ *     y_e,c = fp32(s_down[c] * sum_b d_h,b * I_b(down row c));
+ *   y_t = fp32(sum_k w_k * y_e_k + y_shared) in fp64 (shared weight 1).
+ * Tokens that share an expert read its weights once (bucketing).
+ *   w: layer weights; x [n_tok, H] fp32 (the normalised layer input);
+ *   y [n_tok, H] fp32 (out; with COLI_FWD_ACCUM y = y + fp32(layer)).
+ *   ws/ws_bytes: workspace (see coli_moe_workspace_bytes), overwritten.
+ * n_tok == 0 is a no-op. */
+COLI_API int coli_moe_forward(const coli_moe_weights* w, const float* x, int64_t n_tok,
+                              float* y, void* ws, size_t ws_bytes, uint32_t flags,
+                              void* stream);
+
+/* As coli_moe_forward, and additionally records the HIP events events[0..n-1]
+ * (hipEvent_t passed as void*) on the stream before each kernel launch of the
+ * forward and after the last one. Returns the number of launch boundaries in
+ * *n_used (kernels + 1); events beyond n_events are not recorded. For timing
+ * single kernels; results are identical to coli_moe_forward. */
+COLI_API int coli_moe_forward_profiled(const coli_moe_weights* w, const float* x,
+                                       int64_t n_tok, float* y, void* ws, size_t ws_bytes,
+                                       uint32_t flags, void* stream, void* const* events,
+                                       int n_events, int* n_used, const char** names);
+
+/* RMSNorm with unit gain (the pre-norm between stacked layers):
+ *   out = fp32(x / sqrt(mean(x^2) + eps)), computed in fp64.
+ *   x [n_tok, dim] fp32 (in), out [n_tok, dim] fp32 (out, may alias x). */
+COLI_API int coli_rmsnorm(const float* x, int64_t n_tok, int64_t dim, float eps, float* out,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLI_MOE_H */

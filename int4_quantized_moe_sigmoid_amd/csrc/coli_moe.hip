@@ -1,0 +1,380 @@
+// Host side of the C ABI (include/coli_moe.h): argument checks, workspace
+// layout, kernel selection and launches. No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "coli_moe.h"
+#include "coli_common.h"
+#include "k_gemv.h"
+#include "k_route.h"
+#include "k_small.h"
+
+namespace {
+
+constexpr int kMaxHidden = 8192;  // 4 blocks of 64 per lane in the GEMV kernels
+constexpr int kMaxInter = 8192;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 16;
+constexpr int kGemvChunk = 4;     // tokens per item on the GEMV path
+constexpr int64_t kTapBudget = 1ll << 24;  // int32 entries of the block-dot tap
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_cfg(const coli_moe_cfg* c) {
+    if (!c) return COLI_E_INVAL;
+    if (c->hidden <= 0 || c->hidden % 32 || c->inter <= 0 || c->inter % 32) return COLI_E_INVAL;
+    if (c->n_experts <= 0 || c->top_k <= 0 || c->top_k > c->n_experts) return COLI_E_INVAL;
+    if (c->n_shared < 0 || c->n_shared > 1) return COLI_E_INVAL;
+    if (!std::isfinite(c->routed_scale)) return COLI_E_INVAL;
+    if (c->hidden > kMaxHidden || c->inter > kMaxInter || c->n_experts > kMaxExperts ||
+        c->top_k > kMaxTopK)
+        return COLI_E_UNSUPPORTED;
+    return COLI_OK;
+}
+
+struct Layout {
+    coli_moe_ws_layout pub;
+    size_t lists, items, n_items;
+    int64_t max_items;
+    int ch;
+};
+
+int64_t max_items_for(const coli_moe_cfg& c, int64_t T, int ch) {
+    const int64_t TK = T * c.top_k;
+    const int64_t routed = (TK < c.n_experts ? TK : c.n_experts) + TK / ch;
+    const int64_t shared = c.n_shared ? (T + ch - 1) / ch : 0;
+    return routed + shared;
+}
+
+void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
+    const int64_t H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, S = c.n_shared;
+    const int64_t NE = E + S, KS = K + S, NS = T * KS;
+    std::memset(L, 0, sizeof(*L));
+    L->ch = kGemvChunk;
+    L->max_items = max_items_for(c, T, L->ch);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    coli_moe_ws_layout& P = L->pub;
+    P.n_slots = NS;
+    P.qx = take(T * H);
+    P.dx = take(T * (H / 32) * 4);
+    P.logits = take(T * E * 8);
+    P.topk_idx = take(T * K * 4);
+    P.topk_w = take(T * K * 4);
+    P.counts = take(NE * 4);
+    P.offs = take((NE + 1) * 4);
+    L->lists = take(NE * T * 4);
+    P.slot_of = take(T * KS * 4);
+    P.slot_tok = take(NS * 4);
+    L->items = take(3 * L->max_items * 4);
+    L->n_items = take(4);
+    P.qh = take(NS * I);
+    P.dh = take(NS * (I / 32) * 4);
+    P.ye = take(NS * H * 4);
+    if (flags & COLI_FWD_DEBUG_TAPS) {
+        const int64_t per_row = NS * (H / 32);
+        int64_t stride = 1;
+        while (per_row * ((I + stride - 1) / stride) > kTapBudget) stride *= 2;
+        P.tap_stride = stride;
+        P.tap_rows = (I + stride - 1) / stride;
+        P.tap = take(NS * P.tap_rows * (H / 32) * 4);
+    }
+    P.total = off;
+}
+
+// Optional event marks between launches (coli_moe_forward_profiled).
+struct Marks {
+    hipStream_t s;
+    void* const* ev = nullptr;
+    const char** names = nullptr;
+    int n = 0, used = 0;
+    void mark(const char* name) {
+        if (ev && used < n) (void)hipEventRecord((hipEvent_t)ev[used], s);
+        if (names && used < n) names[used] = name;
+        ++used;
+    }
+};
+
+template <int NT>
+void launch_gateup_nt(int nbj, dim3 grid, hipStream_t s, const coli_moe_weights* w,
+                      int64_t blob_q, int64_t blob_s, const int8_t* qx, const float* dx,
+                      ItemArgs it, const int32_t* slot_tok, int8_t* qh, float* dh, int32_t* tap,
+                      int tap_rows, int tap_stride) {
+    const int H = w->cfg.hidden, I = w->cfg.inter;
+#define COLI_GU(NBJ)                                                                          \
+    k_gateup_gemv<NT, NBJ><<<grid, 256, 0, s>>>(w->experts_q, w->experts_scale, blob_q, blob_s, \
+                                                qx, dx, it, slot_tok, H, I, qh, dh, tap,        \
+                                                tap_rows, tap_stride)
+    switch (nbj) {
+        case 1: COLI_GU(1); break;
+        case 2: COLI_GU(2); break;
+        case 3: COLI_GU(3); break;
+        default: COLI_GU(4); break;
+    }
+#undef COLI_GU
+}
+
+template <int NT>
+void launch_down_nt(int nbj, dim3 grid, hipStream_t s, const coli_moe_weights* w,
+                    int64_t blob_q, int64_t blob_s, const int8_t* qh, const float* dh,
+                    ItemArgs it, float* ye) {
+    const int H = w->cfg.hidden, I = w->cfg.inter;
+#define COLI_DN(NBJ)                                                                          \
+    k_down_gemv<NT, NBJ><<<grid, 256, 0, s>>>(w->experts_q, w->experts_scale, blob_q, blob_s, \
+                                              qh, dh, it, H, I, ye)
+    switch (nbj) {
+        case 1: COLI_DN(1); break;
+        case 2: COLI_DN(2); break;
+        case 3: COLI_DN(3); break;
+        default: COLI_DN(4); break;
+    }
+#undef COLI_DN
+}
+
+// Router + top-k into ws (shared by coli_moe_route and coli_moe_forward).
+void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const float* bias,
+                  int64_t T, double* logits, int32_t* idx, float* wts, hipStream_t s,
+                  Marks& mk) {
+    const int H = c.hidden, E = c.n_experts, K = c.top_k;
+    mk.mark("router_logits");
+    if (T <= 8) {
+        if (T <= 1)
+            k_router_gemv<1><<<E, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
+        else if (T <= 4)
+            k_router_gemv<4><<<E, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
+        else
+            k_router_gemv<8><<<E, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
+    } else {
+        dim3 g((unsigned)((T + 63) / 64), (unsigned)((E + 31) / 32));
+        k_router_gemm<<<g, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
+    }
+    mk.mark("topk");
+    const unsigned gb = (unsigned)((T + 3) / 4);
+    const double rho = (double)c.routed_scale;
+    const int norm = c.norm_topk ? 1 : 0;
+    if (E <= 64)
+        k_topk<1><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+    else if (E <= 128)
+        k_topk<2><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+    else if (E <= 256)
+        k_topk<4><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+    else if (E <= 512)
+        k_topk<8><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+    else
+        k_topk<16><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+}
+
+int hip_status() {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? COLI_OK : COLI_E_HIP;
+}
+
+int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y, void* ws,
+                 size_t ws_bytes, uint32_t flags, hipStream_t s, Marks& mk) {
+    if (!w || T < 0) return COLI_E_INVAL;
+    int rc = check_cfg(&w->cfg);
+    if (rc) return rc;
+    if (w->cfg.reserved != 0) return COLI_E_INVAL;
+    if (flags & ~(COLI_FWD_ACCUM | COLI_FWD_DEBUG_TAPS)) return COLI_E_INVAL;
+    if (T == 0) return COLI_OK;  // no-op; x, y and ws may be NULL
+    if (!x || !y || !ws) return COLI_E_INVAL;
+    if (!w->w_router || !w->bias || !w->experts_q || !w->experts_scale) return COLI_E_INVAL;
+    if (misaligned(x) || misaligned(y) || misaligned(ws) || misaligned(w->w_router) ||
+        misaligned(w->bias) || misaligned(w->experts_q) || misaligned(w->experts_scale))
+        return COLI_E_ALIGN;
+    if (T > (int64_t)1 << 20) return COLI_E_UNSUPPORTED;
+    const coli_moe_cfg& c = w->cfg;
+    Layout L;
+    make_layout(c, T, flags, &L);
+    if (ws_bytes < L.pub.total) return COLI_E_WORKSPACE;
+
+    const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, S = c.n_shared;
+    const int64_t blob_q = 3ll * I * H / 2, blob_s = 2ll * I + H;
+    char* base = static_cast<char*>(ws);
+    int8_t* qx = reinterpret_cast<int8_t*>(base + L.pub.qx);
+    float* dx = reinterpret_cast<float*>(base + L.pub.dx);
+    double* logits = reinterpret_cast<double*>(base + L.pub.logits);
+    int32_t* idx = reinterpret_cast<int32_t*>(base + L.pub.topk_idx);
+    float* wts = reinterpret_cast<float*>(base + L.pub.topk_w);
+    int32_t* counts = reinterpret_cast<int32_t*>(base + L.pub.counts);
+    int32_t* offs = reinterpret_cast<int32_t*>(base + L.pub.offs);
+    int32_t* lists = reinterpret_cast<int32_t*>(base + L.lists);
+    int32_t* slot_of = reinterpret_cast<int32_t*>(base + L.pub.slot_of);
+    int32_t* slot_tok = reinterpret_cast<int32_t*>(base + L.pub.slot_tok);
+    int32_t* items = reinterpret_cast<int32_t*>(base + L.items);
+    int32_t* n_items = reinterpret_cast<int32_t*>(base + L.n_items);
+    int8_t* qh = reinterpret_cast<int8_t*>(base + L.pub.qh);
+    float* dh = reinterpret_cast<float*>(base + L.pub.dh);
+    float* ye = reinterpret_cast<float*>(base + L.pub.ye);
+    int32_t* tap = (flags & COLI_FWD_DEBUG_TAPS) ? reinterpret_cast<int32_t*>(base + L.pub.tap)
+                                                 : nullptr;
+    ItemArgs it{items, items + L.max_items, items + 2 * L.max_items, n_items};
+
+    mk.mark("quant_x");
+    const int64_t nblk = T * (H / 32);
+    k_quant_q8<true><<<(unsigned)((nblk * 4 + 255) / 256), 256, 0, s>>>(x, nblk, qx, dx);
+
+    launch_route(c, x, w->w_router, w->bias, T, logits, idx, wts, s, mk);
+
+    mk.mark("bucket_lists");
+    k_bucket_lists<<<E + S, 256, 0, s>>>(idx, (int)T, K, E, S, lists, counts);
+    mk.mark("bucket_scan");
+    k_bucket_scan<<<1, 1024, 0, s>>>(counts, lists, (int)T, K, E, S, L.ch, offs, slot_of,
+                                     slot_tok, it.item_e, it.item_s0, it.item_n, n_items);
+
+    const int nt = (T >= L.ch) ? L.ch : (int)T;  // tokens per item at most
+    const int nbj_h = (H / 32 + 63) / 64;
+    const int nbj_i = (I / 32 + 63) / 64;
+    mk.mark("gateup");
+    {
+        dim3 grid((unsigned)((I / 32) * L.max_items));
+        const int tr = (int)L.pub.tap_rows, ts = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
+        if (nt <= 1)
+            launch_gateup_nt<1>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
+                                tap, tr, ts);
+        else if (nt <= 2)
+            launch_gateup_nt<2>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
+                                tap, tr, ts);
+        else
+            launch_gateup_nt<4>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
+                                tap, tr, ts);
+    }
+    mk.mark("down");
+    {
+        dim3 grid((unsigned)((H / 32) * L.max_items));
+        if (nt <= 1)
+            launch_down_nt<1>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye);
+        else if (nt <= 2)
+            launch_down_nt<2>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye);
+        else
+            launch_down_nt<4>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye);
+    }
+    mk.mark("combine");
+    {
+        dim3 grid((unsigned)(((H + 255) / 256) * T));
+        k_combine<<<grid, 256, 0, s>>>(ye, slot_of, wts, K, S, H, y,
+                                       (flags & COLI_FWD_ACCUM) ? 1 : 0);
+    }
+    mk.mark("end");
+    return hip_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+COLI_API const char* coli_strerror(int code) {
+    switch (code) {
+        case COLI_OK: return "ok";
+        case COLI_E_INVAL: return "invalid argument (null pointer, bad shape or flag)";
+        case COLI_E_ALIGN: return "pointer not 16-byte aligned";
+        case COLI_E_WORKSPACE: return "workspace too small";
+        case COLI_E_HIP: return "HIP launch failed";
+        case COLI_E_UNSUPPORTED: return "size beyond the compiled limits";
+        default: return "unknown error";
+    }
+}
+
+COLI_API int coli_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* scale,
+                            void* stream) {
+    if (rows < 0 || cols <= 0 || cols % 32) return COLI_E_INVAL;
+    if (rows == 0) return COLI_OK;
+    if (!w || !q || !scale) return COLI_E_INVAL;
+    if (misaligned(w) || misaligned(q) || misaligned(scale)) return COLI_E_ALIGN;
+    if (rows > 0x7fffffffll) return COLI_E_UNSUPPORTED;
+    k_pack_int4<<<(unsigned)rows, 256, 0, (hipStream_t)stream>>>(w, cols, q, scale);
+    return hip_status();
+}
+
+COLI_API int coli_quant_q8(const float* x, int64_t n_tok, int64_t dim, int8_t* q, float* d,
+                           void* stream) {
+    if (n_tok < 0 || dim <= 0 || dim % 32) return COLI_E_INVAL;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !q || !d) return COLI_E_INVAL;
+    if (misaligned(x) || misaligned(q) || misaligned(d)) return COLI_E_ALIGN;
+    const int64_t nblk = n_tok * (dim / 32);
+    const int64_t nthr = nblk * 4;
+    if ((nthr + 255) / 256 > 0x7fffffffll) return COLI_E_UNSUPPORTED;
+    k_quant_q8<false><<<(unsigned)((nthr + 255) / 256), 256, 0, (hipStream_t)stream>>>(x, nblk, q,
+                                                                                       d);
+    return hip_status();
+}
+
+COLI_API size_t coli_moe_workspace_bytes(const coli_moe_cfg* cfg, int64_t max_tok,
+                                         uint32_t flags) {
+    if (check_cfg(cfg) != COLI_OK || max_tok < 0) return 0;
+    Layout L;
+    make_layout(*cfg, max_tok, flags, &L);
+    return L.pub.total;
+}
+
+COLI_API int coli_moe_workspace_layout(const coli_moe_cfg* cfg, int64_t n_tok, uint32_t flags,
+                                       coli_moe_ws_layout* out) {
+    const int rc = check_cfg(cfg);
+    if (rc) return rc;
+    if (!out || n_tok < 0) return COLI_E_INVAL;
+    Layout L;
+    make_layout(*cfg, n_tok, flags, &L);
+    *out = L.pub;
+    return COLI_OK;
+}
+
+COLI_API int coli_moe_route(const float* x, const float* w_router, const float* bias,
+                            int64_t n_tok, const coli_moe_cfg* cfg, int32_t* topk_idx,
+                            float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_cfg(cfg);
+    if (rc) return rc;
+    if (n_tok < 0) return COLI_E_INVAL;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !w_router || !bias || !topk_idx || !topk_w || !ws) return COLI_E_INVAL;
+    if (misaligned(x) || misaligned(w_router) || misaligned(bias) || misaligned(topk_idx) ||
+        misaligned(topk_w) || misaligned(ws))
+        return COLI_E_ALIGN;
+    if (n_tok > (int64_t)1 << 20) return COLI_E_UNSUPPORTED;
+    Layout L;
+    make_layout(*cfg, n_tok, 0, &L);
+    if (ws_bytes < L.pub.total) return COLI_E_WORKSPACE;
+    Marks mk{(hipStream_t)stream};
+    launch_route(*cfg, x, w_router, bias, n_tok,
+                 reinterpret_cast<double*>(static_cast<char*>(ws) + L.pub.logits), topk_idx,
+                 topk_w, (hipStream_t)stream, mk);
+    return hip_status();
+}
+
+COLI_API int coli_moe_forward(const coli_moe_weights* w, const float* x, int64_t n_tok, float* y,
+                              void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
+    Marks mk{(hipStream_t)stream};
+    return forward_impl(w, x, n_tok, y, ws, ws_bytes, flags, (hipStream_t)stream, mk);
+}
+
+COLI_API int coli_moe_forward_profiled(const coli_moe_weights* w, const float* x, int64_t n_tok,
+                                       float* y, void* ws, size_t ws_bytes, uint32_t flags,
+                                       void* stream, void* const* events, int n_events,
+                                       int* n_used, const char** names) {
+    Marks mk{(hipStream_t)stream, events, names, n_events < 0 ? 0 : n_events, 0};
+    const int rc = forward_impl(w, x, n_tok, y, ws, ws_bytes, flags, (hipStream_t)stream, mk);
+    if (n_used) *n_used = mk.used;
+    return rc;
+}
+
+COLI_API int coli_rmsnorm(const float* x, int64_t n_tok, int64_t dim, float eps, float* out,
+                          void* stream) {
+    if (n_tok < 0 || dim <= 0 || !(eps >= 0.0f)) return COLI_E_INVAL;
+    if (n_tok == 0) return COLI_OK;
+    if (!x || !out) return COLI_E_INVAL;
+    if (misaligned(x) || misaligned(out)) return COLI_E_ALIGN;
+    if (n_tok > 0x7fffffffll) return COLI_E_UNSUPPORTED;
+    k_rmsnorm<<<(unsigned)n_tok, 256, 0, (hipStream_t)stream>>>(x, dim, (double)eps, out);
+    return hip_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,300 @@
+// Router (fp32 inputs, fp64 accumulation), sigmoid + correction bias + top-k
+// in wavefront registers, and token->expert bucketing by histogram and scan.
+#pragma once
+
+#include "coli_common.h"
+
+// ---------------------------------------------------------------------------
+// Router logits for few tokens: one workgroup per expert row streams its
+// H floats once and dots them with every token (tokens come from L2).
+// ---------------------------------------------------------------------------
+template <int NT>
+__global__ __launch_bounds__(256) void k_router_gemv(const float* __restrict__ x,
+                                                     const float* __restrict__ wr, int T, int H,
+                                                     int E, double* __restrict__ logits) {
+    __shared__ double red[NT][4];
+    const int e = blockIdx.x;
+    const float* wrow = wr + (int64_t)e * H;
+    double acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = 0.0;
+    for (int h = threadIdx.x * 4; h < H; h += 1024) {
+        const float4 wv = *reinterpret_cast<const float4*>(wrow + h);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < T) {
+                const float4 xv = *reinterpret_cast<const float4*>(x + (int64_t)t * H + h);
+                acc[t] += (double)xv.x * (double)wv.x;
+                acc[t] += (double)xv.y * (double)wv.y;
+                acc[t] += (double)xv.z * (double)wv.z;
+                acc[t] += (double)xv.w * (double)wv.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const double s = wave_sum_f64(acc[t]);
+        if ((threadIdx.x & 63) == 0) red[t][threadIdx.x >> 6] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < NT && (int)threadIdx.x < T) {
+        const int t = threadIdx.x;
+        logits[(int64_t)t * E + e] = (red[t][0] + red[t][1]) + (red[t][2] + red[t][3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Router logits for many tokens: 64 tokens x 32 experts per workgroup, K
+// chunks of 32 staged in LDS as doubles, 4x2 outputs per lane.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x,
+                                                     const float* __restrict__ wr, int T, int H,
+                                                     int E, double* __restrict__ logits) {
+    __shared__ double xs[64][33];
+    __shared__ double ws[32][33];
+    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 32;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    double acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = 0.0;
+    for (int k0 = 0; k0 < H; k0 += 32) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int li = tid * 2 + i, row = li >> 3, c4 = li & 7;
+            const int t = t0 + row;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < T) v = *reinterpret_cast<const float4*>(x + (int64_t)t * H + k0 + c4 * 4);
+            xs[row][c4 * 4 + 0] = v.x;
+            xs[row][c4 * 4 + 1] = v.y;
+            xs[row][c4 * 4 + 2] = v.z;
+            xs[row][c4 * 4 + 3] = v.w;
+        }
+        {
+            const int row = tid >> 3, c4 = tid & 7;
+            const int e = e0 + row;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (e < E) v = *reinterpret_cast<const float4*>(wr + (int64_t)e * H + k0 + c4 * 4);
+            ws[row][c4 * 4 + 0] = v.x;
+            ws[row][c4 * 4 + 1] = v.y;
+            ws[row][c4 * 4 + 2] = v.z;
+            ws[row][c4 * 4 + 3] = v.w;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int k = 0; k < 32; ++k) {
+            double a[4], b[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = xs[ty * 4 + i][k];
+            b[0] = ws[tx * 2 + 0][k];
+            b[1] = ws[tx * 2 + 1][k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[i][0] += a[i] * b[0];
+                acc[i][1] += a[i] * b[1];
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = t0 + ty * 4 + i, e = e0 + tx * 2 + j;
+            if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Sigmoid, correction bias and top-k: one wave per token, EPL candidates per
+// lane. K rounds of a wave arg-max under the total order (c desc, index asc);
+// lane k keeps the k-th choice. Gate values: unbiased sigmoid, normalised by
+// their sum (k ascending) when asked, times rho, rounded to fp32.
+// ---------------------------------------------------------------------------
+template <int EPL>
+__global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
+                                              const float* __restrict__ bias, int T, int E, int K,
+                                              int norm, double rho, int32_t* __restrict__ idx,
+                                              float* __restrict__ wout) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;  // whole wave leaves together
+    double c[EPL], s[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E) {
+            const double l = logits[(int64_t)t * E + e];
+            s[j] = 1.0 / (1.0 + exp(-l));
+            c[j] = s[j] + (double)bias[e];
+        } else {
+            s[j] = 0.0;
+            c[j] = -__builtin_inf();
+        }
+    }
+    uint32_t taken = 0;
+    int my_e = 0;
+    double my_s = 0.0;
+    for (int k = 0; k < K; ++k) {
+        double bc = -__builtin_inf(), bs = 0.0;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E && !((taken >> j) & 1u) && (c[j] > bc || (c[j] == bc && e < be))) {
+                bc = c[j];
+                be = e;
+                bs = s[j];
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const double oc = __shfl_xor(bc, o, 64);
+            const int oe = __shfl_xor(be, o, 64);
+            const double os = __shfl_xor(bs, o, 64);
+            if (oc > bc || (oc == bc && oe < be)) {
+                bc = oc;
+                be = oe;
+                bs = os;
+            }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        if (lane == k) {
+            my_e = be;
+            my_s = bs;
+        }
+    }
+    double sum = 0.0;
+    for (int k = 0; k < K; ++k) sum += __shfl(my_s, k, 64);
+    if (lane < K) {
+        double v = my_s;
+        if (norm) v = v / sum;
+        v = v * rho;
+        idx[(int64_t)t * K + lane] = my_e;
+        wout[(int64_t)t * K + lane] = (float)v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Bucketing, step 1: one workgroup per expert scans the [T, K] choices in
+// token order and compacts the matching (t, k) entries (value t*(K+S)+k) into
+// a fixed-capacity list; the shared expert (index E) takes every token. No
+// atomics: ballot + popcount ranks inside a wave, LDS across waves, so the
+// lists are in ascending token order and identical on every run.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bucket_lists(const int32_t* __restrict__ idx, int T,
+                                                      int K, int E, int S,
+                                                      int32_t* __restrict__ lists,
+                                                      int32_t* __restrict__ counts) {
+    __shared__ int wave_cnt[4];
+    const int e = blockIdx.x;
+    const int KS = K + S;
+    int32_t* out = lists + (int64_t)e * T;
+    if (e == E) {
+        for (int t = threadIdx.x; t < T; t += 256) out[t] = t * KS + K;
+        if (threadIdx.x == 0) counts[e] = T;
+        return;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int base = 0;
+    for (int t0 = 0; t0 < T; t0 += 256) {
+        const int t = t0 + threadIdx.x;
+        int kk = -1;
+        if (t < T)
+            for (int k = 0; k < K; ++k)
+                if (idx[(int64_t)t * K + k] == e) kk = k;
+        const uint64_t bal = __ballot(kk >= 0);
+        const int pre = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_cnt[wave] = __popcll(bal);
+        __syncthreads();
+        int off = base;
+        for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+        if (kk >= 0) out[off + pre] = t * KS + kk;
+        base += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) counts[e] = base;
+}
+
+// In-place exclusive scan of n <= 4 * 1024 ints in LDS by a 1024-thread block;
+// returns the total.
+__device__ int block_exclusive_scan_1024(int* v, int n, int* part) {
+    const int tid = threadIdx.x;
+    int loc[4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = tid * 4 + i;
+        loc[i] = (j < n) ? v[j] : 0;
+        sum += loc[i];
+    }
+    part[tid] = sum;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+        const int add = (tid >= o) ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += add;
+        __syncthreads();
+    }
+    const int total = part[1023];
+    int run = part[tid] - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = tid * 4 + i;
+        if (j < n) v[j] = run;
+        run += loc[i];
+    }
+    __syncthreads();
+    return total;
+}
+
+// ---------------------------------------------------------------------------
+// Bucketing, step 2 (one 1024-thread workgroup): exclusive scan of the
+// per-expert counts into slot offsets, slot <-> (t, k) maps, and the work
+// items of the expert kernels: each expert's slots cut into chunks of <= CH
+// tokens (item = expert, first slot, count), experts in ascending order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_bucket_scan(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ lists, int T, int K, int E,
+    int S, int CH, int32_t* __restrict__ offs, int32_t* __restrict__ slot_of,
+    int32_t* __restrict__ slot_tok, int32_t* __restrict__ item_e, int32_t* __restrict__ item_s0,
+    int32_t* __restrict__ item_n, int32_t* __restrict__ n_items) {
+    __shared__ int s_off[1040];
+    __shared__ int s_ioff[1040];
+    __shared__ int s_part[1024];
+    const int NE = E + S, KS = K + S;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < NE; e += 1024) {
+        const int c = counts[e];
+        s_off[e] = c;
+        s_ioff[e] = (c + CH - 1) / CH;
+    }
+    __syncthreads();
+    const int total = block_exclusive_scan_1024(s_off, NE, s_part);
+    const int total_items = block_exclusive_scan_1024(s_ioff, NE, s_part);
+    for (int e = tid; e < NE; e += 1024) offs[e] = s_off[e];
+    if (tid == 0) {
+        offs[NE] = total;
+        *n_items = total_items;
+    }
+    for (int e = tid; e < NE; e += 1024) {
+        const int c = counts[e];
+        const int ni = (c + CH - 1) / CH;
+        for (int j = 0; j < ni; ++j) {
+            const int it = s_ioff[e] + j;
+            item_e[it] = e;
+            item_s0[it] = s_off[e] + j * CH;
+            item_n[it] = min(CH, c - j * CH);
+        }
+    }
+    for (int g = tid; g < total; g += 1024) {
+        int lo = 0, hi = NE - 1;  // last e with s_off[e] <= g owns slot g
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_off[mid] <= g) lo = mid; else hi = mid - 1;
+        }
+        const int pos = g - s_off[lo];
+        const int entry = lists[(int64_t)lo * T + pos];
+        slot_of[entry] = g;
+        slot_tok[g] = entry / KS;
+    }
+}

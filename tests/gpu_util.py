@@ -1,0 +1,62 @@
+"""GPU-test helpers: device layers packed by the library, oracle layers packed
+by the oracle from the same seeded fp32 draws, and layout conversions."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import coli_synth as cs
+
+
+def unperm8(q: np.ndarray) -> np.ndarray:
+    """Undo the library's 8-group order (e0,e2,e4,e6,e1,e3,e5,e7) along the last axis."""
+    q = np.asarray(q)
+    g = q.reshape(*q.shape[:-1], -1, 2, 4)          # [..., groups, (evens, odds), 4]
+    out = np.stack([g[..., 0, :], g[..., 1, :]], axis=-1)  # [..., groups, 4, 2]
+    return out.reshape(q.shape)
+
+
+def lib_cfg(C, cfg):
+    return C.make_cfg(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
+                      cfg.norm_topk, cfg.rho)
+
+
+def gpu_layer(C, cfg, layer=0):
+    """LayerWeights on cuda:0, every matrix packed by coli_pack_int4."""
+    wr, b, q, s = cs.build_layer(cfg, layer, "cuda", lambda w, qv, sv: C.coli_pack_int4(w, qv, sv))
+    return C.LayerWeights(lib_cfg(C, cfg), wr, b, q, s)
+
+
+def layer_input(ref, cfg, layer=0, n_tok=None, first_tok=0):
+    """Layer input on the host: the raw draw, RMS-normalised by the oracle when
+    the workload says the input is normalised."""
+    x = cs.activations(cfg, layer, "cpu", n_tok=n_tok, first_tok=first_tok).numpy()
+    if cfg.rmsnorm_input:
+        x = ref.rmsnorm(x, np.float32(1e-5))
+    return np.ascontiguousarray(x, np.float32)
+
+
+def oracle_layer_for(ref, cfg, layer, x, forced_idx=None, draw_device="cuda"):
+    """OracleLayer holding only the experts that tokens x select (plus shared),
+    each drawn as fp32 by coli_synth (on draw_device, bit-identical to the CPU
+    draw) and packed by the oracle."""
+    wr, b = cs.router(cfg, layer, "cpu")
+    wr, b = wr.numpy(), b.numpy()
+    if forced_idx is None:
+        idx, _, _ = ref.route(x, wr, b, cfg.top_k, cfg.norm_topk, cfg.rho)
+    else:
+        idx = forced_idx
+    need = sorted(set(int(e) for e in np.unique(idx)) | ({cfg.n_experts} if cfg.n_shared else set()))
+    L = ref.OracleLayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
+                        cfg.norm_topk, cfg.rho, wr, b, {})
+    for e in need:
+        mats = [cs.expert_matrix(cfg, layer, e, w, draw_device).cpu().numpy()
+                for w in ("gate", "up", "down")]
+        L.add_expert(e, ref.pack_expert(*mats))
+    return L
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))

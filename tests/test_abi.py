@@ -1,0 +1,48 @@
+"""The C-ABI library loads on the CPU and exports every symbol include/*.h declares
+(no compute calls: those need a GPU)."""
+import ctypes
+import glob
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        names += re.findall(r"COLI_API\s+[\w\s\*]+?\b(coli_\w+)\s*\(", src)
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = set(_declared())
+    for n in ("coli_pack_int4", "coli_quant_q8", "coli_moe_route", "coli_moe_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(os.path.join(ROOT, "int4_quantized_moe_sigmoid_amd", "libcoli_moe.so"))
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_host_side_queries_without_gpu():
+    import int4_quantized_moe_sigmoid_amd as C
+    cfg = C.make_cfg(6144, 2048, 256, 8)
+    n1 = C.coli_moe_workspace_bytes(cfg, 1)
+    n512 = C.coli_moe_workspace_bytes(cfg, 512)
+    assert 0 < n1 < n512
+    L = C.coli_moe_workspace_layout(cfg, 3)
+    assert L.n_slots == 27 and L.total <= C.coli_moe_workspace_bytes(cfg, 3)
+    offs = [L.qx, L.dx, L.logits, L.topk_idx, L.topk_w, L.counts, L.offs, L.slot_of,
+            L.slot_tok, L.qh, L.dh, L.ye]
+    assert all(o % 256 == 0 for o in offs) and len(set(offs)) == len(offs)
+    assert C.lib().coli_strerror(C.COLI_E_WORKSPACE).decode().startswith("workspace")
+    for bad in (C.make_cfg(6144, 2048, 4, 8), C.make_cfg(100, 2048, 256, 8),
+                C.make_cfg(6144, 2048, 256, 8, n_shared=2)):
+        assert C.lib().coli_moe_workspace_bytes(bad, 1, 0) == 0
+    big = C.make_cfg(6144, 2048, 2048, 8)
+    rc = C.lib().coli_moe_workspace_layout(big, 1, 0, C.coli_moe_ws_layout())
+    assert rc == C.COLI_E_UNSUPPORTED
