@@ -37,11 +37,30 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this many MiB a few times (the "
+                         "reference kernel that scales HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int):
+    import torch
+    torch.cuda.set_device(0)
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "launches": 5}), flush=True)
 
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU: the layer is not sharded "
                                    "across GPUs (use --gpus 1)", "n_gpus": args.gpus}))
