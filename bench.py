@@ -26,6 +26,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 
+# HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (two runs), scaled by what the counters read for a plain device
+# copy of known size (FETCH_SIZE x 2, WRITE_SIZE x 1). Keyed by (kernel,
+# workload); dropped whenever that kernel changes.
+TRAFFIC = {}
+
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -149,19 +155,25 @@ def main():
         kern = {k: v / n_prof for k, v in sums.items()}
     uniq_avg = float(np.mean(unique_counts)) if unique_counts else float(min(E, T * K) + S)
 
+    # algorithmic HBM bytes of the gate/up launch: the packed gate and up rows and
+    # their scales of every expert in use, Q8_0(x) in, Q8_0(h) out (+ the fp64
+    # router logits the decode kernel reads to redo the top-k)
     gate_up_bytes = uniq_avg * (2 * I * H // 2 + 4 * 2 * I) + T * (H + H // 8) + \
         T * (K + S) * (I + I // 8)
-    down_bytes = uniq_avg * (I * H // 2 + 4 * H) + T * (K + S) * (I + I // 8 + 4 * H)
     step_bytes = uniq_avg * eb + 4 * E * H + 4 * E + 8 * T * H
     weight_gbps = uniq_avg * eb / (ms_per_step * 1e-3) / 1e9
 
     roofline = None
-    if "gateup" in kern:
-        ms = kern["gateup"]
+    gk = "dec_gateup" if "dec_gateup" in kern else ("gateup" if "gateup" in kern else None)
+    if gk is not None:
+        if gk == "dec_gateup":
+            gate_up_bytes += 8 * T * E
+        ms = kern[gk]
         ach = gate_up_bytes / (ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
-                    "kernel": "k_gateup_gemv", "bytes_per_launch": int(gate_up_bytes),
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                    "traffic": TRAFFIC.get((gk, cfg.name)),
+                    "kernel": gk, "bytes_per_launch": int(gate_up_bytes),
                     "avg_launch_us": round(ms * 1e3, 2)}
 
     cpu = None

@@ -2,8 +2,6 @@
 // layout, kernel selection and launches. No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -12,7 +10,6 @@
 #include "coli_moe.h"
 #include "coli_common.h"
 #include "k_decode.h"
-#include "k_persist.h"
 #include "k_gemv.h"
 #include "k_route.h"
 #include "k_small.h"
@@ -44,7 +41,7 @@ int check_cfg(const coli_moe_cfg* c) {
 
 struct Layout {
     coli_moe_ws_layout pub;
-    size_t lists, items, n_items, uinfo, sync;
+    size_t lists, items, n_items, uinfo;
     int64_t max_items;
     int ch;
 };
@@ -83,7 +80,7 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
     L->items = take(3 * L->max_items * 4);
     L->n_items = take(4);
     L->uinfo = take(4 * (1 + 4 * dec::kMaxEntries + 64));
-    L->sync = take(8 * dec::kSyncWords + 64);
+
     P.qh = take(NS * I);
     P.dh = take(NS * (I / 32) * 4);
     P.ye = take(NS * H * 4);
@@ -95,6 +92,7 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
         P.tap_rows = (I + stride - 1) / stride;
         P.tap = take(NS * P.tap_rows * (H / 32) * 4);
     }
+
     P.total = off;
 }
 
@@ -181,120 +179,40 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
 }
 
 // Template selection for the fused few-token path.
-template <int NT, int NBJH, int NBJI, bool TAP>
+// Few-token path: three fused kernels (k_decode.h). Shapes it covers:
+// hidden <= 6144, intermediate <= 2048, <= 256 routed experts.
+bool small_path_fits(const coli_moe_cfg& c, int64_t T) {
+    return T <= dec::kMaxTok && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
+           c.inter <= 2048 && c.n_experts <= 256;
+}
+
+template <int NT, int NBJH, bool TAP>
 void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     const int nrb = a.I / 32;
-    mk.mark("dec_router_shared");
-    if (a.E <= 256)
-        dec::k_dec_router_shared<NT, NBJH, 4, TAP><<<a.E + (a.S ? nrb : 0), 512, 0, s>>>(a);
-    else
-        dec::k_dec_router_shared<NT, NBJH, 16, TAP><<<a.E + (a.S ? nrb : 0), 512, 0, s>>>(a);
+    mk.mark("dec_router");
+    dec::k_dec_router<NT><<<a.E, 256, 0, s>>>(a);
     mk.mark("dec_gateup");
-    const int nu = (a.T * a.K < a.E) ? a.T * a.K : a.E;
-    dec::k_dec_gateup<NT, NBJH, TAP><<<nu * nrb, 512, 0, s>>>(a);
-    mk.mark("dec_down");
-    const int nexp = nu + a.S;  // experts in use at most
-    const int waves = nexp < 16 ? nexp : 16;
-    dec::k_dec_down<NT, NBJI><<<a.H / 8, 64 * waves, 0, s>>>(a);
-}
-
-// Resident workgroups of a kernel on the current device (0 if unknown).
-template <typename F>
-int resident_capacity(F* kern, int threads) {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] > 0) return cache[dev];
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess)
-        return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    cache[dev] = per_cu * cus;
-    return cache[dev];
-}
-
-template <int NT, int NBJH, int NBJI, int EPL, bool TAP>
-bool launch_persist(const dec::DecArgs& a, int32_t* err, hipStream_t s, Marks& mk) {
-    auto* kern = dec::k_dec_persist<NT, NBJH, NBJI, EPL, TAP>;
-    const int cap = resident_capacity(kern, 256);
-    if (cap <= 0) return false;
-    dec::PArgs P{};
-    P.d = a;
-    P.err = err;
-    const int nrb = a.I / 32;
     const int um = (a.T * a.K < a.E) ? a.T * a.K : a.E;
-    P.n_router = a.E;
-    P.n_shared = a.S ? nrb : 0;
-    P.n_routed = um * nrb;
-    P.n_down = a.H / dec::kRPG;
-    P.n_items = P.n_router + P.n_shared + P.n_routed + P.n_down;
-    P.grid = P.n_items < cap ? P.n_items : cap;
-    mk.mark("dec_persist");
-    kern<<<P.grid, 256, 0, s>>>(P);
-    return true;
-}
-
-template <int NT, int NBJH, int NBJI>
-void launch_small_nt(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
-    static const bool three = [] {
-        const char* v = getenv("COLI_DECODE_3K");
-        return v && v[0] == '1';
-    }();
-    int32_t* err = reinterpret_cast<int32_t*>(a.sync + dec::kSyncWords);
-    if (!three) {
-        bool ok;
-        if (a.tap)
-            ok = (a.E <= 256) ? launch_persist<NT, NBJH, NBJI, 4, true>(a, err, s, mk)
-                              : launch_persist<NT, NBJH, NBJI, 16, true>(a, err, s, mk);
-        else
-            ok = (a.E <= 256) ? launch_persist<NT, NBJH, NBJI, 4, false>(a, err, s, mk)
-                              : launch_persist<NT, NBJH, NBJI, 16, false>(a, err, s, mk);
-        if (ok) return;
-    }
-    if (a.tap)
-        launch_small_tap<NT, NBJH, NBJI, true>(a, s, mk);
-    else
-        launch_small_tap<NT, NBJH, NBJI, false>(a, s, mk);
-}
-
-// Per-call tag of the workspace's tagged counters: process-unique start,
-// advanced by every forward call.
-uint32_t next_call_tag() {
-    static std::atomic<uint32_t> tag{(uint32_t)std::chrono::steady_clock::now()
-                                         .time_since_epoch()
-                                         .count() *
-                                     2654435761u};
-    uint32_t t = tag.fetch_add(1, std::memory_order_relaxed) + 1;
-    return t;
-}
-
-inline int nbj_bucket(int nblocks) {  // 64-block groups per lane, rounded to 1, 3 or 4
-    const int g = (nblocks + 63) / 64;
-    return g <= 1 ? 1 : (g <= 3 ? 3 : 4);
+    dec::k_dec_gateup<NT, NBJH, 4, TAP><<<(a.S + um) * nrb, 256, 0, s>>>(a);
+    mk.mark("dec_down");
+    dec::k_dec_down<NT, 1, 2, 4><<<a.H / 8, 256, 0, s>>>(a);
 }
 
 template <int NT>
-void launch_small_h(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
-    const int nh = nbj_bucket(a.H / 32), ni = nbj_bucket(a.I / 32);
-#define COLI_SM(A, B)                          \
-    if (nh == A && ni == B) {                  \
-        launch_small_nt<NT, A, B>(a, s, mk);   \
-        return;                                \
+void launch_small_nt(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
+    if (a.H <= 2048) {
+        if (a.tap) launch_small_tap<NT, 1, true>(a, s, mk);
+        else launch_small_tap<NT, 1, false>(a, s, mk);
+    } else {
+        if (a.tap) launch_small_tap<NT, 3, true>(a, s, mk);
+        else launch_small_tap<NT, 3, false>(a, s, mk);
     }
-    COLI_SM(1, 1) COLI_SM(1, 3) COLI_SM(1, 4)
-    COLI_SM(3, 1) COLI_SM(3, 3) COLI_SM(3, 4)
-    COLI_SM(4, 1) COLI_SM(4, 3) COLI_SM(4, 4)
-#undef COLI_SM
 }
 
 void launch_small(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
-    if (a.T <= 1)
-        launch_small_h<1>(a, s, mk);
-    else if (a.T <= 2)
-        launch_small_h<2>(a, s, mk);
-    else
-        launch_small_h<4>(a, s, mk);
+    if (a.T <= 1) launch_small_nt<1>(a, s, mk);
+    else if (a.T <= 2) launch_small_nt<2>(a, s, mk);
+    else launch_small_nt<4>(a, s, mk);
 }
 
 int hip_status() {
@@ -343,7 +261,7 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
                                                  : nullptr;
     ItemArgs it{items, items + L.max_items, items + 2 * L.max_items, n_items};
 
-    if (T <= dec::kMaxTok && (int64_t)T * K <= dec::kMaxEntries) {
+    if (small_path_fits(c, T)) {
         dec::DecArgs a{};
         a.x = x; a.wr = w->w_router; a.bias = w->bias; a.eq = w->experts_q; a.es = w->experts_scale;
         a.blob_q = blob_q; a.blob_s = blob_s;
@@ -356,8 +274,6 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         a.tap_rows = (int)L.pub.tap_rows;
         a.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
         a.y = y; a.accum = (flags & COLI_FWD_ACCUM) ? 1 : 0;
-        a.sync = reinterpret_cast<unsigned long long*>(base + L.sync);
-        a.tag = next_call_tag();
         launch_small(a, s, mk);
         mk.mark("end");
         return hip_status();

@@ -1,21 +1,19 @@
 // Fused path for few tokens (decode at batch 1, MTP verify): three launches.
 //
-//   A  router rows (one workgroup per expert row, fp64 logits) and, in the
-//      same grid, the shared expert's gate/up + SwiGLU + Q8_0(h): the shared
-//      expert does not depend on routing, so its weights stream while the
-//      router runs. The router workgroup that finishes last (a tagged
-//      device-scope counter, see tagged_add) runs the top-k and the expert
-//      bucketing of the <= 4 tokens once and publishes them.
-//   B  routed gate/up + SwiGLU + Q8_0(h): one workgroup per (expert in use,
-//      block of 32 intermediate rows); tokens that share an expert are served
-//      by one pass over its weights.
+//   A  router rows, one workgroup per expert (fp64 logits); workgroup 0 also
+//      writes Q8_0(x).
+//   B  gate/up + SwiGLU + Q8_0(h). The shared expert's h-blocks come first in
+//      the grid: they need no routing, so they stream while the routed
+//      workgroups each recompute the top-k and expert bucketing of the <= 4
+//      tokens in LDS (a few hundred values; cheaper here than any grid-wide
+//      hand-off, which on this GPU means an L2 write-back per workgroup).
+//      Tokens that share an expert are served by one pass over its weights.
 //   C  down projection of every expert in use plus the weighted combine,
 //      written straight into y.
 //
-// Weight streams use 16-byte nontemporal loads (each byte is used once);
-// lane l owns blocks l, l+64, l+128 of a row so a wave instruction reads 1 KiB
-// contiguous. Activations are quantised to Q8_0 in registers by each
-// workgroup straight from fp32 x (bit-identical to the Q8_0 kernel).
+// Kernel boundaries are the only synchronisation. Weight streams use 16-byte
+// nontemporal loads (each byte is used once); lane l owns blocks l, l+64,
+// l+128 of a row so a wave instruction reads 1 KiB contiguous.
 #pragma once
 
 #include "coli_common.h"
@@ -113,9 +111,7 @@ __device__ __forceinline__ void route_token_wave(const double* logits, const flo
     for (int j = 0; j < EPL; ++j) {
         const int e = lane + 64 * j;
         if (e < E) {
-            // written by other workgroups of this grid: device-coherent load
-            const double l = __hip_atomic_load(logits + (int64_t)t * E + e, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+            const double l = logits[(int64_t)t * E + e];
             s[j] = 1.0 / (1.0 + exp(-l));
             c[j] = s[j] + (double)bias[e];
         } else {
@@ -218,140 +214,6 @@ __device__ __forceinline__ void route_small(const double* logits, const float* b
     __syncthreads();
 }
 
-// 64-bit counter in the workspace whose high word is a per-call tag and low
-// word a count: the first increment of a call replaces a stale tag (left by
-// an earlier call, or arbitrary memory) by compare-and-swap, so the counter
-// needs no clearing between calls. Returns the count before this increment.
-// The data a workgroup publishes before its increment is written with
-// device-scope atomic stores (coherent across the chip's L2 slices without a
-// cache write-back) and completed before the increment (the workgroup
-// barrier waits for outstanding stores); the observer reads it back with
-// device-scope atomic loads. Agent-scope release/acquire fences would instead
-// write back and invalidate whole L2 slices, which costs microseconds each.
-__device__ __forceinline__ uint32_t tagged_add(unsigned long long* c, uint32_t tag) {
-    unsigned long long v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {
-        if ((uint32_t)(v >> 32) == tag)
-            return (uint32_t)__hip_atomic_fetch_add(c, 1ull, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-        const unsigned long long want = ((unsigned long long)tag << 32) | 1ull;
-        if (__hip_atomic_compare_exchange_strong(c, &v, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-            return 0;
-    }
-}
-
-// Gate/up GEMV for one expert, NT token slots and 32 intermediate rows
-// (h-block hb), then SwiGLU and Q8_0(h) into qh/dh at slots slot0 + i.
-// Activations (Q8_0 codes in 8-group order and block scales) are read from
-// aq/ad, rows of token tok[i] with strides H and H/32 (global workspace or
-// LDS). An 8-wave workgroup: wave w owns h-rows w, w+8, w+16, w+24, i.e. two
-// steps of (two gate + two up) rows, and requests both steps' weights before
-// any arithmetic, so a CU holding two such workgroups has all of its share of
-// the expert's bytes in flight at once; at every step the eight waves read
-// 16 consecutive rows of each matrix. Loads are unconditional (lanes past the
-// last block read a clamped address and see zero activations).
-template <int NT, int NBJ, bool TAP>
-__device__ __forceinline__ void gateup_block(const uint8_t* gate, const uint8_t* up, const float* gs,
-                                             const float* us, int H, int I, int hb, int n,
-                                             const int8_t* aq, const float* ad, const int* tok,
-                                             int slot0, int8_t* qh, float* dh, int32_t* tap,
-                                             int tap_rows, int tap_stride, float (*hbuf)[32]) {
-    const int BH = H >> 5;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r0 = hb * 32 + wave;  // rows r0 + 8k, k = 0..3
-    int boff[NBJ];
-#pragma unroll
-    for (int j = 0; j < NBJ; ++j) boff[j] = min(lane + 64 * j, BH - 1) * 16;
-
-    uint4 wb[2][4][NBJ];
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = r0 + 8 * (2 * p + (q & 1));
-            const uint8_t* row = ((q < 2) ? gate : up) + (int64_t)r * (H >> 1);
-#pragma unroll
-            for (int j = 0; j < NBJ; ++j) wb[p][q][j] = ldnt(row + boff[j]);
-        }
-    float gsc[4], usc[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        gsc[k] = gs[r0 + 8 * k];
-        usc[k] = us[r0 + 8 * k];
-    }
-    uint4 xa[NT][NBJ][2];
-    double xd[NT][NBJ];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-        const int t = tok[(i < n) ? i : 0];
-#pragma unroll
-        for (int j = 0; j < NBJ; ++j) {
-            const int b = lane + 64 * j;
-            const bool ok = i < n && b < BH;
-            const int bb = min(b, BH - 1);
-            const uint4* p = reinterpret_cast<const uint4*>(aq + (int64_t)t * H + bb * 32);
-            const uint4 a0 = p[0], a1 = p[1];
-            const float d = ad[(int64_t)t * BH + bb];
-            xa[i][j][0] = ok ? a0 : make_uint4(0, 0, 0, 0);
-            xa[i][j][1] = ok ? a1 : make_uint4(0, 0, 0, 0);
-            xd[i][j] = ok ? (double)d * 0.0625 : 0.0;  // undo the x16 of the codes
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        // values ordered (quad, token): quad 0/1 = gate rows of step p, 2/3 = up rows
-        double v[4 * NT];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                double acc = 0.0;
-#pragma unroll
-                for (int j = 0; j < NBJ; ++j) {
-                    const int d16 = dot_block16(wb[p][q][j], xa[i][j][0], xa[i][j][1]);
-                    acc += xd[i][j] * (double)d16;
-                    if (TAP && q < 2) {
-                        const int r = r0 + 8 * (2 * p + q), b = lane + 64 * j;
-                        if (i < n && b < BH && (r % tap_stride) == 0)
-                            tap[((int64_t)(slot0 + i) * tap_rows + r / tap_stride) * BH + b] = d16 / 16;
-                    }
-                }
-                v[q * NT + i] = acc;
-            }
-        const double sum = wave_reduce_tr<4 * NT>(v, lane);
-        const double other = __shfl_xor(sum, 32, 64);  // up value for gate lanes
-        constexpr int kShift = (NT == 1) ? 4 : (NT == 2) ? 3 : 2;  // 6 - log2(4 NT)
-        const int vi = lane >> kShift;   // value index held by this lane
-        if (vi < 2 * NT && lane == (vi << kShift)) {
-            const int q = vi / NT, i = vi - q * NT;   // q in {0, 1}: row r0 + 8(2p+q)
-            if (i < n) {
-                const int k = 2 * p + q;
-                const float g = (float)((double)gsc[k] * sum);
-                const float u = (float)((double)usc[k] * other);
-                hbuf[i][wave + 8 * k] = swiglu_f32(g, u);
-            }
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x < NT * 32) {
-        const int i = threadIdx.x >> 5, k = threadIdx.x & 31;
-        const float val = (i < n) ? hbuf[i][k] : 0.0f;
-        float a = fabsf(val);
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 32));
-        const float dd = a / 127.0f;
-        const int c = q8_code(val, dd);
-        if (i < n) {
-            qh[(int64_t)(slot0 + i) * I + hb * 32 + q8_perm_pos(k)] = (int8_t)c;
-            if (k == 0) dh[(int64_t)(slot0 + i) * (I >> 5) + hb] = dd;
-        }
-    }
-}
-
 struct DecArgs {
     const float* x;
     const float* wr;
@@ -378,13 +240,125 @@ struct DecArgs {
     int tap_rows, tap_stride;
     float* y;
     int accum;
-    unsigned long long* sync;  // tagged counters
-    uint32_t tag;
 };
 
 constexpr int kUinfoW = 1 + 3 * kMaxEntries;  // offset of the slot weights in uinfo
 
-// Publishes the routing computed in R (by the last router workgroup).
+
+// Gate/up GEMV for one expert, NT token slots and 32 intermediate rows
+// (h-block hb), then SwiGLU and Q8_0(h) into qh/dh at slots slot0 + i.
+// Activations: Q8_0 codes of x in 8-group order (qx) and block scales (dx),
+// rows of token tok[i]. Four waves; wave w owns h-rows w, w+4, ..., w+28,
+// taken two per step (two gate + two up rows), so the four waves read 8
+// consecutive rows of each matrix at a time; the loop is fully unrolled and
+// every load unconditional (lanes past the last block read a clamped address
+// and see zero activations), with two steps' loads in flight.
+template <int NT, int NBJ, bool TAP>
+__device__ __forceinline__ void gateup_block(const DecArgs& a, int e, int hb, int n,
+                                             const int* tok, int slot0, float (*hbuf)[32]) {
+    const int H = a.H, I = a.I, BH = H >> 5;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
+    const uint8_t* up = gate + (int64_t)I * (H >> 1);
+    const float* gs = a.es + (int64_t)e * a.blob_s;
+    const float* us = gs + I;
+    const int r0 = hb * 32 + wave;  // rows r0 + 4k, k = 0..7
+    int boff[NBJ];
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j) boff[j] = min(lane + 64 * j, BH - 1) * 16;
+    uint4 wb[2][4][NBJ];
+    auto load_pair = [&](int p, uint4 (&dst)[4][NBJ]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r0 + 4 * (2 * p + (q & 1));
+            const uint8_t* row = ((q < 2) ? gate : up) + (int64_t)r * (H >> 1);
+#pragma unroll
+            for (int j = 0; j < NBJ; ++j) dst[q][j] = ldnt(row + boff[j]);
+        }
+    };
+    load_pair(0, wb[0]);
+    load_pair(1, wb[1]);
+    // row scales, one per lane (lane k & 7 holds row r0 + 4 (k & 7))
+    const float gsl = gs[r0 + 4 * (lane & 7)];
+    const float usl = us[r0 + 4 * (lane & 7)];
+    uint4 xa[NT][NBJ][2];
+    double xd[NT][NBJ];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int t = tok[(i < n) ? i : 0];
+#pragma unroll
+        for (int j = 0; j < NBJ; ++j) {
+            const int b = lane + 64 * j;
+            const bool ok = i < n && b < BH;
+            const int bb = min(b, BH - 1);
+            const uint4* p = reinterpret_cast<const uint4*>(a.qx + (int64_t)t * H + bb * 32);
+            const uint4 a0 = p[0], a1 = p[1];
+            const float d = a.dx[(int64_t)t * BH + bb];
+            xa[i][j][0] = ok ? a0 : make_uint4(0, 0, 0, 0);
+            xa[i][j][1] = ok ? a1 : make_uint4(0, 0, 0, 0);
+            xd[i][j] = ok ? (double)d * 0.0625 : 0.0;  // undo the x16 of the codes
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        if (p >= 1 && p < 3) load_pair(p + 1, wb[(p + 1) & 1]);
+        // keep the next step's loads issued ahead of this step's arithmetic
+        __builtin_amdgcn_sched_barrier(0);
+        const uint4 (&wc)[4][NBJ] = wb[p & 1];
+        // values ordered (quad, token): quad 0/1 = gate rows of step p, 2/3 = up rows
+        double v[4 * NT];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                double acc = 0.0;
+#pragma unroll
+                for (int j = 0; j < NBJ; ++j) {
+                    const int d16 = dot_block16(wc[q][j], xa[i][j][0], xa[i][j][1]);
+                    acc += xd[i][j] * (double)d16;
+                    if (TAP && q < 2) {
+                        const int r = r0 + 4 * (2 * p + q), b = lane + 64 * j;
+                        if (i < n && b < BH && (r % a.tap_stride) == 0)
+                            a.tap[((int64_t)(slot0 + i) * a.tap_rows + r / a.tap_stride) * BH + b] =
+                                d16 / 16;
+                    }
+                }
+                v[q * NT + i] = acc;
+            }
+        const double sum = wave_reduce_tr<4 * NT>(v, lane);
+        const double other = __shfl_xor(sum, 32, 64);  // up value for gate lanes
+        constexpr int kShift = (NT == 1) ? 4 : (NT == 2) ? 3 : 2;  // 6 - log2(4 NT)
+        const int vi = lane >> kShift;   // value index held by this lane
+        const int kq = 2 * p + ((vi < 2 * NT) ? vi / NT : 0);
+        const float gsk = __shfl(gsl, kq, 64), usk = __shfl(usl, kq, 64);
+        if (vi < 2 * NT && lane == (vi << kShift)) {
+            const int q = vi / NT, i = vi - q * NT;   // q in {0, 1}: row r0 + 4(2p+q)
+            if (i < n) {
+                const float g = (float)((double)gsk * sum);
+                const float u = (float)((double)usk * other);
+                hbuf[i][wave + 4 * (2 * p + q)] = swiglu_f32(g, u);
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < NT * 32) {
+        const int i = threadIdx.x >> 5, k = threadIdx.x & 31;
+        const float val = (i < n) ? hbuf[i][k] : 0.0f;
+        float amax = fabsf(val);
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+        const float dd = amax / 127.0f;
+        const int c = q8_code(val, dd);
+        if (i < n) {
+            a.qh[(int64_t)(slot0 + i) * I + hb * 32 + q8_perm_pos(k)] = (int8_t)c;
+            if (k == 0) a.dh[(int64_t)(slot0 + i) * (I >> 5) + hb] = dd;
+        }
+    }
+}
+
+// Publishes the routing computed in R (one workgroup of B) for C, the taps
+// and the workspace layout.
 __device__ void publish_route(const DecArgs& a, const Route& R) {
     const int T = a.T, K = a.K, E = a.E, S = a.S;
     const int n = T * K;
@@ -419,222 +393,207 @@ __device__ void publish_route(const DecArgs& a, const Route& R) {
     if (threadIdx.x == 0) a.uinfo[0] = R.n_uniq;
 }
 
-// A: blocks [0, E) router rows (the last one to finish also routes);
-//    blocks [E, E + I/32) shared-expert h-blocks.
-template <int NT, int NBJ, int EPL, bool TAP>
-__global__ __launch_bounds__(512) void k_dec_router_shared(DecArgs a) {
-    __shared__ float hbuf[NT][32];
-    __shared__ double red[NT][8];
-    __shared__ int s_last;
-    __shared__ Route R;
-    __shared__ uint4 s_q[NT * 8192 / 16];   // Q8_0 codes of x (8-group order)
-    __shared__ float s_d[NT * 8192 / 32];
-    const int b = blockIdx.x;
+// A: router rows (one workgroup per expert); workgroup 0 also writes Q8_0(x).
+template <int NT>
+__global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
+    __shared__ double red[NT][4];
+    const int e = blockIdx.x;
     const int T = a.T, H = a.H;
-    if (b < a.E) {
-        const int e = b;
-        const float* wrow = a.wr + (int64_t)e * H;
-        double acc[NT];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float* wrow = a.wr + (int64_t)e * H;
+    double acc[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = 0.0;
-        for (int h = threadIdx.x * 4; h < H; h += 2048) {
-            const float4 wv = *reinterpret_cast<const float4*>(wrow + h);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                if (t < T) {
-                    const float4 xv = *reinterpret_cast<const float4*>(a.x + (int64_t)t * H + h);
-                    acc[t] += (double)xv.x * (double)wv.x;
-                    acc[t] += (double)xv.y * (double)wv.y;
-                    acc[t] += (double)xv.z * (double)wv.z;
-                    acc[t] += (double)xv.w * (double)wv.w;
-                }
-            }
-        }
+    for (int t = 0; t < NT; ++t) acc[t] = 0.0;
+    for (int h = threadIdx.x * 4; h < H; h += 1024) {
+        const float4 wv = *reinterpret_cast<const float4*>(wrow + h);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const double s = wave_sum_f64(acc[t]);
-            if ((threadIdx.x & 63) == 0) red[t][threadIdx.x >> 6] = s;
-        }
-        __syncthreads();
-        if ((int)threadIdx.x < T) {
-            const double* r = red[threadIdx.x];
-            __hip_atomic_store(a.logits + (int64_t)threadIdx.x * a.E + e,
-                               ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7])),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (e == 0) {
-            // Q8_0(x) into the workspace for the routed gate/up kernel and the taps
-            const int nblk = T * (H >> 5);
-            for (int blk = threadIdx.x; blk < nblk; blk += 512) {
-                uint4 q0, q1;
-                const float d = q8_block_regs(a.x + (int64_t)blk * 32, q0, q1);
-                uint4* o = reinterpret_cast<uint4*>(a.qx + (int64_t)blk * 32);
-                o[0] = q0;
-                o[1] = q1;
-                a.dx[blk] = d;
+            if (t < T) {
+                const float4 xv = *reinterpret_cast<const float4*>(a.x + (int64_t)t * H + h);
+                acc[t] += (double)xv.x * (double)wv.x;
+                acc[t] += (double)xv.y * (double)wv.y;
+                acc[t] += (double)xv.z * (double)wv.z;
+                acc[t] += (double)xv.w * (double)wv.w;
             }
         }
-        __syncthreads();
-        if (threadIdx.x == 0) s_last = (tagged_add(a.sync, a.tag) == (uint32_t)(a.E - 1));
-        __syncthreads();
-        if (!s_last) return;
-        // every router row is in memory: route the tokens once
-        route_small<EPL>(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R);
-        publish_route(a, R);
-        return;
     }
-    // shared expert: quantise x into LDS cooperatively, then one h-block
-    const int hb = b - a.E;
-    const int se = a.E;
-    const int BH = H >> 5;
-    for (int blk = threadIdx.x; blk < T * BH; blk += 512) {
-        uint4 q0, q1;
-        s_d[blk] = q8_block_regs(a.x + (int64_t)blk * 32, q0, q1);
-        s_q[2 * blk] = q0;
-        s_q[2 * blk + 1] = q1;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const double s = wave_sum_f64(acc[t]);
+        if (lane == 0) red[t][wave] = s;
     }
     __syncthreads();
-    int tok[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) tok[i] = i;
-    const uint8_t* gate = a.eq + (int64_t)se * a.blob_q;
-    const uint8_t* up = gate + (int64_t)a.I * (H >> 1);
-    const float* gs = a.es + (int64_t)se * a.blob_s;
-    gateup_block<NT, NBJ, TAP>(gate, up, gs, gs + a.I, H, a.I, hb, T,
-                               reinterpret_cast<const int8_t*>(s_q), s_d, tok, T * a.K, a.qh,
-                               a.dh, a.tap, a.tap_rows, a.tap_stride, hbuf);
+    if ((int)threadIdx.x < T) {
+        const double* r = red[threadIdx.x];
+        a.logits[(int64_t)threadIdx.x * a.E + e] = (r[0] + r[1]) + (r[2] + r[3]);
+    }
+    if (e == 0) {
+        const int nblk = T * (H >> 5);
+        for (int blk = threadIdx.x; blk < nblk; blk += 256) {
+            uint4 q0, q1;
+            const float d = q8_block_regs(a.x + (int64_t)blk * 32, q0, q1);
+            uint4* o = reinterpret_cast<uint4*>(a.qx + (int64_t)blk * 32);
+            o[0] = q0;
+            o[1] = q1;
+            a.dx[blk] = d;
+        }
+    }
 }
 
-// B: routed gate/up, blocks = (unique expert u, h-block hb), u < min(E, T*K).
-template <int NT, int NBJ, bool TAP>
-__global__ __launch_bounds__(512) void k_dec_gateup(DecArgs a) {
+// B: blocks [0, S*nrb) shared-expert h-blocks, then (u, hb) for the u-th
+// expert in use (u < min(E, T*K)); block (u = 0, hb = 0) publishes routing.
+template <int NT, int NBJ, int EPL, bool TAP>
+__global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
+    __shared__ Route R;
     __shared__ float hbuf[NT][32];
+    __shared__ int s_tok[NT];
     const int nrb = a.I >> 5;
-    const int u = blockIdx.x / nrb, hb = blockIdx.x - u * nrb;
-    const int nu = __builtin_amdgcn_readfirstlane(a.uinfo[0]);
-    if (u >= nu) return;
-    const int e = __builtin_amdgcn_readfirstlane(a.uinfo[1 + 3 * u]);
-    const int s0 = __builtin_amdgcn_readfirstlane(a.uinfo[2 + 3 * u]);
-    const int n = __builtin_amdgcn_readfirstlane(a.uinfo[3 + 3 * u]);
-    int tok[NT];
-#pragma unroll
-    for (int i = 0; i < NT; ++i) tok[i] = (NT == 1) ? 0 : a.slot_tok[s0 + ((i < n) ? i : 0)];
-    const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
-    const uint8_t* up = gate + (int64_t)a.I * (a.H >> 1);
-    const float* gs = a.es + (int64_t)e * a.blob_s;
-    gateup_block<NT, NBJ, TAP>(gate, up, gs, gs + a.I, a.H, a.I, hb, n, a.qx, a.dx, tok, s0,
-                               a.qh, a.dh, a.tap, a.tap_rows, a.tap_stride, hbuf);
+    int b = blockIdx.x;
+    if (a.S) {
+        if (b < nrb) {
+            if ((int)threadIdx.x < NT) s_tok[threadIdx.x] = threadIdx.x;
+            __syncthreads();
+            gateup_block<NT, NBJ, TAP>(a, a.E, b, a.T, s_tok, a.T * a.K, hbuf);
+            return;
+        }
+        b -= nrb;
+    }
+    route_small<EPL>(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R);
+    if (b == 0) publish_route(a, R);
+    const int u = b / nrb, hb = b - u * nrb;
+    if (u >= R.n_uniq) return;
+    const int e = __builtin_amdgcn_readfirstlane(R.u_e[u]);
+    const int s0 = __builtin_amdgcn_readfirstlane(R.u_s0[u]);
+    const int n = __builtin_amdgcn_readfirstlane(R.u_n[u]);
+    gateup_block<NT, NBJ, TAP>(a, e, hb, n, &R.ent_t[s0], s0, hbuf);
 }
 
 // C: down projection of every expert in use and the weighted combine.
-// A workgroup owns 8 output rows and has one wave per expert in use (up to
-// 16; more are taken in rounds): each wave requests its expert's 8 rows and
-// activation blocks at once, reduces 8 rows x NT tokens, and leaves the
-// weighted fp64 contributions in LDS; the combine sums them per row in
-// ascending expert order (shared expert last).
-template <int NT, int NBJ>
-__global__ __launch_bounds__(1024) void k_dec_down(DecArgs a) {
-    constexpr int RPG = 8;
+// Workgroup = 4 waves x RPW rows; lane l owns block l (+64 j) of a down row.
+// Experts are taken NB at a time: all their rows and activation blocks are
+// requested before any is used (unconditional loads, clamped indices), then
+// reduced. Each wave accumulates its rows' combine in LDS (fp64), in
+// ascending expert order with the shared expert last.
+template <int NT, int NBJ, int RPW, int NB>
+__global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
     __shared__ int s_e[kMaxEntries + 1], s_s0[kMaxEntries + 1], s_n[kMaxEntries + 1];
     __shared__ float s_w[kMaxEntries + kMaxTok];
     __shared__ int s_t[kMaxEntries + kMaxTok];
-    __shared__ double s_part[kMaxEntries + 1][RPG][NT];
+    __shared__ double s_acc[4 * RPW][NT];
     __shared__ int s_nu;
     const int T = a.T, K = a.K, E = a.E, S = a.S, H = a.H, I = a.I;
     const int BI = I >> 5;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int nwave = blockDim.x >> 6;
     const int n_ent = T * K;
-    const int c0 = blockIdx.x * RPG;
-    int bcl[NBJ];
-#pragma unroll
-    for (int j = 0; j < NBJ; ++j) bcl[j] = min(lane + 64 * j, BI - 1);
-    // expert of this wave in round 0, straight from the workspace (no LDS round trip)
-    const int nu_r = __builtin_amdgcn_readfirstlane(a.uinfo[0]);
-    const int nu = nu_r + S;
-    auto expert_of = [&](int v, int& e, int& s0, int& n) {
-        if (v < nu_r) {
-            e = __builtin_amdgcn_readfirstlane(a.uinfo[1 + 3 * v]);
-            s0 = __builtin_amdgcn_readfirstlane(a.uinfo[2 + 3 * v]);
-            n = __builtin_amdgcn_readfirstlane(a.uinfo[3 + 3 * v]);
-        } else {
-            e = E;
-            s0 = n_ent;
-            n = T;
+    if (threadIdx.x == 0) {
+        int nu = a.uinfo[0];
+        for (int v = 0; v < nu; ++v) {
+            s_e[v] = a.uinfo[1 + 3 * v];
+            s_s0[v] = a.uinfo[2 + 3 * v];
+            s_n[v] = a.uinfo[3 + 3 * v];
         }
-    };
-    for (int i = threadIdx.x; i < n_ent + S * T; i += blockDim.x) {
+        if (S) {
+            s_e[nu] = E;
+            s_s0[nu] = n_ent;
+            s_n[nu] = T;
+            ++nu;
+        }
+        s_nu = nu;
+    }
+    for (int i = threadIdx.x; i < n_ent + S * T; i += 256) {
         s_w[i] = (i < n_ent) ? reinterpret_cast<const float*>(a.uinfo + kUinfoW)[i] : 1.0f;
         s_t[i] = a.slot_tok[i];
     }
-    for (int i = threadIdx.x; i < nu * RPG * NT; i += blockDim.x) (&s_part[0][0][0])[i] = 0.0;
+    if (threadIdx.x < 4 * RPW * NT) (&s_acc[0][0])[threadIdx.x] = 0.0;
     __syncthreads();
-    constexpr int V = RPG * NT;
-    constexpr int kLog = (V >= 32) ? 5 : (V >= 16) ? 4 : 3;
+    const int c0 = blockIdx.x * (4 * RPW) + wave * RPW;
+    const int nu = __builtin_amdgcn_readfirstlane(s_nu);
+    int bcl[NBJ];
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j) bcl[j] = min(lane + 64 * j, BI - 1);
+    constexpr int V = RPW * NT;
+    constexpr int kLog = (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
     constexpr int kShift = 6 - kLog;
 #pragma unroll 1
-    for (int v = wave; v < nu; v += nwave) {
-        int e, s0, n;
-        expert_of(v, e, s0, n);
-        const uint8_t* down = a.eq + (int64_t)e * a.blob_q + (int64_t)I * H;
-        uint4 w[RPG][NBJ];
+    for (int v0 = 0; v0 < nu; v0 += NB) {
+        uint4 w[NB][RPW][NBJ];
+        uint4 ha[NB][NT][NBJ][2];
+        float hdf[NB][NT][NBJ];
+        float dsv[NB][RPW];
 #pragma unroll
-        for (int r = 0; r < RPG; ++r)
+        for (int bi = 0; bi < NB; ++bi) {
+            const int v = min(v0 + bi, nu - 1);
+            const int ev = __builtin_amdgcn_readfirstlane(s_e[v]);
+            const uint8_t* down = a.eq + (int64_t)ev * a.blob_q + (int64_t)I * H;
 #pragma unroll
-            for (int j = 0; j < NBJ; ++j)
-                w[r][j] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl[j] * 16);
-        const float* ds = a.es + (int64_t)e * a.blob_s + 2 * I;
-        float dsv[RPG];
+            for (int r = 0; r < RPW; ++r)
 #pragma unroll
-        for (int r = 0; r < RPG; ++r) dsv[r] = ds[c0 + r];
-        uint4 ha[NT][NBJ][2];
-        double hd[NT][NBJ];
+                for (int j = 0; j < NBJ; ++j)
+                    w[bi][r][j] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl[j] * 16);
+        }
 #pragma unroll
-        for (int i = 0; i < NT; ++i) {
-            const int sl = s0 + min(i, n - 1);
+        for (int bi = 0; bi < NB; ++bi) {
+            const int v = min(v0 + bi, nu - 1);
+            const int ev = __builtin_amdgcn_readfirstlane(s_e[v]);
+            const int s0 = __builtin_amdgcn_readfirstlane(s_s0[v]);
+            const int n = __builtin_amdgcn_readfirstlane(s_n[v]);
+            const float* ds = a.es + (int64_t)ev * a.blob_s + 2 * I;
 #pragma unroll
-            for (int j = 0; j < NBJ; ++j) {
-                const bool ok = i < n && lane + 64 * j < BI;
-                const uint4* p = reinterpret_cast<const uint4*>(a.qh + (int64_t)sl * I + bcl[j] * 32);
-                ha[i][j][0] = p[0];
-                ha[i][j][1] = p[1];
-                const float d = a.dh[(int64_t)sl * BI + bcl[j]];
-                hd[i][j] = ok ? (double)d * 0.0625 : 0.0;
+            for (int r = 0; r < RPW; ++r) dsv[bi][r] = ds[c0 + r];
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const int sl = s0 + min(i, n - 1);
+#pragma unroll
+                for (int j = 0; j < NBJ; ++j) {
+                    const uint4* p = reinterpret_cast<const uint4*>(a.qh + (int64_t)sl * I + bcl[j] * 32);
+                    ha[bi][i][j][0] = p[0];
+                    ha[bi][i][j][1] = p[1];
+                    hdf[bi][i][j] = a.dh[(int64_t)sl * BI + bcl[j]];
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        double vals[V];
 #pragma unroll
-        for (int r = 0; r < RPG; ++r)
+        for (int bi = 0; bi < NB; ++bi) {
+            const int v = v0 + bi;
+            if (v >= nu) break;
+            const int s0 = __builtin_amdgcn_readfirstlane(s_s0[v]);
+            const int n = __builtin_amdgcn_readfirstlane(s_n[v]);
+            double vals[V];
 #pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                double p = 0.0;
+            for (int r = 0; r < RPW; ++r)
 #pragma unroll
-                for (int j = 0; j < NBJ; ++j)
-                    p += hd[i][j] * (double)dot_block16(w[r][j], ha[i][j][0], ha[i][j][1]);
-                vals[r * NT + i] = p;
+                for (int i = 0; i < NT; ++i) {
+                    double p = 0.0;
+#pragma unroll
+                    for (int j = 0; j < NBJ; ++j) {
+                        const bool ok = i < n && lane + 64 * j < BI;
+                        const double hd = ok ? (double)hdf[bi][i][j] * 0.0625 : 0.0;
+                        p += hd * (double)dot_block16(w[bi][r][j], ha[bi][i][j][0], ha[bi][i][j][1]);
+                    }
+                    vals[r * NT + i] = p;
+                }
+            const double sum = wave_reduce_tr<V>(vals, lane);
+            const int vi = lane >> kShift;
+            if (lane == (vi << kShift)) {
+                const int r = vi / NT, i = vi - r * NT;
+                if (i < n) {
+                    float dsr = dsv[bi][0];
+#pragma unroll
+                    for (int rr = 1; rr < RPW; ++rr)
+                        if (r == rr) dsr = dsv[bi][rr];
+                    const float yv = (float)((double)dsr * sum);
+                    s_acc[wave * RPW + r][s_t[s0 + i]] += (double)s_w[s0 + i] * (double)yv;
+                }
             }
-        const double sum = wave_reduce_tr<V>(vals, lane);
-        const int vi = lane >> kShift;
-        if (lane == (vi << kShift)) {
-            const int r = vi / NT, i = vi - r * NT;
-            float dsr = dsv[0];
-#pragma unroll
-            for (int rr = 1; rr < RPG; ++rr)
-                if (r == rr) dsr = dsv[rr];
-            const float yv = (float)((double)dsr * sum);
-            if (i < n) s_part[v][r][s_t[s0 + i]] = (double)s_w[s0 + i] * (double)yv;
         }
     }
-    __syncthreads();
-    if (threadIdx.x < RPG * NT) {
-        const int r = threadIdx.x / NT, t = threadIdx.x - r * NT;
-        double acc = 0.0;
-        for (int v = 0; v < nu; ++v) acc += s_part[v][r][t];
+    if (lane < RPW * NT) {
+        const int r = lane / NT, t = lane - r * NT;
         if (t < T) {
             float* out = a.y + (int64_t)t * H + c0 + r;
-            const float yv = (float)acc;
+            const float yv = (float)s_acc[wave * RPW + r][t];
             *out = a.accum ? *out + yv : yv;
         }
     }
