@@ -30,7 +30,10 @@ HBM_PEAK_GBPS = 8000.0
 # WRITE_SIZE (two runs), scaled by what the counters read for a plain device
 # copy of known size (FETCH_SIZE x 2, WRITE_SIZE x 1). Keyed by (kernel,
 # workload); dropped whenever that kernel changes.
-TRAFFIC = {}
+TRAFFIC = {
+    # profiles/dec_kernels_decode_T1.txt
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55672.2 * 2 + 38.4) * 1024,
+}
 
 
 def parse():
@@ -172,7 +175,7 @@ def main():
         ach = gate_up_bytes / (ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                    "traffic": TRAFFIC.get((gk, cfg.name)),
+                    "traffic": (int(TRAFFIC[(gk, cfg.name)]) if (gk, cfg.name) in TRAFFIC else None),
                     "kernel": gk, "bytes_per_launch": int(gate_up_bytes),
                     "avg_launch_us": round(ms * 1e3, 2)}
 
