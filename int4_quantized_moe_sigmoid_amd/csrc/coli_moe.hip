@@ -193,7 +193,7 @@ void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     dec::k_dec_router<NT><<<a.E, 256, 0, s>>>(a);
     mk.mark("dec_gateup");
     const int um = (a.T * a.K < a.E) ? a.T * a.K : a.E;
-    dec::k_dec_gateup<NT, NBJH, 4, TAP><<<(a.S + um) * nrb, 256, 0, s>>>(a);
+    dec::k_dec_gateup<NT, NBJH, TAP><<<(a.S + um) * nrb, 256, 0, s>>>(a);
     mk.mark("dec_down");
     dec::k_dec_down<NT, 1, 2, 4><<<a.H / 8, 256, 0, s>>>(a);
 }

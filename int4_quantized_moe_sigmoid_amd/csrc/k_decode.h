@@ -99,76 +99,100 @@ struct Route {
     int u_e[kMaxEntries];       // unique experts, ascending
     int u_s0[kMaxEntries];      // first sorted entry (= slot) of each
     int u_n[kMaxEntries];       // tokens of each
+    // top-k scratch
+    unsigned long long gmax[kMaxTok][8];  // max key of each 32-expert group
+    int ncand[kMaxTok];
+    unsigned long long ckey[kMaxTok][256];
+    int ce[kMaxTok][256];
+    double cs[kMaxTok][256];
+    double ssel[kMaxTok][16];
 };
 
-// One wave per token: sigmoid + bias, K rounds of wave arg-max (c desc, index
-// asc), gates normalised (k ascending) and scaled, as k_topk.
-template <int EPL>
-__device__ __forceinline__ void route_token_wave(const double* logits, const float* bias, int E, int K, int norm,
-                                 double rho, int t, int lane, Route& R) {
-    double c[EPL], s[EPL];
+// Total order on doubles (no NaN) as unsigned integers.
+__device__ __forceinline__ unsigned long long order_key(double c) {
+    const long long b = __double_as_longlong(c);
+    return (b < 0) ? ~(unsigned long long)b : ((unsigned long long)b | 0x8000000000000000ull);
+}
+
+// Sigmoid + bias + top-k + gate weights of T <= 4 tokens by the whole
+// workgroup (thread e owns expert e, E <= blockDim.x). Selection order is c
+// descending, expert index ascending among equal c; an expert's position is
+// the number of experts ahead of it in that order. Only experts whose c is at
+// least the smallest of the 32-expert group maxima can be among the K largest
+// (when there are >= K groups those maxima are >= K distinct experts), so
+// positions are counted among those few candidates only.
+__device__ __forceinline__ void topk_wg(const double* logits, const float* bias, int T, int E, int K,
+                                        int norm, double rho, Route& R) {
+    const int e = threadIdx.x;
+    const int G = (E + 31) >> 5;
+    const bool filt = G >= K;
+    if (threadIdx.x < kMaxTok * 8) (&R.gmax[0][0])[threadIdx.x] = 0ull;
+    if (threadIdx.x < kMaxTok) R.ncand[threadIdx.x] = 0;
+    double l[kMaxTok];
+    float bb = 0.0f;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-        const int e = lane + 64 * j;
-        if (e < E) {
-            const double l = logits[(int64_t)t * E + e];
-            s[j] = 1.0 / (1.0 + exp(-l));
-            c[j] = s[j] + (double)bias[e];
-        } else {
-            s[j] = 0.0;
-            c[j] = -__builtin_inf();
-        }
+    for (int t = 0; t < kMaxTok; ++t) l[t] = (t < T && e < E) ? logits[(int64_t)t * E + e] : 0.0;
+    if (e < E) bb = bias[e];
+    __syncthreads();
+    unsigned long long key[kMaxTok];
+    double s[kMaxTok];
+#pragma unroll
+    for (int t = 0; t < kMaxTok; ++t) {
+        s[t] = 1.0 / (1.0 + exp(-l[t]));
+        key[t] = order_key(s[t] + (double)bb);
+        if (filt && t < T && e < E) atomicMax(&R.gmax[t][e >> 5], key[t]);
     }
-    uint32_t taken = 0;
-    int my_e = 0;
-    double my_s = 0.0;
-    for (int k = 0; k < K; ++k) {
-        double bc = -__builtin_inf(), bs = 0.0;
-        int be = 0x7fffffff;
+    __syncthreads();
 #pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = lane + 64 * j;
-            if (e < E && !((taken >> j) & 1u) && (c[j] > bc || (c[j] == bc && e < be))) {
-                bc = c[j];
-                be = e;
-                bs = s[j];
+    for (int t = 0; t < kMaxTok; ++t) {
+        if (t < T && e < E) {
+            unsigned long long thr = 0ull;
+            if (filt) {
+                thr = ~0ull;
+                for (int g = 0; g < G; ++g) thr = min(thr, R.gmax[t][g]);
+            }
+            if (key[t] >= thr) {
+                const int p = atomicAdd(&R.ncand[t], 1);
+                R.ckey[t][p] = key[t];
+                R.ce[t][p] = e;
+                R.cs[t][p] = s[t];
             }
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const double oc = __shfl_xor(bc, o, 64);
-            const int oe = __shfl_xor(be, o, 64);
-            const double os = __shfl_xor(bs, o, 64);
-            if (oc > bc || (oc == bc && oe < be)) {
-                bc = oc;
-                be = oe;
-                bs = os;
+    }
+    __syncthreads();
+    for (int t = 0; t < T; ++t) {
+        const int m = R.ncand[t];
+        for (int i = threadIdx.x; i < m; i += blockDim.x) {
+            const unsigned long long ki = R.ckey[t][i];
+            const int ei = R.ce[t][i];
+            int rank = 0;
+            for (int j = 0; j < m; ++j) {
+                const unsigned long long kj = R.ckey[t][j];
+                rank += (kj > ki || (kj == ki && R.ce[t][j] < ei)) ? 1 : 0;
+            }
+            if (rank < K) {
+                R.idx[t][rank] = ei;
+                R.ssel[t][rank] = R.cs[t][i];
             }
         }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-        if (lane == k) {
-            my_e = be;
-            my_s = bs;
-        }
     }
-    double sum = 0.0;
-    for (int k = 0; k < K; ++k) sum += __shfl(my_s, k, 64);
-    if (lane < K) {
-        double v = my_s;
+    __syncthreads();
+    if ((int)threadIdx.x < T * K) {
+        const int t = threadIdx.x / K, k = threadIdx.x - t * K;
+        double sum = 0.0;
+        for (int kk = 0; kk < K; ++kk) sum += R.ssel[t][kk];
+        double v = R.ssel[t][k];
         if (norm) v = v / sum;
         v = v * rho;
-        R.idx[t][lane] = my_e;
-        R.w[t][lane] = (float)v;
+        R.w[t][k] = (float)v;
     }
 }
 
-// Fills R (in LDS) for T tokens; must be called by the whole workgroup (>= 64
-// threads, T <= 4 waves route).
-template <int EPL>
+// Fills R (in LDS) for T tokens; must be called by the whole workgroup
+// (blockDim.x >= E).
 __device__ __forceinline__ void route_small(const double* logits, const float* bias, int T, int E, int K, int S,
                             int norm, double rho, Route& R) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (wave < T) route_token_wave<EPL>(logits, bias, E, K, norm, rho, wave, lane, R);
+    topk_wg(logits, bias, T, E, K, norm, rho, R);
     __syncthreads();
     const int n = T * K;
     const int i = threadIdx.x;
@@ -442,7 +466,7 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
 
 // B: blocks [0, S*nrb) shared-expert h-blocks, then (u, hb) for the u-th
 // expert in use (u < min(E, T*K)); block (u = 0, hb = 0) publishes routing.
-template <int NT, int NBJ, int EPL, bool TAP>
+template <int NT, int NBJ, bool TAP>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
     __shared__ Route R;
     __shared__ float hbuf[NT][32];
@@ -458,7 +482,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
         }
         b -= nrb;
     }
-    route_small<EPL>(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R);
+    route_small(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R);
     if (b == 0) publish_route(a, R);
     const int u = b / nrb, hb = b - u * nrb;
     if (u >= R.n_uniq) return;

@@ -173,3 +173,35 @@ def test_batching_and_permutation_are_exact(C, ref):
     for t in (0, 7):
         y1, _ = run_gpu(C, W, np.ascontiguousarray(x[t:t + 1]))
         np.testing.assert_array_equal(y1[0], y[t])
+
+
+@pytest.mark.parametrize("n_tok", [1, 2, 4])
+def test_router_ties_on_the_few_token_path(C, ref, n_tok):
+    """Router rows and biases repeat with period 37, so expert e and e + 37
+    have bit-identical scores; the K-th and (K+1)-th choices tie. Both sides
+    must break ties to the lower expert index: index sets equal exactly."""
+    import dataclasses
+    cfg = dataclasses.replace(cs.CONFIGS[0], name="ties E256 K8", n_tok=n_tok, n_experts=256,
+                              top_k=8)
+    _note(cfg.name, n_tok)
+    wr, b, q, s = cs.build_layer(cfg, 0, "cuda", lambda w, qv, sv: C.coli_pack_int4(w, qv, sv))
+    rows = torch.arange(cfg.n_experts, device="cuda") % 37
+    wr, b = wr[rows].contiguous(), b[rows].contiguous()
+    W = C.LayerWeights(lib_cfg(C, cfg), wr, b, q, s)
+    x = layer_input(ref, cfg)
+    y, taps = run_gpu(C, W, x)
+    wrn, bn = wr.cpu().numpy(), b.cpu().numpy()
+    idx, w, _ = ref.route(x, wrn, bn, cfg.top_k, cfg.norm_topk, cfg.rho)
+    # every token's choice contains tied pairs (same row, different expert)
+    assert all(len(set(int(e) % 37 for e in row)) < cfg.top_k for row in idx)
+    np.testing.assert_array_equal(taps["idx"], idx)
+    np.testing.assert_allclose(taps["w"], w, rtol=1e-6)
+    OL = ref.OracleLayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
+                         cfg.norm_topk, cfg.rho, wrn, bn, {})
+    for e in sorted(set(int(v) for v in np.unique(idx)) | {cfg.n_experts}):
+        mats = [cs.expert_matrix(cfg, 0, e, m, "cuda").cpu().numpy() for m in ("gate", "up", "down")]
+        OL.add_expert(e, ref.pack_expert(*mats))
+    yo = OL.forward(x)
+    err = rel_l2(y, yo)
+    _note("rel_l2", err)
+    assert err <= TOL_REL_L2
