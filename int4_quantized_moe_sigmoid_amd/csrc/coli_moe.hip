@@ -11,6 +11,7 @@
 #include "coli_common.h"
 #include "k_decode.h"
 #include "k_gemv.h"
+#include "k_prefill.h"
 #include "k_route.h"
 #include "k_small.h"
 
@@ -285,12 +286,32 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
 
     launch_route(c, x, w->w_router, w->bias, T, logits, idx, wts, s, mk);
 
+    // grouped MFMA path when the row tiles divide the shapes, else the GEMV path
+    const bool mfma = (H % pf::kRows) == 0 && (I % pf::kRows) == 0;
+    const int ch = mfma ? pf::kTok : L.ch;
+    const int64_t n_it = max_items_for(c, T, ch);
     mk.mark("bucket_lists");
     k_bucket_lists<<<E + S, 256, 0, s>>>(idx, (int)T, K, E, S, lists, counts);
     mk.mark("bucket_scan");
-    k_bucket_scan<<<1, 1024, 0, s>>>(counts, lists, (int)T, K, E, S, L.ch, offs, slot_of,
+    k_bucket_scan<<<1, 1024, 0, s>>>(counts, lists, (int)T, K, E, S, ch, offs, slot_of,
                                      slot_tok, it.item_e, it.item_s0, it.item_n, n_items);
 
+    if (mfma) {
+        pf::PfArgs pa{};
+        pa.eq = w->experts_q; pa.es = w->experts_scale; pa.blob_q = blob_q; pa.blob_s = blob_s;
+        pa.H = H; pa.I = I; pa.qx = qx; pa.dx = dx;
+        pa.item_e = it.item_e; pa.item_s0 = it.item_s0; pa.item_n = it.item_n;
+        pa.n_items = it.n_items; pa.slot_tok = slot_tok;
+        pa.qh = qh; pa.dh = dh; pa.ye = ye; pa.tap = tap;
+        pa.tap_rows = (int)L.pub.tap_rows;
+        pa.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
+        mk.mark("pf_gateup");
+        const dim3 g1((unsigned)((I / pf::kRows) * n_it));
+        if (tap) pf::k_pf_gateup<true><<<g1, 256, 0, s>>>(pa);
+        else pf::k_pf_gateup<false><<<g1, 256, 0, s>>>(pa);
+        mk.mark("pf_down");
+        pf::k_pf_down<<<dim3((unsigned)((H / pf::kRows) * n_it)), 256, 0, s>>>(pa);
+    } else {
     const int nt = (T >= L.ch) ? L.ch : (int)T;  // tokens per item at most
     const int nbj_h = (H / 32 + 63) / 64;
     const int nbj_i = (I / 32 + 63) / 64;
@@ -317,6 +338,7 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
             launch_down_nt<2>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye);
         else
             launch_down_nt<4>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye);
+    }
     }
     mk.mark("combine");
     {

@@ -1,0 +1,322 @@
+// Grouped int8 MFMA kernels for many tokens (prefill, stacked layers).
+//
+// Work item = (expert, first slot, n <= 32 of its tokens). A workgroup takes
+// one item and a tile of 64 output rows; wave w owns rows 16w .. 16w+15 of
+// the tile (for gate/up: those gate rows and the matching up rows, so SwiGLU
+// needs no exchange). Per 32-wide block b every wave issues
+//   D = v_mfma_i32_16x16x32_i8(A = 16 weight rows, B = 16 tokens)
+// whose K extent is exactly one Q8_0 block, so D holds 16 x 16 exact block
+// dots (x16, see below); the fp64 epilogue adds d_b * D into per-lane fp64
+// accumulators, which is the numerics of the plain definition (exact block
+// dots, fp64 sum of scaled dots) regardless of tiling.
+//
+// MFMA operand layout (16x16x32 int8, checked on the device): lane l holds
+// row (A) / column (B) l % 16 and k = 8 (l / 16) + i, i = 0..7; result
+// register i of lane l is row 4 (l / 16) + i, column l % 16. A dword of
+// packed int4 codes (8 consecutive elements) becomes an A operand with the
+// x16 nibble trick: (x << 4) & 0xF0F0F0F0 holds 16 * the even elements and
+// x & 0xF0F0F0F0 16 * the odd ones, i.e. the element order (e0 e2 e4 e6 e1
+// e3 e5 e7) in which activations are stored, so B is 8 plain bytes of the
+// activation row.
+//
+// Weight rows are staged per wave through LDS: 16-byte loads along a row
+// (coalesced 256-byte runs), written with a padded pitch so that the 4-byte
+// operand reads of 16 rows x 2 dwords hit 32 distinct banks. Each wave only
+// reads its own staging area, so no barrier is needed (LDS operations of a
+// wave complete in order).
+#pragma once
+
+#include "coli_common.h"
+
+namespace pf {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kTok = 32;              // tokens per work item
+constexpr int kRows = 64;             // output rows per workgroup
+constexpr int kChunk = 16;            // blocks staged per step
+constexpr int kPitch = kChunk * 16 + 8;  // LDS bytes per staged row
+constexpr int kRing = 4;              // activation blocks loaded ahead
+
+struct PfArgs {
+    const uint8_t* eq;
+    const float* es;
+    int64_t blob_q, blob_s;
+    int H, I;
+    const int8_t* qx;      // [T, H] Q8_0 codes of x (8-group order)
+    const float* dx;       // [T, H/32]
+    const int32_t* item_e;
+    const int32_t* item_s0;
+    const int32_t* item_n;
+    const int32_t* n_items;
+    const int32_t* slot_tok;
+    int8_t* qh;            // [slots, I]
+    float* dh;             // [slots, I/32]
+    float* ye;             // [slots, H]
+    int32_t* tap;
+    int tap_rows, tap_stride;
+};
+
+__device__ __forceinline__ long a_operand(uint32_t w) {
+    return (long)(uint32_t)nib_lo16(w) | ((long)(uint32_t)nib_hi16(w) << 32);
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
+    return *reinterpret_cast<const uint32_t*>(p);
+}
+
+// Stages NR rows (row r at src[r / 4 ...]) of one chunk: lane l loads 16
+// bytes of row (l >> 4) + 4k at block (l & 15) of the chunk.
+template <int NR>
+struct Stager {
+    const uint8_t* row[NR / 4];
+    uint4 v[NR / 4];
+    __device__ __forceinline__ void issue(int c, int BH) {
+        const int b = min(c * kChunk + (int)(threadIdx.x & 15), BH - 1);
+#pragma unroll
+        for (int k = 0; k < NR / 4; ++k)
+            v[k] = *reinterpret_cast<const uint4*>(row[k] + b * 16);
+    }
+    __device__ __forceinline__ void commit(uint8_t* lds) const {
+        const int r0 = (threadIdx.x & 63) >> 4, bi = threadIdx.x & 15;
+#pragma unroll
+        for (int k = 0; k < NR / 4; ++k) {
+            uint8_t* d = lds + (r0 + 4 * k) * kPitch + bi * 16;
+            *reinterpret_cast<uint2*>(d) = make_uint2(v[k].x, v[k].y);
+            *reinterpret_cast<uint2*>(d + 8) = make_uint2(v[k].z, v[k].w);
+        }
+    }
+};
+
+// Gate/up + SwiGLU + Q8_0(h) for one item and 64 intermediate rows.
+template <bool TAP>
+__global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
+    __shared__ __align__(16) uint8_t stage[4][32 * kPitch];
+    __shared__ float hbuf[kTok][kRows + 1];
+    const int nrt = a.I / kRows;
+    const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
+    if (it >= *a.n_items) return;
+    const int e = a.item_e[it], s0 = a.item_s0[it], n = a.item_n[it];
+    const int H = a.H, I = a.I, BH = H >> 5;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, q = lane >> 4;
+    const int ng = (n + 15) >> 4;  // 16-token groups in use (1 or 2)
+    const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
+    const uint8_t* up = gate + (int64_t)I * (H >> 1);
+    const int r0 = rt * kRows + wave * 16;
+    uint8_t* lds = stage[wave];
+
+    Stager<32> st;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int r = q + 4 * k;  // staged row: 0..15 gate, 16..31 up
+        st.row[k] = ((r < 16) ? gate : up) + (int64_t)(r0 + (r & 15)) * (H >> 1);
+    }
+    const int8_t* xrow[2];
+    const float* drow[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int j = min(16 * g + lr, n - 1);
+        const int t = a.slot_tok[s0 + j];
+        xrow[g] = a.qx + (int64_t)t * H + 8 * q;
+        drow[g] = a.dx + (int64_t)t * BH;
+    }
+    long rb[kRing][2];
+    float rd[kRing][2];
+    auto load_act = [&](int b, int slot) {
+        const int bc = min(b, BH - 1);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            rb[slot][g] = *reinterpret_cast<const long*>(xrow[g] + bc * 32);
+            rd[slot][g] = drow[g][bc];
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) load_act(s, s);
+
+    double accg[2][4], accu[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accg[g][i] = accu[g][i] = 0.0;
+    const v4i zero = {0, 0, 0, 0};
+
+    const int nch = (BH + kChunk - 1) / kChunk;
+    st.issue(0, BH);
+    st.commit(lds);
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) st.issue(c + 1, BH);
+#pragma unroll
+        for (int bi = 0; bi < kChunk; ++bi) {
+            const int b = c * kChunk + bi;
+            const int slot = bi % kRing;
+            const long ag = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
+            const long au = a_operand(lds_u32(lds + (16 + lr) * kPitch + bi * 16 + 4 * q));
+            long bv[2];
+            double dd[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                bv[g] = rb[slot][g];
+                dd[g] = (b < BH) ? (double)rd[slot][g] * 0.0625 : 0.0;  // d/16 undoes the x16
+            }
+            load_act(b + kRing, slot);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                if (g < ng) {
+                    const v4i cg = __builtin_amdgcn_mfma_i32_16x16x32_i8(ag, bv[g], zero, 0, 0, 0);
+                    const v4i cu = __builtin_amdgcn_mfma_i32_16x16x32_i8(au, bv[g], zero, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        accg[g][i] += dd[g] * (double)cg[i];
+                        accu[g][i] += dd[g] * (double)cu[i];
+                    }
+                    if (TAP) {
+                        const int j = 16 * g + lr;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = r0 + 4 * q + i;
+                            if (j < n && b < BH && (r % a.tap_stride) == 0)
+                                a.tap[((int64_t)(s0 + j) * a.tap_rows + r / a.tap_stride) * BH + b] =
+                                    cg[i] / 16;
+                        }
+                    }
+                }
+            }
+        }
+        if (c + 1 < nch) st.commit(lds);
+    }
+
+    // SwiGLU, then Q8_0 over each 32 consecutive h rows of a token
+    const float* gs = a.es + (int64_t)e * a.blob_s;
+    const float* us = gs + I;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = r0 + 4 * q + i;
+        const float gsr = gs[r], usr = us[r];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const float gv = (float)((double)gsr * accg[g][i]);
+            const float uv = (float)((double)usr * accu[g][i]);
+            hbuf[16 * g + lr][wave * 16 + 4 * q + i] = swiglu_f32(gv, uv);
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < 2 * n) {
+        const int j = threadIdx.x >> 1, kb = threadIdx.x & 1;
+        const float* hv = &hbuf[j][32 * kb];
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(hv[k]));
+        const float d = amax / 127.0f;
+        uint32_t w[8];
+#pragma unroll
+        for (int g8 = 0; g8 < 4; ++g8) {
+            const float* v = hv + 8 * g8;
+            w[2 * g8] = pack4_i8(q8_code(v[0], d), q8_code(v[2], d), q8_code(v[4], d),
+                                 q8_code(v[6], d));
+            w[2 * g8 + 1] = pack4_i8(q8_code(v[1], d), q8_code(v[3], d), q8_code(v[5], d),
+                                     q8_code(v[7], d));
+        }
+        uint4* o = reinterpret_cast<uint4*>(a.qh + (int64_t)(s0 + j) * I + rt * kRows + 32 * kb);
+        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        a.dh[(int64_t)(s0 + j) * (I >> 5) + rt * 2 + kb] = d;
+    }
+}
+
+// Down projection for one item and 64 output rows: ye[slot, row] =
+// fp32(s_down[row] * sum_b d_h,b * I_b).
+__global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
+    __shared__ __align__(16) uint8_t stage[4][16 * kPitch];
+    __shared__ float ybuf[kTok][kRows + 1];
+    const int nrt = a.H / kRows;
+    const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
+    if (it >= *a.n_items) return;
+    const int e = a.item_e[it], s0 = a.item_s0[it], n = a.item_n[it];
+    const int H = a.H, I = a.I, BI = I >> 5;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, q = lane >> 4;
+    const int ng = (n + 15) >> 4;
+    const uint8_t* down = a.eq + (int64_t)e * a.blob_q + (int64_t)I * H;
+    const int r0 = rt * kRows + wave * 16;
+    uint8_t* lds = stage[wave];
+
+    Stager<16> st;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) st.row[k] = down + (int64_t)(r0 + q + 4 * k) * (I >> 1);
+    const int8_t* hrow[2];
+    const float* drow[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int j = min(16 * g + lr, n - 1);
+        hrow[g] = a.qh + (int64_t)(s0 + j) * I + 8 * q;
+        drow[g] = a.dh + (int64_t)(s0 + j) * BI;
+    }
+    long rb[kRing][2];
+    float rd[kRing][2];
+    auto load_act = [&](int b, int slot) {
+        const int bc = min(b, BI - 1);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            rb[slot][g] = *reinterpret_cast<const long*>(hrow[g] + bc * 32);
+            rd[slot][g] = drow[g][bc];
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) load_act(s, s);
+
+    double acc[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[g][i] = 0.0;
+    const v4i zero = {0, 0, 0, 0};
+
+    const int nch = (BI + kChunk - 1) / kChunk;
+    st.issue(0, BI);
+    st.commit(lds);
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) st.issue(c + 1, BI);
+#pragma unroll
+        for (int bi = 0; bi < kChunk; ++bi) {
+            const int b = c * kChunk + bi;
+            const int slot = bi % kRing;
+            const long aw = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
+            long bv[2];
+            double dd[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                bv[g] = rb[slot][g];
+                dd[g] = (b < BI) ? (double)rd[slot][g] * 0.0625 : 0.0;
+            }
+            load_act(b + kRing, slot);
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                if (g < ng) {
+                    const v4i cd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw, bv[g], zero, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[g][i] += dd[g] * (double)cd[i];
+                }
+            }
+        }
+        if (c + 1 < nch) st.commit(lds);
+    }
+
+    const float* ds = a.es + (int64_t)e * a.blob_s + 2 * I;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rl = wave * 16 + 4 * q + i;
+        const float dsr = ds[rt * kRows + rl];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) ybuf[16 * g + lr][rl] = (float)((double)dsr * acc[g][i]);
+    }
+    __syncthreads();
+    for (int v = threadIdx.x; v < n * kRows; v += 256) {
+        const int j = v >> 6, r = v & 63;
+        a.ye[(int64_t)(s0 + j) * H + rt * kRows + r] = ybuf[j][r];
+    }
+}
+
+}  // namespace pf
