@@ -19,11 +19,11 @@
 // e3 e5 e7) in which activations are stored, so B is 8 plain bytes of the
 // activation row.
 //
-// Weight rows are staged per wave through LDS: 16-byte loads along a row
-// (coalesced 256-byte runs), written with a padded pitch so that the 4-byte
-// operand reads of 16 rows x 2 dwords hit 32 distinct banks. Each wave only
-// reads its own staging area, so no barrier is needed (LDS operations of a
-// wave complete in order).
+// Both operands go through LDS in chunks of 16 blocks, loaded one chunk
+// ahead into registers with coalesced 16-byte loads: weight rows per wave
+// (each wave reads only its own rows), the item's activation rows and block
+// scales once per workgroup (all four waves use the same tokens). Pitches
+// are padded so the operand reads hit distinct banks.
 #pragma once
 
 #include "coli_common.h"
@@ -36,7 +36,10 @@ constexpr int kTok = 32;              // tokens per work item
 constexpr int kRows = 64;             // output rows per workgroup
 constexpr int kChunk = 16;            // blocks staged per step
 constexpr int kPitch = kChunk * 16 + 8;  // LDS bytes per staged row
-constexpr int kRing = 4;              // activation blocks loaded ahead
+constexpr int kActPitch = kChunk * 32 + 16;  // LDS bytes per staged activation row
+constexpr int kDPitch = kChunk + 1;          // floats per staged scale row
+constexpr int kActBytes = kTok * kActPitch;
+constexpr int kDBytes = kTok * kDPitch * 4;
 
 struct PfArgs {
     const uint8_t* eq;
@@ -88,11 +91,56 @@ struct Stager {
     }
 };
 
+// Activation rows of the item's 32 tokens (rows of a [*, NB * 32] int8
+// matrix in 8-group order, with NB block scales per row), one chunk of 16
+// blocks: thread tid loads the 16-byte half (tid & 1) of block (tid & 31) >> 1
+// of token rows (tid >> 5) + 8k, and threads < 128 four block scales.
+struct ActStager {
+    const int8_t* row[4];
+    const float* drow;
+    uint4 v[4];
+    float dv[4];
+    __device__ __forceinline__ void init(const int8_t* base, const float* dbase, int64_t pitch,
+                                         int NB, const int32_t* rows_of, int n) {
+        const int half = threadIdx.x & 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = min((int)(threadIdx.x >> 5) + 8 * k, n - 1);
+            row[k] = base + (int64_t)rows_of[j] * pitch + 16 * half;
+        }
+        const int jd = min((int)(threadIdx.x >> 2), n - 1);
+        drow = dbase + (int64_t)rows_of[jd] * NB;
+    }
+    __device__ __forceinline__ void issue(int c, int NB) {
+        const int b = min(c * kChunk + (int)((threadIdx.x & 31) >> 1), NB - 1);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const uint4*>(row[k] + b * 32);
+        if (threadIdx.x < 128) {
+            const int b0 = c * kChunk + (threadIdx.x & 3) * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dv[i] = drow[min(b0 + i, NB - 1)];
+        }
+    }
+    __device__ __forceinline__ void commit(uint8_t* act, float* dbuf) const {
+        const int blk = (threadIdx.x & 31) >> 1, half = threadIdx.x & 1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = (threadIdx.x >> 5) + 8 * k;
+            *reinterpret_cast<uint4*>(act + j * kActPitch + blk * 32 + 16 * half) = v[k];
+        }
+        if (threadIdx.x < 128) {
+            const int j = threadIdx.x >> 2, b0 = (threadIdx.x & 3) * 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dbuf[j * kDPitch + b0 + i] = dv[i];
+        }
+    }
+};
+
 // Gate/up + SwiGLU + Q8_0(h) for one item and 64 intermediate rows.
 template <bool TAP>
 __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
-    __shared__ __align__(16) uint8_t stage[4][32 * kPitch];
-    __shared__ float hbuf[kTok][kRows + 1];
+    constexpr int kW = 32 * kPitch;  // per-wave weight staging (16 gate + 16 up rows)
+    __shared__ __align__(16) uint8_t smem[4 * kW + kActBytes + kDBytes];
     const int nrt = a.I / kRows;
     const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
     if (it >= *a.n_items) return;
@@ -105,7 +153,9 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
     const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
     const uint8_t* up = gate + (int64_t)I * (H >> 1);
     const int r0 = rt * kRows + wave * 16;
-    uint8_t* lds = stage[wave];
+    uint8_t* lds = smem + wave * kW;
+    uint8_t* act = smem + 4 * kW;
+    float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + kActBytes);
 
     Stager<32> st;
 #pragma unroll
@@ -113,27 +163,8 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
         const int r = q + 4 * k;  // staged row: 0..15 gate, 16..31 up
         st.row[k] = ((r < 16) ? gate : up) + (int64_t)(r0 + (r & 15)) * (H >> 1);
     }
-    const int8_t* xrow[2];
-    const float* drow[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int j = min(16 * g + lr, n - 1);
-        const int t = a.slot_tok[s0 + j];
-        xrow[g] = a.qx + (int64_t)t * H + 8 * q;
-        drow[g] = a.dx + (int64_t)t * BH;
-    }
-    long rb[kRing][2];
-    float rd[kRing][2];
-    auto load_act = [&](int b, int slot) {
-        const int bc = min(b, BH - 1);
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            rb[slot][g] = *reinterpret_cast<const long*>(xrow[g] + bc * 32);
-            rd[slot][g] = drow[g][bc];
-        }
-    };
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) load_act(s, s);
+    ActStager as;
+    as.init(a.qx, a.dx, H, BH, a.slot_tok + s0, n);
 
     double accg[2][4], accu[2][4];
 #pragma unroll
@@ -144,35 +175,34 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
 
     const int nch = (BH + kChunk - 1) / kChunk;
     st.issue(0, BH);
+    as.issue(0, BH);
     st.commit(lds);
+    as.commit(act, dbuf);
+    __syncthreads();
     for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) st.issue(c + 1, BH);
+        if (c + 1 < nch) {
+            st.issue(c + 1, BH);
+            as.issue(c + 1, BH);
+        }
 #pragma unroll
         for (int bi = 0; bi < kChunk; ++bi) {
             const int b = c * kChunk + bi;
-            const int slot = bi % kRing;
             const long ag = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
             const long au = a_operand(lds_u32(lds + (16 + lr) * kPitch + bi * 16 + 4 * q));
-            long bv[2];
-            double dd[2];
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                bv[g] = rb[slot][g];
-                dd[g] = (b < BH) ? (double)rd[slot][g] * 0.0625 : 0.0;  // d/16 undoes the x16
-            }
-            load_act(b + kRing, slot);
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
                 if (g < ng) {
-                    const v4i cg = __builtin_amdgcn_mfma_i32_16x16x32_i8(ag, bv[g], zero, 0, 0, 0);
-                    const v4i cu = __builtin_amdgcn_mfma_i32_16x16x32_i8(au, bv[g], zero, 0, 0, 0);
+                    const int j = 16 * g + lr;
+                    const long bv = *reinterpret_cast<const long*>(act + j * kActPitch + bi * 32 + 8 * q);
+                    const double dd = (b < BH) ? (double)dbuf[j * kDPitch + bi] * 0.0625 : 0.0;
+                    const v4i cg = __builtin_amdgcn_mfma_i32_16x16x32_i8(ag, bv, zero, 0, 0, 0);
+                    const v4i cu = __builtin_amdgcn_mfma_i32_16x16x32_i8(au, bv, zero, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        accg[g][i] += dd[g] * (double)cg[i];
-                        accu[g][i] += dd[g] * (double)cu[i];
+                        accg[g][i] += dd * (double)cg[i];
+                        accu[g][i] += dd * (double)cu[i];
                     }
                     if (TAP) {
-                        const int j = 16 * g + lr;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int r = r0 + 4 * q + i;
@@ -184,8 +214,15 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
                 }
             }
         }
-        if (c + 1 < nch) st.commit(lds);
+        if (c + 1 < nch) {
+            __syncthreads();
+            st.commit(lds);
+            as.commit(act, dbuf);
+            __syncthreads();
+        }
     }
+    __syncthreads();  // the activation area is reused for h below
+    float (*hbuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(act);
 
     // SwiGLU, then Q8_0 over each 32 consecutive h rows of a token
     const float* gs = a.es + (int64_t)e * a.blob_s;
@@ -228,8 +265,8 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
 // Down projection for one item and 64 output rows: ye[slot, row] =
 // fp32(s_down[row] * sum_b d_h,b * I_b).
 __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
-    __shared__ __align__(16) uint8_t stage[4][16 * kPitch];
-    __shared__ float ybuf[kTok][kRows + 1];
+    constexpr int kW = 16 * kPitch;
+    __shared__ __align__(16) uint8_t smem[4 * kW + kActBytes + kDBytes];
     const int nrt = a.H / kRows;
     const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
     if (it >= *a.n_items) return;
@@ -241,31 +278,19 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     const int ng = (n + 15) >> 4;
     const uint8_t* down = a.eq + (int64_t)e * a.blob_q + (int64_t)I * H;
     const int r0 = rt * kRows + wave * 16;
-    uint8_t* lds = stage[wave];
+    uint8_t* lds = smem + wave * kW;
+    uint8_t* act = smem + 4 * kW;
+    float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + kActBytes);
 
     Stager<16> st;
 #pragma unroll
     for (int k = 0; k < 4; ++k) st.row[k] = down + (int64_t)(r0 + q + 4 * k) * (I >> 1);
-    const int8_t* hrow[2];
-    const float* drow[2];
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int j = min(16 * g + lr, n - 1);
-        hrow[g] = a.qh + (int64_t)(s0 + j) * I + 8 * q;
-        drow[g] = a.dh + (int64_t)(s0 + j) * BI;
-    }
-    long rb[kRing][2];
-    float rd[kRing][2];
-    auto load_act = [&](int b, int slot) {
-        const int bc = min(b, BI - 1);
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            rb[slot][g] = *reinterpret_cast<const long*>(hrow[g] + bc * 32);
-            rd[slot][g] = drow[g][bc];
-        }
-    };
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) load_act(s, s);
+    // the item's slots are consecutive rows of q_h
+    __shared__ int s_rows[kTok];
+    if (threadIdx.x < kTok) s_rows[threadIdx.x] = s0 + threadIdx.x;
+    __syncthreads();
+    ActStager as;
+    as.init(a.qh, a.dh, I, BI, s_rows, n);
 
     double acc[2][4];
 #pragma unroll
@@ -276,33 +301,40 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
 
     const int nch = (BI + kChunk - 1) / kChunk;
     st.issue(0, BI);
+    as.issue(0, BI);
     st.commit(lds);
+    as.commit(act, dbuf);
+    __syncthreads();
     for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) st.issue(c + 1, BI);
+        if (c + 1 < nch) {
+            st.issue(c + 1, BI);
+            as.issue(c + 1, BI);
+        }
 #pragma unroll
         for (int bi = 0; bi < kChunk; ++bi) {
             const int b = c * kChunk + bi;
-            const int slot = bi % kRing;
             const long aw = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
-            long bv[2];
-            double dd[2];
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                bv[g] = rb[slot][g];
-                dd[g] = (b < BI) ? (double)rd[slot][g] * 0.0625 : 0.0;
-            }
-            load_act(b + kRing, slot);
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
                 if (g < ng) {
-                    const v4i cd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw, bv[g], zero, 0, 0, 0);
+                    const int j = 16 * g + lr;
+                    const long bv = *reinterpret_cast<const long*>(act + j * kActPitch + bi * 32 + 8 * q);
+                    const double dd = (b < BI) ? (double)dbuf[j * kDPitch + bi] * 0.0625 : 0.0;
+                    const v4i cd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw, bv, zero, 0, 0, 0);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[g][i] += dd[g] * (double)cd[i];
+                    for (int i = 0; i < 4; ++i) acc[g][i] += dd * (double)cd[i];
                 }
             }
         }
-        if (c + 1 < nch) st.commit(lds);
+        if (c + 1 < nch) {
+            __syncthreads();
+            st.commit(lds);
+            as.commit(act, dbuf);
+            __syncthreads();
+        }
     }
+    __syncthreads();  // the activation area is reused for y below
+    float (*ybuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(act);
 
     const float* ds = a.es + (int64_t)e * a.blob_s + 2 * I;
 #pragma unroll
