@@ -9,8 +9,8 @@ seeded token and the next of R layer replicas (distinct seeded weights), so
 the 256 MB Infinity Cache never serves a previous step's weights.
 
 Prints one JSON line (see the fields below). Options: --config picks another
-workload (0 tiny, 1 decode, 2 MTP verify T=3, 3 prefill T=512); --gpus must
-be 1 (this build runs on one GPU).
+workload (0 tiny, 1 decode, 2 MTP verify T=3, 3 prefill T=512, 4 the 8-layer
+pre-norm residual stack at T=4096); --gpus must be 1 (one GPU).
 """
 from __future__ import annotations
 
@@ -84,9 +84,8 @@ def main():
     torch.cuda.set_device(0)
     cfg = cs.CONFIGS[args.config]
     if cfg.n_layers > 1:
-        print(json.dumps({"error": "the layer-stack workload has its own script path; "
-                                   "use --config 0..3"}))
-        sys.exit(2)
+        run_stack(args, cfg)
+        return
     T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
     lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho)
     R = max(1, args.replicas)
@@ -166,18 +165,7 @@ def main():
     step_bytes = uniq_avg * eb + 4 * E * H + 4 * E + 8 * T * H
     weight_gbps = uniq_avg * eb / (ms_per_step * 1e-3) / 1e9
 
-    roofline = None
-    gk = "dec_gateup" if "dec_gateup" in kern else ("gateup" if "gateup" in kern else None)
-    if gk is not None:
-        if gk == "dec_gateup":
-            gate_up_bytes += 8 * T * E
-        ms = kern[gk]
-        ach = gate_up_bytes / (ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                    "traffic": (int(TRAFFIC[(gk, cfg.name)]) if (gk, cfg.name) in TRAFFIC else None),
-                    "kernel": gk, "bytes_per_launch": int(gate_up_bytes),
-                    "avg_launch_us": round(ms * 1e3, 2)}
+    roofline = gateup_roofline(kern, cfg, gate_up_bytes, T)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -199,6 +187,111 @@ def main():
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def gateup_roofline(kern, cfg, gate_up_bytes, T):
+    """Roofline of the gate/up kernel (the dominant launch of every path):
+    algorithmic HBM bytes per launch / its mean event-timed duration."""
+    gk = next((k for k in ("dec_gateup", "pf_gateup", "gateup") if k in kern), None)
+    if gk is None:
+        return None
+    if gk == "dec_gateup":
+        gate_up_bytes += 8 * T * cfg.n_experts  # the fp64 logits the kernel reads
+    ms = kern[gk]
+    ach = gate_up_bytes / (ms * 1e-3) / 1e9
+    out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+           "traffic": (int(TRAFFIC[(gk, cfg.name)]) if (gk, cfg.name) in TRAFFIC else None),
+           "kernel": gk, "bytes_per_launch": int(gate_up_bytes),
+           "avg_launch_us": round(ms * 1e3, 2)}
+    if gk == "pf_gateup":
+        # useful int8 ops of the launch: 2 per MAC over T*(K+S) (token, expert)
+        # pairs x 2I rows x H
+        ops = 2.0 * T * (cfg.top_k + cfg.n_shared) * 2 * cfg.inter * cfg.hidden
+        out["int8_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
+        out["int8_frac_of_5000_tops"] = round(ops / (ms * 1e-3) / 5.0e15, 4)
+    return out
+
+
+def run_stack(args, cfg):
+    """The stacked workload: x <- x + MoE_l(RMSNorm(x)) for every layer l, one
+    step = all layers over one batch of T tokens."""
+    import numpy as np
+    import torch
+
+    import coli_synth as cs
+    import int4_quantized_moe_sigmoid_amd as C
+
+    T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
+    NL = cfg.n_layers
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho)
+    n_steps, n_warm = args.steps, args.warmup
+    t_setup = time.time()
+    layers = []
+    for l in range(NL):
+        wr, b, q, s = cs.build_layer(cfg, l, "cuda", lambda w, qv, sv: C.coli_pack_int4(w, qv, sv))
+        layers.append(C.LayerWeights(lc, wr, b, q, s))
+        print(f"[bench] layer {l} packed", file=sys.stderr, flush=True)
+    xs = [cs.activations(cfg, 0, "cuda", n_tok=T, first_tok=i * T) for i in range(n_steps + n_warm)]
+    xn = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(C.coli_moe_workspace_bytes(lc, T), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    def step(x):
+        for l in range(NL):
+            C.coli_rmsnorm(x, xn, 1e-5)
+            C.coli_moe_forward(layers[l], xn, x, ws, C.COLI_FWD_ACCUM)
+
+    for i in range(n_warm):
+        step(xs[n_steps + i])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        step(xs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / n_steps
+
+    kern = {}
+    uniq = []
+    if not args.no_profile:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(16)]
+        for e in evs:
+            e.record()
+        torch.cuda.synchronize()
+        hs = [e.cuda_event for e in evs]
+        lay = C.coli_moe_workspace_layout(lc, T, 0)
+        counts_view = ws[lay.counts:lay.counts + 4 * (E + S)].view(torch.int32)
+        x = cs.activations(cfg, 0, "cuda", n_tok=T, first_tok=10 ** 6)
+        for l in range(NL):
+            C.coli_rmsnorm(x, xn, 1e-5)
+            names = C.coli_moe_forward_profiled(layers[l], xn, x, ws, hs, C.COLI_FWD_ACCUM)
+            torch.cuda.synchronize()
+            for j in range(len(names) - 1):
+                kern[names[j]] = kern.get(names[j], 0.0) + evs[j].elapsed_time(evs[j + 1]) / NL
+            uniq.append(int((counts_view[:E] > 0).sum().item()) + S)
+    uniq_avg = float(np.mean(uniq)) if uniq else float(E + S)
+    gate_up_bytes = uniq_avg * (2 * I * H // 2 + 4 * 2 * I) + T * (H + H // 8) + \
+        T * (K + S) * (I + I // 8)
+    out = {
+        "metric": "MoE-stack tokens/s (8 pre-norm residual MoE layers)",
+        "value": round(T * n_steps / elapsed, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": n_steps, "warmup": n_warm, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4xint8 (int32 block dots, f64 scales)",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed by coli_pack_int4)",
+        "config": {"workload": cfg.name, "tokens_per_step": T, "layers": NL, "hidden": H,
+                   "inter": I, "n_experts": E, "top_k": K, "n_shared": S,
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_layer": round(ms_per_step / NL, 4),
+        "unique_experts_per_layer": round(uniq_avg, 2),
+        "kernel_avg_us_per_layer": {k: round(v * 1e3, 2) for k, v in kern.items()},
+        "roofline": gateup_roofline(kern, cfg, gate_up_bytes, T),
+        "cpu_baseline": None,
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(out), flush=True)

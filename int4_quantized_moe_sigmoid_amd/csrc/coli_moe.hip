@@ -2,6 +2,7 @@
 // layout, kernel selection and launches. No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -22,6 +23,7 @@ constexpr int kMaxInter = 8192;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 16;
 constexpr int kGemvChunk = 4;     // tokens per item on the GEMV path
+constexpr int kMaxRouterSplit = 16;  // hidden-dimension slices of the router GEMM
 constexpr int64_t kTapBudget = 1ll << 24;  // int32 entries of the block-dot tap
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -42,7 +44,7 @@ int check_cfg(const coli_moe_cfg* c) {
 
 struct Layout {
     coli_moe_ws_layout pub;
-    size_t lists, items, n_items, uinfo;
+    size_t lists, items, n_items, uinfo, rpart;
     int64_t max_items;
     int ch;
 };
@@ -81,6 +83,7 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
     L->items = take(3 * L->max_items * 4);
     L->n_items = take(4);
     L->uinfo = take(4 * (1 + 4 * dec::kMaxEntries + 64));
+    L->rpart = take(T > 8 ? (size_t)kMaxRouterSplit * T * E * 8 : 0);
 
     P.qh = take(NS * I);
     P.dh = take(NS * (I / 32) * 4);
@@ -147,9 +150,18 @@ void launch_down_nt(int nbj, dim3 grid, hipStream_t s, const coli_moe_weights* w
 }
 
 // Router + top-k into ws (shared by coli_moe_route and coli_moe_forward).
+// Slices of the hidden dimension for the many-token router GEMM: enough
+// workgroups to cover the GPU (~512), each slice a multiple of 32.
+int router_ksplit(int H, int64_t T, int E) {
+    const int64_t tiles = ((T + kRouterTile - 1) / kRouterTile) * ((E + kRouterTile - 1) / kRouterTile);
+    int ks = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxRouterSplit, 512 / std::max<int64_t>(tiles, 1)));
+    while (ks > 1 && H % (kRouterK * ks) != 0) --ks;
+    return ks;
+}
+
 void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const float* bias,
-                  int64_t T, double* logits, int32_t* idx, float* wts, hipStream_t s,
-                  Marks& mk) {
+                  int64_t T, double* logits, double* rpart, int32_t* idx, float* wts,
+                  hipStream_t s, Marks& mk) {
     const int H = c.hidden, E = c.n_experts, K = c.top_k;
     mk.mark("router_logits");
     if (T <= 8) {
@@ -160,8 +172,13 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
         else
             k_router_gemv<8><<<E, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
     } else {
-        dim3 g((unsigned)((T + 63) / 64), (unsigned)((E + 31) / 32));
-        k_router_gemm<<<g, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
+        const int ks = router_ksplit(H, T, E);
+        dim3 g((unsigned)((T + kRouterTile - 1) / kRouterTile),
+               (unsigned)((E + kRouterTile - 1) / kRouterTile), (unsigned)ks);
+        k_router_gemm<<<g, 256, 0, s>>>(x, wr, (int)T, H, E, ks, rpart);
+        const int64_t n = T * E;
+        mk.mark("router_reduce");
+        k_router_reduce<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rpart, ks, n, logits);
     }
     mk.mark("topk");
     const unsigned gb = (unsigned)((T + 3) / 4);
@@ -284,7 +301,8 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
     const int64_t nblk = T * (H / 32);
     k_quant_q8<true><<<(unsigned)((nblk * 4 + 255) / 256), 256, 0, s>>>(x, nblk, qx, dx);
 
-    launch_route(c, x, w->w_router, w->bias, T, logits, idx, wts, s, mk);
+    launch_route(c, x, w->w_router, w->bias, T, logits,
+                 reinterpret_cast<double*>(base + L.rpart), idx, wts, s, mk);
 
     // grouped MFMA path when the row tiles divide the shapes, else the GEMV path
     const bool mfma = (H % pf::kRows) == 0 && (I % pf::kRows) == 0;
@@ -427,8 +445,9 @@ COLI_API int coli_moe_route(const float* x, const float* w_router, const float* 
     if (ws_bytes < L.pub.total) return COLI_E_WORKSPACE;
     Marks mk{(hipStream_t)stream};
     launch_route(*cfg, x, w_router, bias, n_tok,
-                 reinterpret_cast<double*>(static_cast<char*>(ws) + L.pub.logits), topk_idx,
-                 topk_w, (hipStream_t)stream, mk);
+                 reinterpret_cast<double*>(static_cast<char*>(ws) + L.pub.logits),
+                 reinterpret_cast<double*>(static_cast<char*>(ws) + L.rpart), topk_idx, topk_w,
+                 (hipStream_t)stream, mk);
     return hip_status();
 }
 

@@ -43,65 +43,80 @@ __global__ __launch_bounds__(256) void k_router_gemv(const float* __restrict__ x
     }
 }
 
-// ---------------------------------------------------------------------------
-// Router logits for many tokens: 64 tokens x 32 experts per workgroup, K
-// chunks of 32 staged in LDS as doubles, 4x2 outputs per lane.
-// ---------------------------------------------------------------------------
+// Router logits for many tokens: a 64-token x 64-expert tile per workgroup
+// over one of `ksplit` equal slices of the hidden dimension; each thread
+// accumulates a 4 x 4 block of the tile in fp64 (sequential over its slice).
+// Operands are converted to fp64 in LDS, stored k-major so a thread's four
+// tokens (four experts) are two 16-byte reads. Partial sums go to
+// part[slice][t][e]; k_router_reduce adds the slices in order.
+constexpr int kRouterTile = 64;
+constexpr int kRouterK = 32;
+
 __global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x,
                                                      const float* __restrict__ wr, int T, int H,
-                                                     int E, double* __restrict__ logits) {
-    __shared__ double xs[64][33];
-    __shared__ double ws[32][33];
-    const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 32;
+                                                     int E, int ksplit,
+                                                     double* __restrict__ part) {
+    __shared__ __align__(16) double xs[kRouterK][kRouterTile + 2];
+    __shared__ __align__(16) double ws[kRouterK][kRouterTile + 2];
+    const int t0 = blockIdx.x * kRouterTile, e0 = blockIdx.y * kRouterTile;
+    const int kper = H / ksplit, kbeg = blockIdx.z * kper;
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    double acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = 0.0;
-    for (int k0 = 0; k0 < H; k0 += 32) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int li = tid * 2 + i, row = li >> 3, c4 = li & 7;
-            const int t = t0 + row;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < T) v = *reinterpret_cast<const float4*>(x + (int64_t)t * H + k0 + c4 * 4);
-            xs[row][c4 * 4 + 0] = v.x;
-            xs[row][c4 * 4 + 1] = v.y;
-            xs[row][c4 * 4 + 2] = v.z;
-            xs[row][c4 * 4 + 3] = v.w;
-        }
-        {
-            const int row = tid >> 3, c4 = tid & 7;
-            const int e = e0 + row;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (e < E) v = *reinterpret_cast<const float4*>(wr + (int64_t)e * H + k0 + c4 * 4);
-            ws[row][c4 * 4 + 0] = v.x;
-            ws[row][c4 * 4 + 1] = v.y;
-            ws[row][c4 * 4 + 2] = v.z;
-            ws[row][c4 * 4 + 3] = v.w;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int k = 0; k < 32; ++k) {
-            double a[4], b[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = xs[ty * 4 + i][k];
-            b[0] = ws[tx * 2 + 0][k];
-            b[1] = ws[tx * 2 + 1][k];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[i][0] += a[i] * b[0];
-                acc[i][1] += a[i] * b[1];
-            }
-        }
-        __syncthreads();
-    }
+    double acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = t0 + ty * 4 + i, e = e0 + tx * 2 + j;
-            if (t < T && e < E) logits[(int64_t)t * E + e] = acc[i][j];
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int k0 = kbeg; k0 < kbeg + kper; k0 += kRouterK) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int li = tid * 2 + i, row = li >> 3, c4 = li & 7;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f), w = v;
+            if (t0 + row < T) v = *reinterpret_cast<const float4*>(x + (int64_t)(t0 + row) * H + k0 + c4 * 4);
+            if (e0 + row < E) w = *reinterpret_cast<const float4*>(wr + (int64_t)(e0 + row) * H + k0 + c4 * 4);
+            xs[c4 * 4 + 0][row] = v.x;
+            xs[c4 * 4 + 1][row] = v.y;
+            xs[c4 * 4 + 2][row] = v.z;
+            xs[c4 * 4 + 3][row] = v.w;
+            ws[c4 * 4 + 0][row] = w.x;
+            ws[c4 * 4 + 1][row] = w.y;
+            ws[c4 * 4 + 2][row] = w.z;
+            ws[c4 * 4 + 3][row] = w.w;
         }
+        __syncthreads();
+#pragma unroll 8
+        for (int k = 0; k < kRouterK; ++k) {
+            const double2 a01 = *reinterpret_cast<const double2*>(&xs[k][ty * 4]);
+            const double2 a23 = *reinterpret_cast<const double2*>(&xs[k][ty * 4 + 2]);
+            const double2 b01 = *reinterpret_cast<const double2*>(&ws[k][tx * 4]);
+            const double2 b23 = *reinterpret_cast<const double2*>(&ws[k][tx * 4 + 2]);
+            const double av[4] = {a01.x, a01.y, a23.x, a23.y};
+            const double bv[4] = {b01.x, b01.y, b23.x, b23.y};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+        }
+        __syncthreads();
+    }
+    double* out = part + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
+            if (t < T && e < E) out[(int64_t)t * E + e] = acc[i][j];
+        }
+}
+
+// logits[i] = sum over slices s = 0 .. ksplit-1 of part[s][i], in that order.
+__global__ __launch_bounds__(256) void k_router_reduce(const double* __restrict__ part,
+                                                       int ksplit, int64_t n,
+                                                       double* __restrict__ logits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    double v = part[i];
+    for (int s = 1; s < ksplit; ++s) v += part[(int64_t)s * n + i];
+    logits[i] = v;
 }
 
 // ---------------------------------------------------------------------------
