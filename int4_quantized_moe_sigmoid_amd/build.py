@@ -17,6 +17,8 @@ HIPCC_FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results straight into VGPRs (no accumulator-register copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -68,17 +68,21 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
     return *reinterpret_cast<const uint32_t*>(p);
 }
 
-// Stages NR rows (row r at src[r / 4 ...]) of one chunk: lane l loads 16
-// bytes of row (l >> 4) + 4k at block (l & 15) of the chunk.
+// Stages NR rows of one chunk: lane l loads 16 bytes of staged row
+// (l >> 4) + 4k at block (l & 15) of the chunk. Staged rows 16m .. 16m+15
+// are rows 0..15 of matrix m, starting at base[m] (this lane's row l >> 4)
+// with `stride` bytes between rows.
 template <int NR>
 struct Stager {
-    const uint8_t* row[NR / 4];
+    const uint8_t* base[NR / 16];
+    int64_t stride;
     uint4 v[NR / 4];
     __device__ __forceinline__ void issue(int c, int BH) {
         const int b = min(c * kChunk + (int)(threadIdx.x & 15), BH - 1);
 #pragma unroll
         for (int k = 0; k < NR / 4; ++k)
-            v[k] = *reinterpret_cast<const uint4*>(row[k] + b * 16);
+            v[k] = *reinterpret_cast<const uint4*>(base[k / 4] + (int64_t)(4 * (k % 4)) * stride +
+                                                   b * 16);
     }
     __device__ __forceinline__ void commit(uint8_t* lds) const {
         const int r0 = (threadIdx.x & 63) >> 4, bi = threadIdx.x & 15;
@@ -121,7 +125,8 @@ struct ActStager {
             for (int i = 0; i < 4; ++i) dv[i] = drow[min(b0 + i, NB - 1)];
         }
     }
-    __device__ __forceinline__ void commit(uint8_t* act, float* dbuf) const {
+    // Scales of blocks past NB are stored as 0, so those blocks add nothing.
+    __device__ __forceinline__ void commit(int c, int NB, uint8_t* act, float* dbuf) const {
         const int blk = (threadIdx.x & 31) >> 1, half = threadIdx.x & 1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -131,14 +136,79 @@ struct ActStager {
         if (threadIdx.x < 128) {
             const int j = threadIdx.x >> 2, b0 = (threadIdx.x & 3) * 4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dbuf[j * kDPitch + b0 + i] = dv[i];
+            for (int i = 0; i < 4; ++i)
+                dbuf[j * kDPitch + b0 + i] = (c * kChunk + b0 + i < NB) ? dv[i] : 0.0f;
         }
     }
 };
 
+// K loop of the gate/up kernel for NG 16-token groups: MFMA per block and
+// group, fp64 epilogue. Inside a chunk there are no branches, so the
+// compiler can overlap the next block's LDS reads and MFMAs with the current
+// block's epilogue.
+template <int NG, bool TAP>
+__device__ __forceinline__ void gateup_loop(const PfArgs& a, Stager<32>& st, ActStager& as,
+                                            uint8_t* lds, uint8_t* act, float* dbuf,
+                                            double (&accg)[2][4], double (&accu)[2][4], int BH,
+                                            int r0, int q, int lr, int s0, int n) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) accg[g][i] = accu[g][i] = 0.0;
+    const v4i zero = {0, 0, 0, 0};
+    const int nch = (BH + kChunk - 1) / kChunk;
+    st.issue(0, BH);
+    as.issue(0, BH);
+    st.commit(lds);
+    as.commit(0, BH, act, dbuf);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) {
+            st.issue(c + 1, BH);
+            as.issue(c + 1, BH);
+        }
+#pragma unroll
+        for (int bi = 0; bi < kChunk; ++bi) {
+            const long ag = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
+            const long au = a_operand(lds_u32(lds + (16 + lr) * kPitch + bi * 16 + 4 * q));
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int j = 16 * g + lr;
+                const long bv = *reinterpret_cast<const long*>(act + j * kActPitch + bi * 32 + 8 * q);
+                const double dd = (double)dbuf[j * kDPitch + bi];
+                const v4i cg = __builtin_amdgcn_mfma_i32_16x16x32_i8(ag, bv, zero, 0, 0, 0);
+                const v4i cu = __builtin_amdgcn_mfma_i32_16x16x32_i8(au, bv, zero, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    accg[g][i] += dd * (double)cg[i];
+                    accu[g][i] += dd * (double)cu[i];
+                    asm volatile("" : "+v"(accg[g][i]), "+v"(accu[g][i]));
+                }
+                if (TAP) {
+                    const int b = c * kChunk + bi;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = r0 + 4 * q + i;
+                        if (j < n && b < BH && (r % a.tap_stride) == 0)
+                            a.tap[((int64_t)(s0 + j) * a.tap_rows + r / a.tap_stride) * BH + b] =
+                                cg[i] / 16;
+                    }
+                }
+            }
+        }
+        if (c + 1 < nch) {
+            __syncthreads();
+            st.commit(lds);
+            as.commit(c + 1, BH, act, dbuf);
+            __syncthreads();
+        }
+    }
+}
+
 // Gate/up + SwiGLU + Q8_0(h) for one item and 64 intermediate rows.
 template <bool TAP>
-__global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_pf_gateup(PfArgs a) {
     constexpr int kW = 32 * kPitch;  // per-wave weight staging (16 gate + 16 up rows)
     __shared__ __align__(16) uint8_t smem[4 * kW + kActBytes + kDBytes];
     const int nrt = a.I / kRows;
@@ -157,70 +227,18 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
     uint8_t* act = smem + 4 * kW;
     float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + kActBytes);
 
-    Stager<32> st;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int r = q + 4 * k;  // staged row: 0..15 gate, 16..31 up
-        st.row[k] = ((r < 16) ? gate : up) + (int64_t)(r0 + (r & 15)) * (H >> 1);
-    }
+    Stager<32> st;  // staged rows 0..15: gate rows r0.., 16..31: up rows r0..
+    st.stride = H >> 1;
+    st.base[0] = gate + (int64_t)(r0 + q) * (H >> 1);
+    st.base[1] = up + (int64_t)(r0 + q) * (H >> 1);
     ActStager as;
     as.init(a.qx, a.dx, H, BH, a.slot_tok + s0, n);
 
     double accg[2][4], accu[2][4];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) accg[g][i] = accu[g][i] = 0.0;
-    const v4i zero = {0, 0, 0, 0};
-
-    const int nch = (BH + kChunk - 1) / kChunk;
-    st.issue(0, BH);
-    as.issue(0, BH);
-    st.commit(lds);
-    as.commit(act, dbuf);
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) {
-            st.issue(c + 1, BH);
-            as.issue(c + 1, BH);
-        }
-#pragma unroll
-        for (int bi = 0; bi < kChunk; ++bi) {
-            const int b = c * kChunk + bi;
-            const long ag = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
-            const long au = a_operand(lds_u32(lds + (16 + lr) * kPitch + bi * 16 + 4 * q));
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                if (g < ng) {
-                    const int j = 16 * g + lr;
-                    const long bv = *reinterpret_cast<const long*>(act + j * kActPitch + bi * 32 + 8 * q);
-                    const double dd = (b < BH) ? (double)dbuf[j * kDPitch + bi] * 0.0625 : 0.0;
-                    const v4i cg = __builtin_amdgcn_mfma_i32_16x16x32_i8(ag, bv, zero, 0, 0, 0);
-                    const v4i cu = __builtin_amdgcn_mfma_i32_16x16x32_i8(au, bv, zero, 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        accg[g][i] += dd * (double)cg[i];
-                        accu[g][i] += dd * (double)cu[i];
-                    }
-                    if (TAP) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = r0 + 4 * q + i;
-                            if (j < n && b < BH && (r % a.tap_stride) == 0)
-                                a.tap[((int64_t)(s0 + j) * a.tap_rows + r / a.tap_stride) * BH + b] =
-                                    cg[i] / 16;
-                        }
-                    }
-                }
-            }
-        }
-        if (c + 1 < nch) {
-            __syncthreads();
-            st.commit(lds);
-            as.commit(act, dbuf);
-            __syncthreads();
-        }
-    }
+    if (ng == 1)
+        gateup_loop<1, TAP>(a, st, as, lds, act, dbuf, accg, accu, BH, r0, q, lr, s0, n);
+    else
+        gateup_loop<2, TAP>(a, st, as, lds, act, dbuf, accg, accu, BH, r0, q, lr, s0, n);
     __syncthreads();  // the activation area is reused for h below
     float (*hbuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(act);
 
@@ -233,8 +251,9 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
         const float gsr = gs[r], usr = us[r];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-            const float gv = (float)((double)gsr * accg[g][i]);
-            const float uv = (float)((double)usr * accu[g][i]);
+            // the sums carry the x16 of the weight codes: scale by 1/16 (exact)
+            const float gv = (float)((double)gsr * (accg[g][i] * 0.0625));
+            const float uv = (float)((double)usr * (accu[g][i] * 0.0625));
             hbuf[16 * g + lr][wave * 16 + 4 * q + i] = swiglu_f32(gv, uv);
         }
     }
@@ -262,6 +281,53 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
     }
 }
 
+// K loop of the down kernel (as gateup_loop, one weight matrix).
+template <int NG>
+__device__ __forceinline__ void down_loop(Stager<16>& st, ActStager& as, uint8_t* lds,
+                                          uint8_t* act, float* dbuf, double (&acc)[2][4],
+                                          int BI, int q, int lr) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[g][i] = 0.0;
+    const v4i zero = {0, 0, 0, 0};
+    const int nch = (BI + kChunk - 1) / kChunk;
+    st.issue(0, BI);
+    as.issue(0, BI);
+    st.commit(lds);
+    as.commit(0, BI, act, dbuf);
+    __syncthreads();
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+        if (c + 1 < nch) {
+            st.issue(c + 1, BI);
+            as.issue(c + 1, BI);
+        }
+#pragma unroll
+        for (int bi = 0; bi < kChunk; ++bi) {
+            const long aw = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int j = 16 * g + lr;
+                const long bv = *reinterpret_cast<const long*>(act + j * kActPitch + bi * 32 + 8 * q);
+                const double dd = (double)dbuf[j * kDPitch + bi];
+                const v4i cd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw, bv, zero, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[g][i] += dd * (double)cd[i];
+                    asm volatile("" : "+v"(acc[g][i]));
+                }
+            }
+        }
+        if (c + 1 < nch) {
+            __syncthreads();
+            st.commit(lds);
+            as.commit(c + 1, BI, act, dbuf);
+            __syncthreads();
+        }
+    }
+}
+
 // Down projection for one item and 64 output rows: ye[slot, row] =
 // fp32(s_down[row] * sum_b d_h,b * I_b).
 __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
@@ -283,8 +349,8 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + kActBytes);
 
     Stager<16> st;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) st.row[k] = down + (int64_t)(r0 + q + 4 * k) * (I >> 1);
+    st.stride = I >> 1;
+    st.base[0] = down + (int64_t)(r0 + q) * (I >> 1);
     // the item's slots are consecutive rows of q_h
     __shared__ int s_rows[kTok];
     if (threadIdx.x < kTok) s_rows[threadIdx.x] = s0 + threadIdx.x;
@@ -293,46 +359,10 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     as.init(a.qh, a.dh, I, BI, s_rows, n);
 
     double acc[2][4];
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[g][i] = 0.0;
-    const v4i zero = {0, 0, 0, 0};
-
-    const int nch = (BI + kChunk - 1) / kChunk;
-    st.issue(0, BI);
-    as.issue(0, BI);
-    st.commit(lds);
-    as.commit(act, dbuf);
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) {
-            st.issue(c + 1, BI);
-            as.issue(c + 1, BI);
-        }
-#pragma unroll
-        for (int bi = 0; bi < kChunk; ++bi) {
-            const int b = c * kChunk + bi;
-            const long aw = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                if (g < ng) {
-                    const int j = 16 * g + lr;
-                    const long bv = *reinterpret_cast<const long*>(act + j * kActPitch + bi * 32 + 8 * q);
-                    const double dd = (b < BI) ? (double)dbuf[j * kDPitch + bi] * 0.0625 : 0.0;
-                    const v4i cd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw, bv, zero, 0, 0, 0);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[g][i] += dd * (double)cd[i];
-                }
-            }
-        }
-        if (c + 1 < nch) {
-            __syncthreads();
-            st.commit(lds);
-            as.commit(act, dbuf);
-            __syncthreads();
-        }
-    }
+    if (ng == 1)
+        down_loop<1>(st, as, lds, act, dbuf, acc, BI, q, lr);
+    else
+        down_loop<2>(st, as, lds, act, dbuf, acc, BI, q, lr);
     __syncthreads();  // the activation area is reused for y below
     float (*ybuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(act);
 
@@ -342,7 +372,8 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
         const int rl = wave * 16 + 4 * q + i;
         const float dsr = ds[rt * kRows + rl];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) ybuf[16 * g + lr][rl] = (float)((double)dsr * acc[g][i]);
+        for (int g = 0; g < 2; ++g)
+            ybuf[16 * g + lr][rl] = (float)((double)dsr * (acc[g][i] * 0.0625));  // undo x16
     }
     __syncthreads();
     for (int v = threadIdx.x; v < n * kRows; v += 256) {
