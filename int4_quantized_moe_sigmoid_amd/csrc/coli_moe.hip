@@ -201,7 +201,7 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
 // hidden <= 6144, intermediate <= 2048, <= 256 routed experts.
 bool small_path_fits(const coli_moe_cfg& c, int64_t T) {
     return T <= dec::kMaxTok && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
-           c.inter <= 2048 && c.n_experts <= 256;
+           c.inter <= 2048 && c.inter % 64 == 0 && c.n_experts <= 256;
 }
 
 template <int NT, int NBJH, bool TAP>
@@ -211,9 +211,13 @@ void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     dec::k_dec_router<NT><<<a.E, 256, 0, s>>>(a);
     mk.mark("dec_gateup");
     const int um = (a.T * a.K < a.E) ? a.T * a.K : a.E;
-    dec::k_dec_gateup<NT, NBJH, TAP><<<(a.S + um) * nrb, 256, 0, s>>>(a);
+    const int hbw = (NT > 1) ? 2 : 1;  // h-blocks per workgroup (k_dec_gateup)
+    dec::k_dec_gateup<NT, NBJH, TAP><<<(a.S + um) * (nrb / hbw), 256, 0, s>>>(a);
     mk.mark("dec_down");
-    dec::k_dec_down<NT, 1, 2, 4><<<a.H / 8, 256, 0, s>>>(a);
+    if (NT == 1)
+        dec::k_dec_down<1, 1, 2, 4><<<a.H / 8, 256, 0, s>>>(a);
+    else
+        dec::k_dec_down_x<NT, 1><<<a.H / 8, 256, 0, s>>>(a);
 }
 
 template <int NT>

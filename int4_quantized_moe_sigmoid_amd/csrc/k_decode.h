@@ -99,7 +99,10 @@ struct Route {
     int u_e[kMaxEntries];       // unique experts, ascending
     int u_s0[kMaxEntries];      // first sorted entry (= slot) of each
     int u_n[kMaxEntries];       // tokens of each
-    // top-k scratch
+};
+
+// LDS scratch of the top-k, dead once the routing is done.
+struct TopkScratch {
     unsigned long long gmax[kMaxTok][8];  // max key of each 32-expert group
     int ncand[kMaxTok];
     unsigned long long ckey[kMaxTok][256];
@@ -122,12 +125,12 @@ __device__ __forceinline__ unsigned long long order_key(double c) {
 // (when there are >= K groups those maxima are >= K distinct experts), so
 // positions are counted among those few candidates only.
 __device__ __forceinline__ void topk_wg(const double* logits, const float* bias, int T, int E, int K,
-                                        int norm, double rho, Route& R) {
+                                        int norm, double rho, Route& R, TopkScratch& Z) {
     const int e = threadIdx.x;
     const int G = (E + 31) >> 5;
     const bool filt = G >= K;
-    if (threadIdx.x < kMaxTok * 8) (&R.gmax[0][0])[threadIdx.x] = 0ull;
-    if (threadIdx.x < kMaxTok) R.ncand[threadIdx.x] = 0;
+    if (threadIdx.x < kMaxTok * 8) (&Z.gmax[0][0])[threadIdx.x] = 0ull;
+    if (threadIdx.x < kMaxTok) Z.ncand[threadIdx.x] = 0;
     double l[kMaxTok];
     float bb = 0.0f;
 #pragma unroll
@@ -140,7 +143,7 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
     for (int t = 0; t < kMaxTok; ++t) {
         s[t] = 1.0 / (1.0 + exp(-l[t]));
         key[t] = order_key(s[t] + (double)bb);
-        if (filt && t < T && e < E) atomicMax(&R.gmax[t][e >> 5], key[t]);
+        if (filt && t < T && e < E) atomicMax(&Z.gmax[t][e >> 5], key[t]);
     }
     __syncthreads();
 #pragma unroll
@@ -149,30 +152,30 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
             unsigned long long thr = 0ull;
             if (filt) {
                 thr = ~0ull;
-                for (int g = 0; g < G; ++g) thr = min(thr, R.gmax[t][g]);
+                for (int g = 0; g < G; ++g) thr = min(thr, Z.gmax[t][g]);
             }
             if (key[t] >= thr) {
-                const int p = atomicAdd(&R.ncand[t], 1);
-                R.ckey[t][p] = key[t];
-                R.ce[t][p] = e;
-                R.cs[t][p] = s[t];
+                const int p = atomicAdd(&Z.ncand[t], 1);
+                Z.ckey[t][p] = key[t];
+                Z.ce[t][p] = e;
+                Z.cs[t][p] = s[t];
             }
         }
     }
     __syncthreads();
     for (int t = 0; t < T; ++t) {
-        const int m = R.ncand[t];
+        const int m = Z.ncand[t];
         for (int i = threadIdx.x; i < m; i += blockDim.x) {
-            const unsigned long long ki = R.ckey[t][i];
-            const int ei = R.ce[t][i];
+            const unsigned long long ki = Z.ckey[t][i];
+            const int ei = Z.ce[t][i];
             int rank = 0;
             for (int j = 0; j < m; ++j) {
-                const unsigned long long kj = R.ckey[t][j];
-                rank += (kj > ki || (kj == ki && R.ce[t][j] < ei)) ? 1 : 0;
+                const unsigned long long kj = Z.ckey[t][j];
+                rank += (kj > ki || (kj == ki && Z.ce[t][j] < ei)) ? 1 : 0;
             }
             if (rank < K) {
                 R.idx[t][rank] = ei;
-                R.ssel[t][rank] = R.cs[t][i];
+                Z.ssel[t][rank] = Z.cs[t][i];
             }
         }
     }
@@ -180,8 +183,8 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
     if ((int)threadIdx.x < T * K) {
         const int t = threadIdx.x / K, k = threadIdx.x - t * K;
         double sum = 0.0;
-        for (int kk = 0; kk < K; ++kk) sum += R.ssel[t][kk];
-        double v = R.ssel[t][k];
+        for (int kk = 0; kk < K; ++kk) sum += Z.ssel[t][kk];
+        double v = Z.ssel[t][k];
         if (norm) v = v / sum;
         v = v * rho;
         R.w[t][k] = (float)v;
@@ -191,8 +194,8 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
 // Fills R (in LDS) for T tokens; must be called by the whole workgroup
 // (blockDim.x >= E).
 __device__ __forceinline__ void route_small(const double* logits, const float* bias, int T, int E, int K, int S,
-                            int norm, double rho, Route& R) {
-    topk_wg(logits, bias, T, E, K, norm, rho, R);
+                            int norm, double rho, Route& R, TopkScratch& Z) {
+    topk_wg(logits, bias, T, E, K, norm, rho, R, Z);
     __syncthreads();
     const int n = T * K;
     const int i = threadIdx.x;
@@ -381,6 +384,119 @@ __device__ __forceinline__ void gateup_block(const DecArgs& a, int e, int hb, in
     }
 }
 
+// As gateup_block for experts with several tokens: the Q8_0 codes and
+// scales of the n tokens are staged in LDS (xs: n rows of H bytes, xds: n
+// rows of H/32 scales) and read per step, one token at a time, so the
+// activations do not occupy registers for the whole kernel.
+template <int NT, int NBJ, bool TAP>
+__device__ __forceinline__ void gateup_block_lds(const DecArgs& a, int e, int hb, int n,
+                                                 int slot0, const uint8_t* xs, const float* xds,
+                                                 float (*hbuf)[32]) {
+    const int H = a.H, I = a.I, BH = H >> 5;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
+    const uint8_t* up = gate + (int64_t)I * (H >> 1);
+    const float* gs = a.es + (int64_t)e * a.blob_s;
+    const float* us = gs + I;
+    const int r0 = hb * 32 + wave;  // rows r0 + 4k, k = 0..7
+    int boff[NBJ];
+#pragma unroll
+    for (int j = 0; j < NBJ; ++j) boff[j] = min(lane + 64 * j, BH - 1) * 16;
+    uint4 wb[2][4][NBJ];
+    auto load_pair = [&](int p, uint4 (&dst)[4][NBJ]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r0 + 4 * (2 * p + (q & 1));
+            const uint8_t* row = ((q < 2) ? gate : up) + (int64_t)r * (H >> 1);
+#pragma unroll
+            for (int j = 0; j < NBJ; ++j) dst[q][j] = ldnt(row + boff[j]);
+        }
+    };
+    load_pair(0, wb[0]);
+    load_pair(1, wb[1]);
+    const float gsl = gs[r0 + 4 * (lane & 7)];
+    const float usl = us[r0 + 4 * (lane & 7)];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        if (p >= 1 && p < 3) load_pair(p + 1, wb[(p + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint4 (&wc)[4][NBJ] = wb[p & 1];
+        double v[4 * NT];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            double acc[4] = {0.0, 0.0, 0.0, 0.0};
+            if (i < n) {
+#pragma unroll
+                for (int j = 0; j < NBJ; ++j) {
+                    const int b = lane + 64 * j, bb = min(b, BH - 1);
+                    const uint4* px = reinterpret_cast<const uint4*>(xs + i * H + bb * 32);
+                    const uint4 x0 = px[0], x1 = px[1];
+                    const double xd = (b < BH) ? (double)xds[i * BH + bb] * 0.0625 : 0.0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int d16 = dot_block16(wc[q][j], x0, x1);
+                        acc[q] += xd * (double)d16;
+                        if (TAP && q < 2) {
+                            const int r = r0 + 4 * (2 * p + q);
+                            if (b < BH && (r % a.tap_stride) == 0)
+                                a.tap[((int64_t)(slot0 + i) * a.tap_rows + r / a.tap_stride) * BH +
+                                      b] = d16 / 16;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q * NT + i] = acc[q];
+        }
+        const double sum = wave_reduce_tr<4 * NT>(v, lane);
+        const double other = __shfl_xor(sum, 32, 64);
+        constexpr int kShift = (NT == 1) ? 4 : (NT == 2) ? 3 : 2;
+        const int vi = lane >> kShift;
+        const int kq = 2 * p + ((vi < 2 * NT) ? vi / NT : 0);
+        const float gsk = __shfl(gsl, kq, 64), usk = __shfl(usl, kq, 64);
+        if (vi < 2 * NT && lane == (vi << kShift)) {
+            const int q = vi / NT, i = vi - q * NT;
+            if (i < n) {
+                const float g = (float)((double)gsk * sum);
+                const float u = (float)((double)usk * other);
+                hbuf[i][wave + 4 * (2 * p + q)] = swiglu_f32(g, u);
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < NT * 32) {
+        const int i = threadIdx.x >> 5, k = threadIdx.x & 31;
+        const float val = (i < n) ? hbuf[i][k] : 0.0f;
+        float amax = fabsf(val);
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+        const float dd = amax / 127.0f;
+        const int c = q8_code(val, dd);
+        if (i < n) {
+            a.qh[(int64_t)(slot0 + i) * I + hb * 32 + q8_perm_pos(k)] = (int8_t)c;
+            if (k == 0) a.dh[(int64_t)(slot0 + i) * (I >> 5) + hb] = dd;
+        }
+    }
+    __syncthreads();  // hbuf is reused by the workgroup's next h-block
+}
+
+// Copies the Q8_0 codes and scales of tokens tok[0..n) into LDS (xs, xds).
+__device__ __forceinline__ void stage_tokens(const DecArgs& a, const int* tok, int n, uint8_t* xs,
+                                             float* xds) {
+    const int H = a.H, BH = H >> 5, V = H >> 4;  // uint4 per row
+    for (int x = threadIdx.x; x < n * V; x += blockDim.x) {
+        const int i = x / V, c = x - i * V;
+        reinterpret_cast<uint4*>(xs + i * H)[c] =
+            reinterpret_cast<const uint4*>(a.qx + (int64_t)tok[i] * H)[c];
+    }
+    for (int x = threadIdx.x; x < n * BH; x += blockDim.x) {
+        const int i = x / BH, c = x - i * BH;
+        xds[i * BH + c] = a.dx[(int64_t)tok[i] * BH + c];
+    }
+    __syncthreads();
+}
+
 // Publishes the routing computed in R (one workgroup of B) for C, the taps
 // and the workspace layout.
 __device__ void publish_route(const DecArgs& a, const Route& R) {
@@ -468,28 +584,55 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
 // expert in use (u < min(E, T*K)); block (u = 0, hb = 0) publishes routing.
 template <int NT, int NBJ, bool TAP>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
+    // several tokens: activations staged in LDS, sharing space with the
+    // top-k scratch (dead by then); H <= 6144 on this path
+    constexpr int kAct = (NT > 1) ? NT * 6144 + NT * 192 * 4 : 16;
+    union Shared {
+        TopkScratch z;
+        uint8_t act[kAct];
+    };
+    __shared__ __align__(16) Shared U;
     __shared__ Route R;
     __shared__ float hbuf[NT][32];
     __shared__ int s_tok[NT];
-    const int nrb = a.I >> 5;
+    uint8_t* xs = U.act;
+    float* xds = reinterpret_cast<float*>(U.act + NT * a.H);
+    // a workgroup covers HB consecutive h-blocks of 32 rows (one at a single
+    // token; two with several, so fewer workgroups redo the routing)
+    constexpr int HB = (NT > 1) ? 2 : 1;
+    const int nw = (a.I >> 5) / HB;  // workgroups per expert
     int b = blockIdx.x;
     if (a.S) {
-        if (b < nrb) {
-            if ((int)threadIdx.x < NT) s_tok[threadIdx.x] = threadIdx.x;
+        if (b < nw) {
+            if ((int)threadIdx.x < NT) s_tok[threadIdx.x] = min((int)threadIdx.x, a.T - 1);
             __syncthreads();
-            gateup_block<NT, NBJ, TAP>(a, a.E, b, a.T, s_tok, a.T * a.K, hbuf);
+            if (NT > 1) {
+                stage_tokens(a, s_tok, a.T, xs, xds);
+#pragma unroll 1
+                for (int h = 0; h < HB; ++h)
+                    gateup_block_lds<NT, NBJ, TAP>(a, a.E, b * HB + h, a.T, a.T * a.K, xs, xds, hbuf);
+            } else {
+                gateup_block<NT, NBJ, TAP>(a, a.E, b, a.T, s_tok, a.T * a.K, hbuf);
+            }
             return;
         }
-        b -= nrb;
+        b -= nw;
     }
-    route_small(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R);
+    route_small(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R, U.z);
     if (b == 0) publish_route(a, R);
-    const int u = b / nrb, hb = b - u * nrb;
+    const int u = b / nw, hw = b - u * nw;
     if (u >= R.n_uniq) return;
     const int e = __builtin_amdgcn_readfirstlane(R.u_e[u]);
     const int s0 = __builtin_amdgcn_readfirstlane(R.u_s0[u]);
     const int n = __builtin_amdgcn_readfirstlane(R.u_n[u]);
-    gateup_block<NT, NBJ, TAP>(a, e, hb, n, &R.ent_t[s0], s0, hbuf);
+    if (NT > 1) {
+        stage_tokens(a, &R.ent_t[s0], n, xs, xds);
+#pragma unroll 1
+        for (int h = 0; h < HB; ++h)
+            gateup_block_lds<NT, NBJ, TAP>(a, e, hw * HB + h, n, s0, xs, xds, hbuf);
+    } else {
+        gateup_block<NT, NBJ, TAP>(a, e, hw, n, &R.ent_t[s0], s0, hbuf);
+    }
 }
 
 // C: down projection of every expert in use and the weighted combine.
@@ -539,12 +682,15 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
     constexpr int V = RPW * NT;
     constexpr int kLog = (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
     constexpr int kShift = 6 - kLog;
-#pragma unroll 1
-    for (int v0 = 0; v0 < nu; v0 += NB) {
+    // experts in batches of NB, the next batch's loads issued before the
+    // current batch's arithmetic (two register buffers)
+    struct Batch {
         uint4 w[NB][RPW][NBJ];
         uint4 ha[NB][NT][NBJ][2];
         float hdf[NB][NT][NBJ];
         float dsv[NB][RPW];
+    };
+    auto load = [&](int v0, Batch& bt) {
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi) {
             const int v = min(v0 + bi, nu - 1);
@@ -554,7 +700,7 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
             for (int r = 0; r < RPW; ++r)
 #pragma unroll
                 for (int j = 0; j < NBJ; ++j)
-                    w[bi][r][j] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl[j] * 16);
+                    bt.w[bi][r][j] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl[j] * 16);
         }
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi) {
@@ -564,20 +710,21 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
             const int n = __builtin_amdgcn_readfirstlane(s_n[v]);
             const float* ds = a.es + (int64_t)ev * a.blob_s + 2 * I;
 #pragma unroll
-            for (int r = 0; r < RPW; ++r) dsv[bi][r] = ds[c0 + r];
+            for (int r = 0; r < RPW; ++r) bt.dsv[bi][r] = ds[c0 + r];
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 const int sl = s0 + min(i, n - 1);
 #pragma unroll
                 for (int j = 0; j < NBJ; ++j) {
                     const uint4* p = reinterpret_cast<const uint4*>(a.qh + (int64_t)sl * I + bcl[j] * 32);
-                    ha[bi][i][j][0] = p[0];
-                    ha[bi][i][j][1] = p[1];
-                    hdf[bi][i][j] = a.dh[(int64_t)sl * BI + bcl[j]];
+                    bt.ha[bi][i][j][0] = p[0];
+                    bt.ha[bi][i][j][1] = p[1];
+                    bt.hdf[bi][i][j] = a.dh[(int64_t)sl * BI + bcl[j]];
                 }
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](int v0, const Batch& bt) {
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi) {
             const int v = v0 + bi;
@@ -593,8 +740,9 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
 #pragma unroll
                     for (int j = 0; j < NBJ; ++j) {
                         const bool ok = i < n && lane + 64 * j < BI;
-                        const double hd = ok ? (double)hdf[bi][i][j] * 0.0625 : 0.0;
-                        p += hd * (double)dot_block16(w[bi][r][j], ha[bi][i][j][0], ha[bi][i][j][1]);
+                        const double hd = ok ? (double)bt.hdf[bi][i][j] * 0.0625 : 0.0;
+                        p += hd * (double)dot_block16(bt.w[bi][r][j], bt.ha[bi][i][j][0],
+                                                      bt.ha[bi][i][j][1]);
                     }
                     vals[r * NT + i] = p;
                 }
@@ -603,15 +751,26 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
             if (lane == (vi << kShift)) {
                 const int r = vi / NT, i = vi - r * NT;
                 if (i < n) {
-                    float dsr = dsv[bi][0];
+                    float dsr = bt.dsv[bi][0];
 #pragma unroll
                     for (int rr = 1; rr < RPW; ++rr)
-                        if (r == rr) dsr = dsv[bi][rr];
+                        if (r == rr) dsr = bt.dsv[bi][rr];
                     const float yv = (float)((double)dsr * sum);
                     s_acc[wave * RPW + r][s_t[s0 + i]] += (double)s_w[s0 + i] * (double)yv;
                 }
             }
         }
+    };
+    // at one token at most top_k (<= 16) + 1 experts are in use
+    constexpr int kMaxB = (NT == 1) ? (17 + NB - 1) / NB : (kMaxEntries + 1 + NB - 1) / NB;
+    Batch b0, b1;
+    load(0, b0);
+#pragma unroll
+    for (int k = 0; k < kMaxB; ++k) {
+        if (k * NB >= nu) break;
+        if ((k + 1) * NB < nu) load((k + 1) * NB, (k & 1) ? b0 : b1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(k * NB, (k & 1) ? b1 : b0);
     }
     if (lane < RPW * NT) {
         const int r = lane / NT, t = lane - r * NT;
@@ -620,6 +779,120 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
             const float yv = (float)s_acc[wave * RPW + r][t];
             *out = a.accum ? *out + yv : yv;
         }
+    }
+}
+
+
+// C (expert-split variant): down projection and combine for 8 output rows
+// per workgroup. Wave w takes the experts in use v = w, w+4, w+8, ... in
+// batches of PB; a batch's 8 rows per expert and its activation blocks are
+// all requested before any is used (at batch 1 with 9 experts in use this is
+// the whole job: one memory round trip per wave). Per-(row, expert, token)
+// results y_e = fp32(s_down * sum) go to LDS; the combine then runs in
+// ascending expert order with the shared expert last.
+template <int NT, int PB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_down_x(DecArgs a) {
+    constexpr int RW = 8;                        // rows per workgroup
+    constexpr int kSlots = kMaxEntries + kMaxTok;
+    __shared__ int s_e[kMaxEntries + 1], s_s0[kMaxEntries + 1], s_n[kMaxEntries + 1];
+    __shared__ float s_w[kSlots];
+    __shared__ int s_t[kSlots];
+    __shared__ float s_y[RW][kSlots];            // y_e of (row, slot)
+    __shared__ int s_nu;
+    const int T = a.T, K = a.K, E = a.E, S = a.S, H = a.H, I = a.I;
+    const int BI = I >> 5;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_ent = T * K;
+    if (threadIdx.x == 0) {
+        int nu = a.uinfo[0];
+        for (int v = 0; v < nu; ++v) {
+            s_e[v] = a.uinfo[1 + 3 * v];
+            s_s0[v] = a.uinfo[2 + 3 * v];
+            s_n[v] = a.uinfo[3 + 3 * v];
+        }
+        if (S) {
+            s_e[nu] = E;
+            s_s0[nu] = n_ent;
+            s_n[nu] = T;
+            ++nu;
+        }
+        s_nu = nu;
+    }
+    for (int i = threadIdx.x; i < n_ent + S * T; i += 256) {
+        s_w[i] = (i < n_ent) ? reinterpret_cast<const float*>(a.uinfo + kUinfoW)[i] : 1.0f;
+        s_t[i] = a.slot_tok[i];
+    }
+    __syncthreads();
+    const int c0 = blockIdx.x * RW;
+    const int nu = __builtin_amdgcn_readfirstlane(s_nu);
+    const int bcl = min(lane, BI - 1);           // I <= 2048: one block per lane
+#pragma unroll 1
+    for (int v0 = wave; v0 < nu; v0 += 4 * PB) {
+        uint4 w[PB][RW];
+        uint4 ha[PB][NT][2];
+        float hdf[PB][NT];
+        int ev[PB];
+#pragma unroll
+        for (int m = 0; m < PB; ++m) {
+            const int v = min(v0 + 4 * m, nu - 1);
+            ev[m] = __builtin_amdgcn_readfirstlane(s_e[v]);
+            const uint8_t* down = a.eq + (int64_t)ev[m] * a.blob_q + (int64_t)I * H;
+#pragma unroll
+            for (int r = 0; r < RW; ++r) w[m][r] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl * 16);
+        }
+#pragma unroll
+        for (int m = 0; m < PB; ++m) {
+            const int v = min(v0 + 4 * m, nu - 1);
+            const int s0 = __builtin_amdgcn_readfirstlane(s_s0[v]);
+            const int n = __builtin_amdgcn_readfirstlane(s_n[v]);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const int sl = s0 + min(i, n - 1);
+                const uint4* p = reinterpret_cast<const uint4*>(a.qh + (int64_t)sl * I + bcl * 32);
+                ha[m][i][0] = p[0];
+                ha[m][i][1] = p[1];
+                hdf[m][i] = a.dh[(int64_t)sl * BI + bcl];
+            }
+        }
+        // row scales: lane r (< RW) of the wave holds expert m's scale of row c0 + r
+        float dsm[PB];
+#pragma unroll
+        for (int m = 0; m < PB; ++m) dsm[m] = a.es[(int64_t)ev[m] * a.blob_s + 2 * I + c0 + (lane & (RW - 1))];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < PB; ++m) {
+            const int v = v0 + 4 * m;
+            const int vc = min(v, nu - 1);
+            const int n = __builtin_amdgcn_readfirstlane(s_n[vc]);
+            const int s0 = __builtin_amdgcn_readfirstlane(s_s0[vc]);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const bool ok = i < n && lane < BI;
+                const double hd = ok ? (double)hdf[m][i] * 0.0625 : 0.0;
+                double vals[RW];
+#pragma unroll
+                for (int r = 0; r < RW; ++r)
+                    vals[r] = hd * (double)dot_block16(w[m][r], ha[m][i][0], ha[m][i][1]);
+                const double sum = wave_reduce_tr<RW>(vals, lane);
+                const int r = lane >> 3;  // 64 / RW lanes per value
+                const float ds = __shfl(dsm[m], r, 64);
+                if (v < nu && i < n && (lane & 7) == 0) s_y[r][s0 + i] = (float)((double)ds * sum);
+            }
+        }
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < RW * T) {
+        const int r = threadIdx.x / T, t = threadIdx.x - r * T;
+        double acc = 0.0;
+        for (int v = 0; v < nu; ++v) {
+            const int s0 = s_s0[v], n = s_n[v];
+            for (int i = 0; i < n; ++i)
+                if (s_t[s0 + i] == t) acc += (double)s_w[s0 + i] * (double)s_y[r][s0 + i];
+        }
+        float* out = a.y + (int64_t)t * H + c0 + r;
+        const float yv = (float)acc;
+        *out = a.accum ? *out + yv : yv;
     }
 }
 
