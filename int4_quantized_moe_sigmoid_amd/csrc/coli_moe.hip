@@ -208,7 +208,8 @@ template <int NT, int NBJH, bool TAP>
 void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     const int nrb = a.I / 32;
     mk.mark("dec_router");
-    dec::k_dec_router<NT><<<a.E, 256, 0, s>>>(a);
+    const int qb = (a.T * (a.H / 32) + 7) / 8;  // workgroups needed for Q8_0(x)
+    dec::k_dec_router<NT><<<(a.E > qb) ? a.E : qb, 256, 0, s>>>(a);
     mk.mark("dec_gateup");
     const int um = (a.T * a.K < a.E) ? a.T * a.K : a.E;
     const int hbw = (NT > 1) ? 2 : 1;  // h-blocks per workgroup (k_dec_gateup)

@@ -533,50 +533,66 @@ __device__ void publish_route(const DecArgs& a, const Route& R) {
     if (threadIdx.x == 0) a.uinfo[0] = R.n_uniq;
 }
 
-// A: router rows (one workgroup per expert); workgroup 0 also writes Q8_0(x).
+// A: router rows (one workgroup per expert) and Q8_0(x): workgroup e also
+// quantises blocks 8e .. 8e+7 of the T x H/32 activation blocks (half a
+// wave per block, lane k holding element k), while its router row loads are
+// in flight.
 template <int NT>
 __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
     __shared__ double red[NT][4];
-    const int e = blockIdx.x;
+    const int e = blockIdx.x;  // grid: max(E, blocks / 8) workgroups
     const int T = a.T, H = a.H;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const float* wrow = a.wr + (int64_t)e * H;
+    const bool router = e < a.E;
+    const float* wrow = a.wr + (int64_t)min(e, a.E - 1) * H;
+    constexpr int kIt = 6;  // H <= 6144 on this path: 6144 / (256 threads x 4)
+    float4 wv[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int h = min((int)threadIdx.x * 4 + 1024 * it, H - 4);
+        wv[it] = *reinterpret_cast<const float4*>(wrow + h);
+    }
+    {
+        const int blk = e * 8 + (int)(threadIdx.x >> 5);
+        const int k = threadIdx.x & 31;
+        if (blk < T * (H >> 5)) {
+            const float v = a.x[(int64_t)blk * 32 + k];
+            float amax = fabsf(v);
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+            const float d = amax / 127.0f;
+            a.qx[(int64_t)blk * 32 + q8_perm_pos(k)] = (int8_t)q8_code(v, d);
+            if (k == 0) a.dx[blk] = d;
+        }
+    }
     double acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0;
-    for (int h = threadIdx.x * 4; h < H; h += 1024) {
-        const float4 wv = *reinterpret_cast<const float4*>(wrow + h);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < T) {
-                const float4 xv = *reinterpret_cast<const float4*>(a.x + (int64_t)t * H + h);
-                acc[t] += (double)xv.x * (double)wv.x;
-                acc[t] += (double)xv.y * (double)wv.y;
-                acc[t] += (double)xv.z * (double)wv.z;
-                acc[t] += (double)xv.w * (double)wv.w;
+    for (int t = 0; t < NT; ++t) {
+        if (t < T) {
+#pragma unroll
+            for (int it = 0; it < kIt; ++it) {
+                const int h = threadIdx.x * 4 + 1024 * it;
+                if (h < H) {
+                    const float4 xv = *reinterpret_cast<const float4*>(a.x + (int64_t)t * H + h);
+                    acc[t] += (double)xv.x * (double)wv[it].x;
+                    acc[t] += (double)xv.y * (double)wv[it].y;
+                    acc[t] += (double)xv.z * (double)wv[it].z;
+                    acc[t] += (double)xv.w * (double)wv[it].w;
+                }
             }
         }
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const double s = wave_sum_f64(acc[t]);
-        if (lane == 0) red[t][wave] = s;
+        const double sm = wave_sum_f64(acc[t]);
+        if (lane == 0) red[t][wave] = sm;
     }
     __syncthreads();
-    if ((int)threadIdx.x < T) {
+    if (router && (int)threadIdx.x < T) {
         const double* r = red[threadIdx.x];
         a.logits[(int64_t)threadIdx.x * a.E + e] = (r[0] + r[1]) + (r[2] + r[3]);
-    }
-    if (e == 0) {
-        const int nblk = T * (H >> 5);
-        for (int blk = threadIdx.x; blk < nblk; blk += 256) {
-            uint4 q0, q1;
-            const float d = q8_block_regs(a.x + (int64_t)blk * 32, q0, q1);
-            uint4* o = reinterpret_cast<uint4*>(a.qx + (int64_t)blk * 32);
-            o[0] = q0;
-            o[1] = q1;
-            a.dx[blk] = d;
-        }
     }
 }
 
