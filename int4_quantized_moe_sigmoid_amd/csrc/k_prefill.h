@@ -31,6 +31,9 @@
 namespace pf {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+// plain vector type for 16-byte moves (HIP's uint4 struct copies become
+// memcpy calls that keep staging arrays out of registers)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kTok = 32;              // tokens per work item
 constexpr int kRows = 64;             // output rows per workgroup
@@ -76,21 +79,21 @@ template <int NR>
 struct Stager {
     const uint8_t* base[NR / 16];
     int64_t stride;
-    uint4 v[NR / 4];
-    __device__ __forceinline__ void issue(int c, int BH) {
+    __device__ __forceinline__ void issue(int c, int BH, v4u (&v)[NR / 4]) const {
         const int b = min(c * kChunk + (int)(threadIdx.x & 15), BH - 1);
 #pragma unroll
         for (int k = 0; k < NR / 4; ++k)
-            v[k] = *reinterpret_cast<const uint4*>(base[k / 4] + (int64_t)(4 * (k % 4)) * stride +
-                                                   b * 16);
+            v[k] = *reinterpret_cast<const v4u*>(base[k / 4] + (int64_t)(4 * (k % 4)) * stride +
+                                                 b * 16);
     }
-    __device__ __forceinline__ void commit(uint8_t* lds) const {
+    __device__ __forceinline__ void commit(uint8_t* lds, const v4u (&v)[NR / 4]) const {
         const int r0 = (threadIdx.x & 63) >> 4, bi = threadIdx.x & 15;
+        typedef unsigned v2u __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int k = 0; k < NR / 4; ++k) {
             uint8_t* d = lds + (r0 + 4 * k) * kPitch + bi * 16;
-            *reinterpret_cast<uint2*>(d) = make_uint2(v[k].x, v[k].y);
-            *reinterpret_cast<uint2*>(d + 8) = make_uint2(v[k].z, v[k].w);
+            *reinterpret_cast<v2u*>(d) = v[k].xy;
+            *reinterpret_cast<v2u*>(d + 8) = v[k].zw;
         }
     }
 };
@@ -102,8 +105,6 @@ struct Stager {
 struct ActStager {
     const int8_t* row[4];
     const float* drow;
-    uint4 v[4];
-    float dv[4];
     __device__ __forceinline__ void init(const int8_t* base, const float* dbase, int64_t pitch,
                                          int NB, const int32_t* rows_of, int n) {
         const int half = threadIdx.x & 1;
@@ -112,26 +113,27 @@ struct ActStager {
             const int j = min((int)(threadIdx.x >> 5) + 8 * k, n - 1);
             row[k] = base + (int64_t)rows_of[j] * pitch + 16 * half;
         }
-        const int jd = min((int)(threadIdx.x >> 2), n - 1);
+        const int jd = min((int)((threadIdx.x & 127) >> 2), n - 1);
         drow = dbase + (int64_t)rows_of[jd] * NB;
     }
-    __device__ __forceinline__ void issue(int c, int NB) {
+    __device__ __forceinline__ void issue(int c, int NB, v4u (&v)[4], float (&dv)[4]) const {
         const int b = min(c * kChunk + (int)((threadIdx.x & 31) >> 1), NB - 1);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const uint4*>(row[k] + b * 32);
-        if (threadIdx.x < 128) {
-            const int b0 = c * kChunk + (threadIdx.x & 3) * 4;
+        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const v4u*>(row[k] + b * 32);
+        // every thread loads (threads >= 128 repeat rows of the first 128, in
+        // bounds), so the values stay in registers; only threads < 128 store
+        const int b0 = c * kChunk + (threadIdx.x & 3) * 4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dv[i] = drow[min(b0 + i, NB - 1)];
-        }
+        for (int i = 0; i < 4; ++i) dv[i] = drow[min(b0 + i, NB - 1)];
     }
     // Scales of blocks past NB are stored as 0, so those blocks add nothing.
-    __device__ __forceinline__ void commit(int c, int NB, uint8_t* act, float* dbuf) const {
+    __device__ __forceinline__ void commit(int c, int NB, uint8_t* act, float* dbuf,
+                                           const v4u (&v)[4], const float (&dv)[4]) const {
         const int blk = (threadIdx.x & 31) >> 1, half = threadIdx.x & 1;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int j = (threadIdx.x >> 5) + 8 * k;
-            *reinterpret_cast<uint4*>(act + j * kActPitch + blk * 32 + 16 * half) = v[k];
+            *reinterpret_cast<v4u*>(act + j * kActPitch + blk * 32 + 16 * half) = v[k];
         }
         if (threadIdx.x < 128) {
             const int j = threadIdx.x >> 2, b0 = (threadIdx.x & 3) * 4;
@@ -147,7 +149,7 @@ struct ActStager {
 // compiler can overlap the next block's LDS reads and MFMAs with the current
 // block's epilogue.
 template <int NG, bool TAP>
-__device__ __forceinline__ void gateup_loop(const PfArgs& a, Stager<32>& st, ActStager& as,
+__device__ __forceinline__ void gateup_loop(const PfArgs& a, const Stager<32>& st, const ActStager& as,
                                             uint8_t* lds, uint8_t* act, float* dbuf,
                                             double (&accg)[2][4], double (&accu)[2][4], int BH,
                                             int r0, int q, int lr, int s0, int n) {
@@ -157,17 +159,20 @@ __device__ __forceinline__ void gateup_loop(const PfArgs& a, Stager<32>& st, Act
         for (int i = 0; i < 4; ++i) accg[g][i] = accu[g][i] = 0.0;
     const v4i zero = {0, 0, 0, 0};
     const int nch = (BH + kChunk - 1) / kChunk;
-    st.issue(0, BH);
-    as.issue(0, BH);
-    st.commit(lds);
-    as.commit(0, BH, act, dbuf);
+    v4u wv[8], av[4];
+    float adv[4];
+    st.issue(0, BH, wv);
+    as.issue(0, BH, av, adv);
+    st.commit(lds, wv);
+    as.commit(0, BH, act, dbuf, av, adv);
     __syncthreads();
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) {
-            st.issue(c + 1, BH);
-            as.issue(c + 1, BH);
-        }
+        // unconditional (keeps the staging registers out of memory); after
+        // the last chunk this re-reads that chunk, from cache
+        const int cn = min(c + 1, nch - 1);
+        st.issue(cn, BH, wv);
+        as.issue(cn, BH, av, adv);
 #pragma unroll
         for (int bi = 0; bi < kChunk; ++bi) {
             const long ag = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
@@ -197,12 +202,10 @@ __device__ __forceinline__ void gateup_loop(const PfArgs& a, Stager<32>& st, Act
                 }
             }
         }
-        if (c + 1 < nch) {
-            __syncthreads();
-            st.commit(lds);
-            as.commit(c + 1, BH, act, dbuf);
-            __syncthreads();
-        }
+        __syncthreads();
+        st.commit(lds, wv);
+        as.commit(cn, BH, act, dbuf, av, adv);
+        __syncthreads();
     }
 }
 
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 
 // K loop of the down kernel (as gateup_loop, one weight matrix).
 template <int NG>
-__device__ __forceinline__ void down_loop(Stager<16>& st, ActStager& as, uint8_t* lds,
+__device__ __forceinline__ void down_loop(const Stager<16>& st, const ActStager& as, uint8_t* lds,
                                           uint8_t* act, float* dbuf, double (&acc)[2][4],
                                           int BI, int q, int lr) {
 #pragma unroll
@@ -292,17 +295,20 @@ __device__ __forceinline__ void down_loop(Stager<16>& st, ActStager& as, uint8_t
         for (int i = 0; i < 4; ++i) acc[g][i] = 0.0;
     const v4i zero = {0, 0, 0, 0};
     const int nch = (BI + kChunk - 1) / kChunk;
-    st.issue(0, BI);
-    as.issue(0, BI);
-    st.commit(lds);
-    as.commit(0, BI, act, dbuf);
+    v4u wv[4], av[4];
+    float adv[4];
+    st.issue(0, BI, wv);
+    as.issue(0, BI, av, adv);
+    st.commit(lds, wv);
+    as.commit(0, BI, act, dbuf, av, adv);
     __syncthreads();
 #pragma unroll 1
     for (int c = 0; c < nch; ++c) {
-        if (c + 1 < nch) {
-            st.issue(c + 1, BI);
-            as.issue(c + 1, BI);
-        }
+        // unconditional (keeps the staging registers out of memory); after
+        // the last chunk this re-reads that chunk, from cache
+        const int cn = min(c + 1, nch - 1);
+        st.issue(cn, BI, wv);
+        as.issue(cn, BI, av, adv);
 #pragma unroll
         for (int bi = 0; bi < kChunk; ++bi) {
             const long aw = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
@@ -319,12 +325,10 @@ __device__ __forceinline__ void down_loop(Stager<16>& st, ActStager& as, uint8_t
                 }
             }
         }
-        if (c + 1 < nch) {
-            __syncthreads();
-            st.commit(lds);
-            as.commit(c + 1, BI, act, dbuf);
-            __syncthreads();
-        }
+        __syncthreads();
+        st.commit(lds, wv);
+        as.commit(cn, BI, act, dbuf, av, adv);
+        __syncthreads();
     }
 }
 
