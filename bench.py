@@ -32,7 +32,9 @@ HBM_PEAK_GBPS = 8000.0
 # workload); dropped whenever that kernel changes.
 TRAFFIC = {
     # profiles/dec_kernels_decode_T1.txt
-    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55672.2 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55685.5 * 2 + 38.4) * 1024,
+    # profiles/pf_kernels_prefill_T512.txt
+    ("pf_gateup", "prefill T512 zipf-bias"): (1750193.6 * 2 + 14446.1) * 1024,
 }
 
 
