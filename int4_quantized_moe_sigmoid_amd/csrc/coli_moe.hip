@@ -216,7 +216,7 @@ void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     dec::k_dec_gateup<NT, NBJH, TAP><<<(a.S + um) * (nrb / hbw), 256, 0, s>>>(a);
     mk.mark("dec_down");
     if (NT == 1)
-        dec::k_dec_down<1, 1, 2, 4><<<a.H / 8, 256, 0, s>>>(a);
+        dec::k_dec_down<1, 1, 2, 2><<<a.H / 8, 256, 0, s>>>(a);
     else
         dec::k_dec_down_x<NT, 1><<<a.H / 8, 256, 0, s>>>(a);
 }
