@@ -89,6 +89,7 @@ __device__ __forceinline__ float q8_block_regs(const float* x, uint4& a0, uint4&
 // Routing of T <= 4 tokens, computed redundantly by every workgroup of B.
 struct Route {
     int idx[kMaxTok][16];
+    int flat[kMaxEntries];      // idx in (token, k) order: entry t * K + k
     float w[kMaxTok][16];
     int n_ent;                  // T * K entries, ordered by (expert, token)
     int ent_e[kMaxEntries];     // expert of sorted entry
@@ -141,9 +142,13 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
     double s[kMaxTok];
 #pragma unroll
     for (int t = 0; t < kMaxTok; ++t) {
-        s[t] = 1.0 / (1.0 + exp(-l[t]));
-        key[t] = order_key(s[t] + (double)bb);
-        if (filt && t < T && e < E) atomicMax(&Z.gmax[t][e >> 5], key[t]);
+        s[t] = 0.0;
+        key[t] = 0ull;
+        if (t < T) {  // uniform: no fp64 exp for absent tokens
+            s[t] = 1.0 / (1.0 + exp(-l[t]));
+            key[t] = order_key(s[t] + (double)bb);
+            if (filt && e < E) atomicMax(&Z.gmax[t][e >> 5], key[t]);
+        }
     }
     __syncthreads();
 #pragma unroll
@@ -169,12 +174,23 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
             const unsigned long long ki = Z.ckey[t][i];
             const int ei = Z.ce[t][i];
             int rank = 0;
-            for (int j = 0; j < m; ++j) {
-                const unsigned long long kj = Z.ckey[t][j];
-                rank += (kj > ki || (kj == ki && Z.ce[t][j] < ei)) ? 1 : 0;
+            // eight candidates per round, loads issued together
+            for (int j0 = 0; j0 < m; j0 += 8) {
+                unsigned long long kj[8];
+                int ej[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = min(j0 + u, m - 1);
+                    kj[u] = Z.ckey[t][j];
+                    ej[u] = Z.ce[t][j];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    rank += (j0 + u < m && (kj[u] > ki || (kj[u] == ki && ej[u] < ei))) ? 1 : 0;
             }
             if (rank < K) {
                 R.idx[t][rank] = ei;
+                R.flat[t * K + rank] = ei;
                 Z.ssel[t][rank] = Z.cs[t][i];
             }
         }
@@ -182,8 +198,13 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
     __syncthreads();
     if ((int)threadIdx.x < T * K) {
         const int t = threadIdx.x / K, k = threadIdx.x - t * K;
+        double sv[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) sv[kk] = Z.ssel[t][min(kk, K - 1)];
         double sum = 0.0;
-        for (int kk = 0; kk < K; ++kk) sum += Z.ssel[t][kk];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+            if (kk < K) sum += sv[kk];  // k ascending
         double v = Z.ssel[t][k];
         if (norm) v = v / sum;
         v = v * rho;
@@ -197,19 +218,30 @@ __device__ __forceinline__ void route_small(const double* logits, const float* b
                             int norm, double rho, Route& R, TopkScratch& Z) {
     topk_wg(logits, bias, T, E, K, norm, rho, R, Z);
     __syncthreads();
+    // entries j = t K + k in (token, k) order; entry j belongs to an earlier
+    // token than entry i exactly when j < t_i K
     const int n = T * K;
     const int i = threadIdx.x;
     int e = 0, t = 0, k = 0, rank = 0, first = 1, cnt = 0;
     if (i < n) {
         t = i / K;
         k = i - t * K;
-        e = R.idx[t][k];
-        for (int j = 0; j < n; ++j) {
-            const int tj = j / K, ej = R.idx[tj][j - tj * K];
-            if (ej < e || (ej == e && tj < t)) ++rank;
-            if (ej == e) {
-                ++cnt;
-                if (tj < t) first = 0;
+        e = R.flat[i];
+        const int tk = t * K;
+        for (int j0 = 0; j0 < n; j0 += 8) {
+            int ej[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ej[u] = R.flat[min(j0 + u, n - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;
+                if (j < n) {
+                    if (ej[u] < e || (ej[u] == e && j < tk)) ++rank;
+                    if (ej[u] == e) {
+                        ++cnt;
+                        if (j < tk) first = 0;
+                    }
+                }
             }
         }
     }
@@ -222,21 +254,29 @@ __device__ __forceinline__ void route_small(const double* logits, const float* b
     }
     if (i < T && S) R.slot_of[i][K] = n + i;
     __syncthreads();
+    // u = number of distinct experts below e = number of sorted entries j
+    // that start a new expert run and hold an expert < e
     if (i < n && first) {
         int u = 0;
-        for (int j = 0; j < n; ++j) {
-            const int ej = R.ent_e[j];
-            if ((j == 0 || R.ent_e[j - 1] != ej) && ej < e) ++u;
+        for (int j0 = 0; j0 < n; j0 += 8) {
+            int ej[8], ep[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const int j = min(j0 + v, n - 1);
+                ej[v] = R.ent_e[j];
+                ep[v] = R.ent_e[max(j - 1, 0)];
+            }
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const int j = j0 + v;
+                if (j < n && (j == 0 || ep[v] != ej[v]) && ej[v] < e) ++u;
+            }
         }
         R.u_e[u] = e;
         R.u_s0[u] = rank;
         R.u_n[u] = cnt;
-    }
-    if (i == 0) {
-        int u = 0;
-        for (int j = 0; j < n; ++j)
-            if (j == 0 || R.ent_e[j - 1] != R.ent_e[j]) ++u;
-        R.n_uniq = u;
+        // the largest expert's run ends the sorted entries: u + 1 experts
+        if (rank + cnt == n) R.n_uniq = u + 1;
     }
     __syncthreads();
 }
