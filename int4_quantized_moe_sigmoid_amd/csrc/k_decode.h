@@ -281,6 +281,117 @@ __device__ __forceinline__ void route_small(const double* logits, const float* b
     __syncthreads();
 }
 
+// Routing of a single token by one wave (wave 0), the other waves waiting
+// at one barrier; same selection rule and results as route_small. Lane L
+// holds experts 4L .. 4L+3 (E <= 256). The smallest of the 32-expert group
+// maxima (8 lanes per group) is found with lane shuffles; the experts at or
+// above it are compacted into LDS with ballots and ranked by who is ahead
+// (c descending, index ascending). All LDS traffic stays within the wave,
+// whose LDS operations complete in program order.
+__device__ __forceinline__ void route_one(const double* logits, const float* bias, int E, int K,
+                                          int S, int norm, double rho, Route& R, TopkScratch& Z) {
+    const int lane = threadIdx.x & 63;
+    if (threadIdx.x < 64) {
+        unsigned long long key[4];
+        double sv[4];
+        bool ok[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = 4 * lane + j;
+            ok[j] = e < E;
+            const double l = ok[j] ? logits[e] : 0.0;
+            const float b = ok[j] ? bias[e] : 0.0f;
+            sv[j] = 1.0 / (1.0 + exp(-l));
+            key[j] = ok[j] ? order_key(sv[j] + (double)b) : 0ull;
+        }
+        const int G = (E + 31) >> 5;
+        unsigned long long thr = 0ull;
+        if (G >= K) {
+            // group maximum over the 8 lanes of a group, then minimum over groups
+            unsigned long long gm = max(max(key[0], key[1]), max(key[2], key[3]));
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) gm = max(gm, (unsigned long long)__shfl_xor(gm, o, 64));
+            if ((lane >> 3) >= G) gm = ~0ull;  // no experts in this group
+#pragma unroll
+            for (int o = 8; o < 64; o <<= 1) gm = min(gm, (unsigned long long)__shfl_xor(gm, o, 64));
+            thr = gm;
+        }
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool c = ok[j] && key[j] >= thr;
+            const unsigned long long bal = __ballot(c);
+            if (c) {
+                const int p = base + __popcll(bal & ((1ull << lane) - 1ull));
+                Z.ckey[0][p] = key[j];
+                Z.ce[0][p] = 4 * lane + j;
+                Z.cs[0][p] = sv[j];
+            }
+            base += __popcll(bal);
+        }
+        const int m = base;
+        for (int i = lane; i < m; i += 64) {
+            const unsigned long long ki = Z.ckey[0][i];
+            const int ei = Z.ce[0][i];
+            int rank = 0;
+            for (int j0 = 0; j0 < m; j0 += 8) {
+                unsigned long long kj[8];
+                int ej[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = min(j0 + u, m - 1);
+                    kj[u] = Z.ckey[0][j];
+                    ej[u] = Z.ce[0][j];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    rank += (j0 + u < m && (kj[u] > ki || (kj[u] == ki && ej[u] < ei))) ? 1 : 0;
+            }
+            if (rank < K) {
+                R.idx[0][rank] = ei;
+                R.flat[rank] = ei;
+                Z.ssel[0][rank] = Z.cs[0][i];
+            }
+        }
+        if (lane < K) {
+            double ss[16];
+            int ix[16];
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                ss[kk] = Z.ssel[0][min(kk, K - 1)];
+                ix[kk] = R.idx[0][min(kk, K - 1)];
+            }
+            double sum = 0.0;
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk)
+                if (kk < K) sum += ss[kk];  // k ascending
+            double v = Z.ssel[0][lane];
+            if (norm) v = v / sum;
+            v = v * rho;
+            const float w = (float)v;
+            R.w[0][lane] = w;
+            // the K experts are distinct: slot = number of chosen experts below
+            const int e = R.idx[0][lane];
+            int slot = 0;
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk)
+                if (kk < K && ix[kk] < e) ++slot;
+            R.ent_e[slot] = e;
+            R.ent_t[slot] = 0;
+            R.ent_w[slot] = w;
+            R.slot_of[0][lane] = slot;
+            R.u_e[slot] = e;
+            R.u_s0[slot] = slot;
+            R.u_n[slot] = 1;
+        }
+        if (lane == 0) {
+            R.n_uniq = K;
+            if (S) R.slot_of[0][K] = K;
+        }
+    }
+    __syncthreads();
+}
+
 struct DecArgs {
     const float* x;
     const float* wr;
@@ -674,7 +785,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
         }
         b -= nw;
     }
-    route_small(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R, U.z);
+    if (NT == 1)
+        route_one(a.logits, a.bias, a.E, a.K, a.S, a.norm, a.rho, R, U.z);
+    else
+        route_small(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R, U.z);
     if (b == 0) publish_route(a, R);
     const int u = b / nw, hw = b - u * nw;
     if (u >= R.n_uniq) return;
