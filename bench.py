@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--sweep", type=str, default="",
+                    help="comma-separated token counts: time the layer of --config at each "
+                         "(one JSON line per count) instead of the default run")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB a few times (the "
                          "reference kernel that scales HBM byte counters) and exit")
@@ -87,6 +90,9 @@ def main():
     cfg = cs.CONFIGS[args.config]
     if cfg.n_layers > 1:
         run_stack(args, cfg)
+        return
+    if args.sweep:
+        run_sweep(args, cfg, [int(v) for v in args.sweep.split(",") if v])
         return
     T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
     lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho)
@@ -216,6 +222,55 @@ def gateup_roofline(kern, cfg, gate_up_bytes, T):
         out["int8_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
         out["int8_frac_of_5000_tops"] = round(ops / (ms * 1e-3) / 5.0e15, 4)
     return out
+
+
+def run_sweep(args, cfg, counts):
+    """Layer time against the number of tokens per call, on the weights and
+    input recipe of `cfg` (the few-token kernels serve T <= 3, the grouped
+    MFMA kernels T >= 4)."""
+    import torch
+
+    import coli_synth as cs
+    import int4_quantized_moe_sigmoid_amd as C
+
+    H, I, E, K, S = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho)
+    R = max(1, args.replicas)
+    layers = [C.LayerWeights(lc, *cs.build_layer(cfg, r, "cuda",
+                                                 lambda w, qv, sv: C.coli_pack_int4(w, qv, sv)))
+              for r in range(R)]
+    Tmax = max(counts)
+    ws = torch.empty(C.coli_moe_workspace_bytes(lc, Tmax), dtype=torch.uint8, device="cuda")
+    lay_counts = None
+    for T in counts:
+        n_in = 16
+        xs = []
+        for i in range(n_in):
+            raw = cs.activations(cs.with_tokens(cfg, T), i % R, "cuda", n_tok=T,
+                                 first_tok=(i // R) * T)
+            if cfg.rmsnorm_input:
+                xn = torch.empty_like(raw)
+                C.coli_rmsnorm(raw, xn, 1e-5)
+                raw = xn
+            xs.append(raw)
+        y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        for i in range(8):
+            C.coli_moe_forward(layers[i % R], xs[i % n_in], y, ws)
+        torch.cuda.synchronize()
+        steps = max(20, min(args.steps, int(2e5 / (T + 20))))
+        t0 = time.perf_counter()
+        for i in range(steps):
+            C.coli_moe_forward(layers[i % R], xs[i % n_in], y, ws)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        lay = C.coli_moe_workspace_layout(lc, T, 0)
+        cnt = ws[lay.counts:lay.counts + 4 * (E + S)].view(torch.int32)
+        uniq = int((cnt[:E] > 0).sum().item()) + S
+        print(json.dumps({"sweep": cfg.name, "tokens": T, "us_per_call": round(dt * 1e6, 2),
+                          "tokens_per_s": round(T / dt, 1), "experts_in_use": uniq,
+                          "path": "few-token" if T <= 3 else "grouped-mfma",
+                          "expert_weight_gbps": round(uniq * cfg.expert_bytes() / dt / 1e9, 1)}),
+              flush=True)
 
 
 def run_stack(args, cfg):

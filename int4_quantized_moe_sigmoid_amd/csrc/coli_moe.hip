@@ -200,7 +200,7 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
 // Few-token path: three fused kernels (k_decode.h). Shapes it covers:
 // hidden <= 6144, intermediate <= 2048, <= 256 routed experts.
 bool small_path_fits(const coli_moe_cfg& c, int64_t T) {
-    return T <= dec::kMaxTok && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
+    return T <= 3 && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
            c.inter <= 2048 && c.inter % 64 == 0 && c.n_experts <= 256;
 }
 
@@ -215,10 +215,10 @@ void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     const int hbw = (NT > 1) ? 2 : 1;  // h-blocks per workgroup (k_dec_gateup)
     dec::k_dec_gateup<NT, NBJH, TAP><<<(a.S + um) * (nrb / hbw), 256, 0, s>>>(a);
     mk.mark("dec_down");
-    if (NT == 1)
-        dec::k_dec_down<1, 1, 2, 2><<<a.H / 8, 256, 0, s>>>(a);
-    else
+    if (NT == 4)
         dec::k_dec_down_x<NT, 1><<<a.H / 8, 256, 0, s>>>(a);
+    else
+        dec::k_dec_down<NT, 1, 2, 2><<<a.H / 8, 256, 0, s>>>(a);
 }
 
 template <int NT>

@@ -931,16 +931,18 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
             }
         }
     };
-    // at one token at most top_k (<= 16) + 1 experts are in use
-    constexpr int kMaxB = (NT == 1) ? (17 + NB - 1) / NB : (kMaxEntries + 1 + NB - 1) / NB;
+    // two batches per iteration with fixed buffer roles (no dynamic indexing)
     Batch b0, b1;
     load(0, b0);
-#pragma unroll
-    for (int k = 0; k < kMaxB; ++k) {
-        if (k * NB >= nu) break;
-        if ((k + 1) * NB < nu) load((k + 1) * NB, (k & 1) ? b0 : b1);
+#pragma unroll 1
+    for (int v0 = 0; v0 < nu; v0 += 2 * NB) {
+        if (v0 + NB < nu) load(v0 + NB, b1);
         __builtin_amdgcn_sched_barrier(0);
-        compute(k * NB, (k & 1) ? b1 : b0);
+        compute(v0, b0);
+        if (v0 + NB >= nu) break;
+        if (v0 + 2 * NB < nu) load(v0 + 2 * NB, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(v0 + NB, b1);
     }
     if (lane < RPW * NT) {
         const int r = lane / NT, t = lane - r * NT;
