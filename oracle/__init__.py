@@ -37,6 +37,10 @@ def lib():
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         L.coli_ref_pack_int4.argtypes = [vp, i64, i64, vp, vp]
         L.coli_ref_unpack_int4.argtypes = [vp, i64, i64, vp]
+        L.coli_ref_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        L.coli_ref_e4m3_to_f32.restype = ctypes.c_float
+        L.coli_ref_fp8_to_f32.argtypes = [vp, vp, i64, i64, vp]
+        L.coli_ref_pack_fp8_int4.argtypes = [vp, vp, i64, i64, vp, vp]
         L.coli_ref_quant_q8.argtypes = [vp, i64, i64, vp, vp]
         L.coli_ref_block_dots.argtypes = [vp, i64, i64, vp, i64, vp]
         L.coli_ref_route.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
@@ -76,6 +80,38 @@ def pack_int4(w) -> tuple[np.ndarray, np.ndarray]:
     q = np.empty((rows, cols // 2), np.uint8)
     s = np.empty(rows, np.float32)
     _check(lib().coli_ref_pack_int4(_p(w), rows, cols, _p(q), _p(s)), "pack_int4")
+    return q, s
+
+
+def e4m3_to_f32(b: int) -> float:
+    """Value of one FP8 e4m3 code (the NaN code converts to 0)."""
+    return float(lib().coli_ref_e4m3_to_f32(int(b)))
+
+
+def fp8_to_f32(q8, block_scale) -> np.ndarray:
+    """FP8 e4m3 codes [rows, cols] (uint8) times their 128 x 128 block scale,
+    in fp32."""
+    q8 = _c(q8, np.uint8)
+    bs = _c(block_scale, np.float32)
+    rows, cols = q8.shape
+    if bs.shape != ((rows + 127) // 128, (cols + 127) // 128):
+        raise ValueError("block scale shape")
+    w = np.empty((rows, cols), np.float32)
+    _check(lib().coli_ref_fp8_to_f32(_p(q8), _p(bs), rows, cols, _p(w)), "fp8_to_f32")
+    return w
+
+
+def pack_fp8_int4(q8, block_scale) -> tuple[np.ndarray, np.ndarray]:
+    """FP8 e4m3 + block scales -> fp32 -> int4 (pack_int4 format)."""
+    q8 = _c(q8, np.uint8)
+    bs = _c(block_scale, np.float32)
+    rows, cols = q8.shape
+    if bs.shape != ((rows + 127) // 128, (cols + 127) // 128):
+        raise ValueError("block scale shape")
+    q = np.empty((rows, cols // 2), np.uint8)
+    s = np.empty(rows, np.float32)
+    _check(lib().coli_ref_pack_fp8_int4(_p(q8), _p(bs), rows, cols, _p(q), _p(s)),
+           "pack_fp8_int4")
     return q, s
 
 

@@ -86,6 +86,45 @@ int coli_ref_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q, f
     return REF_OK;
 }
 
+// ---------------------------------------------------------------------------
+// FP8 -> int4 converter front-end ([W] section 量化流程: source weights in
+// FP8 e4m3 with 128 x 128 block scales, converted to F32, then packed to int4
+// as above; the block size is the quantization_config shown in that section).
+//   e4m3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0 is
+//   subnormal (m * 2^-9); S.1111.111 is NaN; there are no infinities.
+//   w[r][c] = fp32( e4m3(q[r][c]) * bs[r / 128][c / 128] ), one rounding.
+// Readings: the block scale multiplies (it is stored as the inverse of the
+// quantiser's scale, as in the FP8 checkpoints of this model family); the NaN
+// code converts to 0 (a checkpoint holds none, and a NaN must not poison the
+// scale of its whole row).
+// ---------------------------------------------------------------------------
+float coli_ref_e4m3_to_f32(uint8_t b) {
+    const int sign = b >> 7, e = (b >> 3) & 0xF, m = b & 7;
+    if (e == 15 && m == 7) return 0.0f;  // NaN code
+    double v = (e == 0) ? std::ldexp((double)m, -9) : std::ldexp(1.0 + m / 8.0, e - 7);
+    return (float)(sign ? -v : v);
+}
+
+int coli_ref_fp8_to_f32(const uint8_t* q, const float* bs, int64_t rows, int64_t cols, float* w) {
+    if (!q || !bs || !w || rows < 0 || cols <= 0) return REF_EINVAL;
+    const int64_t nbc = (cols + 127) / 128;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            const float scale = bs[(r / 128) * nbc + c / 128];
+            w[r * cols + c] = coli_ref_e4m3_to_f32(q[r * cols + c]) * scale;
+        }
+    return REF_OK;
+}
+
+int coli_ref_pack_fp8_int4(const uint8_t* q8, const float* bs, int64_t rows, int64_t cols,
+                           uint8_t* q, float* scale) {
+    if (!q8 || !bs || !q || !scale || rows < 0 || cols <= 0 || (cols % 2) != 0) return REF_EINVAL;
+    std::vector<float> w((size_t)(rows * cols));
+    int rc = coli_ref_fp8_to_f32(q8, bs, rows, cols, w.data());
+    if (rc) return rc;
+    return coli_ref_pack_int4(w.data(), rows, cols, q, scale);
+}
+
 // Signed value of a 4-bit two's complement nibble (0x8 decodes to -8).
 static int ref_nibble_value(int v) { return v >= 8 ? v - 16 : v; }
 
