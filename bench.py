@@ -35,6 +35,8 @@ TRAFFIC = {
     ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55685.5 * 2 + 38.4) * 1024,
     # profiles/pf_kernels_prefill_T512.txt
     ("pf_gateup", "prefill T512 zipf-bias"): (1750193.6 * 2 + 14446.1) * 1024,
+    # profiles/pack_fp8_int4_layer.txt (the gate/up launch)
+    ("pack_fp8_gateup", "pack_fp8 layer H6144 I2048 experts257"): (3164334.8 * 2 + 3166240.7) * 1024,
 }
 
 
@@ -51,6 +53,9 @@ def parse():
     ap.add_argument("--sweep", type=str, default="",
                     help="comma-separated token counts: time the layer of --config at each "
                          "(one JSON line per count) instead of the default run")
+    ap.add_argument("--op", choices=("layer", "pack_fp8"), default="layer",
+                    help="pack_fp8: time the FP8 e4m3 (128 x 128 block scales) -> int4 "
+                         "conversion of one layer's expert weights instead of the layer")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB a few times (the "
                          "reference kernel that scales HBM byte counters) and exit")
@@ -88,6 +93,9 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = cs.CONFIGS[args.config]
+    if args.op == "pack_fp8":
+        run_pack_fp8(args, cfg)
+        return
     if cfg.n_layers > 1:
         run_stack(args, cfg)
         return
@@ -198,6 +206,92 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(out), flush=True)
+
+
+def run_pack_fp8(args, cfg):
+    """One step = the FP8 -> int4 conversion of one layer's expert weights
+    (E routed + S shared experts) as two launches: the gate and up rows of
+    every expert stacked into one [(E+S)*2I, H] matrix, the down rows into one
+    [(E+S)*H, I] matrix (rows are independent, so stacking changes nothing in
+    the result). Synthetic codes: seeded N(0, 64^2) rounded to e4m3; block
+    scales 2^k * U(1, 2). With power-of-two block scales instead, many w / s
+    are exact half-integers and most chunks take the kernel's exact-division
+    path (about twice the time)."""
+    import torch
+
+    import int4_quantized_moe_sigmoid_amd as C
+    H, I, n_exp = cfg.hidden, cfg.inter, cfg.n_experts + cfg.n_shared
+    mats = []
+    g = torch.Generator(device="cuda").manual_seed(17)
+    for rows_per, cols in ((2 * I, H), (H, I)):
+        rows = n_exp * rows_per
+        q8 = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+        for r0 in range(0, rows, 8192):
+            r1 = min(rows, r0 + 8192)
+            w = torch.randn((r1 - r0, cols), generator=g, device="cuda") * 64.0
+            q8[r0:r1] = w.to(torch.float8_e4m3fn).view(torch.uint8)
+        nb = ((rows + 127) // 128, (cols + 127) // 128)
+        # block scales as a block-wise FP8 quantiser writes them (block max / 448):
+        # arbitrary fp32 values of a few binades
+        bs = torch.exp2(torch.randint(-14, -6, nb, generator=g, device="cuda").float()) * \
+            (1.0 + torch.rand(nb, generator=g, device="cuda"))
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(rows, dtype=torch.float32, device="cuda")
+        mats.append((q8, bs, q, sc))
+    torch.cuda.synchronize()
+
+    def step():
+        for q8, bs, q, sc in mats:
+            C.coli_pack_fp8_int4(q8, bs, q, sc)
+
+    n_steps, n_warm = max(1, args.steps), args.warmup
+    for _ in range(n_warm):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # algorithmic bytes: every code read once, half a byte written per code, the
+    # row scales written, the block scales read
+    step_bytes = sum(q8.numel() * 1.5 + 4 * sc.numel() + 4 * bs.numel()
+                     for q8, bs, q, sc in mats)
+    # per-launch durations with HIP events on the launch stream
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    dur = [0.0, 0.0]
+    n_prof = min(n_steps, 10)
+    for _ in range(n_prof):
+        evs[0].record()
+        for j, (q8, bs, q, sc) in enumerate(mats):
+            C.coli_pack_fp8_int4(q8, bs, q, sc)
+            evs[j + 1].record()
+        torch.cuda.synchronize()
+        for j in range(2):
+            dur[j] += evs[j].elapsed_time(evs[j + 1]) / n_prof
+    gu_bytes = mats[0][0].numel() * 1.5 + 4 * mats[0][3].numel() + 4 * mats[0][1].numel()
+    achieved = gu_bytes / (dur[0] * 1e-3) / 1e9
+    ms = 1e3 * elapsed / n_steps
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    workload = f"pack_fp8 layer H{H} I{I} experts{n_exp}"
+    print(json.dumps({
+        "metric": "FP8 e4m3 (128x128 block scales) -> int4 conversion of one layer's experts, "
+                  "algorithmic HBM GB/s",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": n_warm, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8 e4m3 -> f32 -> int4",
+        "data": "synthetic (seeded N(0, 64^2) rounded to e4m3, block scales 2^k * U(1, 2))",
+        "config": {"workload": workload,
+                   "launches_per_step": 2, "parallelism": "none (1 GPU)"},
+        "kernel_avg_us": {"pack_fp8_gateup": round(dur[0] * 1e3, 1),
+                          "pack_fp8_down": round(dur[1] * 1e3, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "kernel": "k_pack_fp8_int4_wave (gate/up rows)",
+                     "algorithmic_bytes": int(gu_bytes),
+                     "traffic": TRAFFIC.get(("pack_fp8_gateup", workload))},
+        "cpu_baseline": None,
+    }), flush=True)
 
 
 def gateup_roofline(kern, cfg, gate_up_bytes, T):

@@ -132,6 +132,21 @@ COLI_API const char* coli_strerror(int code);
 COLI_API int coli_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q,
                             float* scale, void* stream);
 
+/* FP8 front-end of coli_pack_int4 (wmrh.cn page, section 量化流程: the
+ * source weights are FP8 e4m3 with one scale per 128 x 128 block — the
+ * weight_block_size of the quantization_config shown there — converted to F32
+ * and then packed to int4):
+ *   w[r][c] = fp32(e4m3(q8[r][c]) * block_scale[r/128][c/128]), one rounding;
+ *   e4m3 = 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, exponent 0
+ *   subnormal (m * 2^-9), no infinities; the NaN code S.1111.111 converts
+ *   to 0; then the rows are packed exactly as by coli_pack_int4.
+ *   q8 [rows, cols] u8 codes, block_scale [ceil(rows/128), ceil(cols/128)]
+ *   fp32 (in); q [rows, cols/2] u8, scale [rows] fp32 (out). cols must be a
+ *   positive multiple of 32, rows >= 0 (0: no-op). Bit-exact with the plain
+ *   definition. */
+COLI_API int coli_pack_fp8_int4(const uint8_t* q8, const float* block_scale, int64_t rows,
+                                int64_t cols, uint8_t* q, float* scale, void* stream);
+
 /* Q8_0 quantisation of activations ("Colibri：在笔记本上跑744B参数的AI模型",
  * 关键特性: Q8_0-style int8 activations): per block of 32 consecutive
  * elements d = fp32(max|x|/127), q = clamp(rint(x/d), -127, 127), d == 0

@@ -25,7 +25,7 @@ COLI_E_UNSUPPORTED = -5
 COLI_FWD_ACCUM = 1
 COLI_FWD_DEBUG_TAPS = 2
 
-EXPORTS = ("coli_strerror", "coli_pack_int4", "coli_quant_q8", "coli_moe_workspace_bytes",
+EXPORTS = ("coli_strerror", "coli_pack_int4", "coli_pack_fp8_int4", "coli_quant_q8", "coli_moe_workspace_bytes",
            "coli_moe_workspace_layout", "coli_moe_route", "coli_moe_forward",
            "coli_moe_forward_profiled", "coli_rmsnorm")
 
@@ -67,6 +67,7 @@ def _load():
     L.coli_strerror.argtypes = [i32]
     L.coli_strerror.restype = ctypes.c_char_p
     L.coli_pack_int4.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.coli_pack_fp8_int4.argtypes = [vp, vp, i64, i64, vp, vp, vp]
     L.coli_quant_q8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.coli_moe_workspace_bytes.argtypes = [ctypes.POINTER(coli_moe_cfg), i64, u32]
     L.coli_moe_workspace_bytes.restype = sz
@@ -163,6 +164,17 @@ def coli_pack_int4(w: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream
     _check(_lib.coli_pack_int4(_dev(w, "w", torch.float32), rows, cols,
                                _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
                                _stream(stream)), "coli_pack_int4")
+
+
+def coli_pack_fp8_int4(q8: torch.Tensor, block_scale: torch.Tensor, q: torch.Tensor,
+                       scale: torch.Tensor, stream=None):
+    rows, cols = q8.shape
+    if tuple(block_scale.shape) != ((rows + 127) // 128, (cols + 127) // 128):
+        raise ValueError("block_scale must be [ceil(rows/128), ceil(cols/128)]")
+    _check(_lib.coli_pack_fp8_int4(_dev(q8, "q8", torch.uint8),
+                                   _dev(block_scale, "block_scale", torch.float32), rows, cols,
+                                   _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
+                                   _stream(stream)), "coli_pack_fp8_int4")
 
 
 def coli_quant_q8(x: torch.Tensor, q: torch.Tensor, d: torch.Tensor, stream=None):

@@ -400,6 +400,33 @@ COLI_API int coli_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t*
     return hip_status();
 }
 
+COLI_API int coli_pack_fp8_int4(const uint8_t* q8, const float* block_scale, int64_t rows,
+                                int64_t cols, uint8_t* q, float* scale, void* stream) {
+    if (rows < 0 || cols <= 0 || cols % 32) return COLI_E_INVAL;
+    if (rows == 0) return COLI_OK;
+    if (!q8 || !block_scale || !q || !scale) return COLI_E_INVAL;
+    if (misaligned(q8) || misaligned(block_scale) || misaligned(q) || misaligned(scale))
+        return COLI_E_ALIGN;
+    if (rows > 0x7fffffffll) return COLI_E_UNSUPPORTED;
+    const hipStream_t st = (hipStream_t)stream;
+    if (cols % 1024 == 0 && cols <= 8192) {
+        const int cpl = (int)(cols / 1024);
+        const int64_t rpw = (8 % cpl == 0) ? 8 / cpl : 1;
+        const int64_t waves = (rows + rpw - 1) / rpw;
+        const unsigned grid = (unsigned)((waves + 3) / 4);
+        switch (cpl) {
+#define COLI_PACK_FP8(n) \
+    case n: k_pack_fp8_int4_wave<n><<<grid, 256, 0, st>>>(q8, block_scale, rows, q, scale); break;
+            COLI_PACK_FP8(1) COLI_PACK_FP8(2) COLI_PACK_FP8(3) COLI_PACK_FP8(4)
+            COLI_PACK_FP8(5) COLI_PACK_FP8(6) COLI_PACK_FP8(7) COLI_PACK_FP8(8)
+#undef COLI_PACK_FP8
+        }
+    } else {
+        k_pack_fp8_int4<<<(unsigned)rows, 256, 0, st>>>(q8, block_scale, cols, q, scale);
+    }
+    return hip_status();
+}
+
 COLI_API int coli_quant_q8(const float* x, int64_t n_tok, int64_t dim, int8_t* q, float* d,
                            void* stream) {
     if (n_tok < 0 || dim <= 0 || dim % 32) return COLI_E_INVAL;

@@ -102,3 +102,189 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, int64_t dim, do
     const double rms = sqrt(tot / (double)dim + eps);
     for (int64_t i = threadIdx.x; i < dim; i += 256) out[t * dim + i] = (float)((double)row[i] / rms);
 }
+
+// FP8 e4m3 code -> fp32 (1 sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; exponent 0 is subnormal m * 2^-9; no infinities). The NaN code
+// S.1111.111 converts to 0.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+    const uint32_t sign = (b & 0x80u) << 24, e = (b >> 3) & 0xFu, m = b & 7u;
+    if (e == 15u && m == 7u) return 0.0f;
+    if (e == 0u) return __uint_as_float(sign | __float_as_uint((float)m * 0x1p-9f));
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+// FP8 -> fp32 -> int4 for one row per workgroup: w = e4m3(q8) * bs[r/128][c/128]
+// (one fp32 rounding), then the pack of k_pack_int4. Four codes per thread.
+__global__ __launch_bounds__(256) void k_pack_fp8_int4(const uint8_t* __restrict__ q8,
+                                                       const float* __restrict__ bs,
+                                                       int64_t cols, uint8_t* __restrict__ q,
+                                                       float* __restrict__ scale) {
+    __shared__ float red[4];
+    const int64_t r = blockIdx.x;
+    const uint8_t* row = q8 + r * cols;
+    const float* bsr = bs + (r >> 7) * ((cols + 127) >> 7);
+    const int tid = threadIdx.x;
+    auto load4 = [&](int64_t j, float (&v)[4]) {
+        const uint32_t c = *reinterpret_cast<const uint32_t*>(row + j);
+        const float sc = bsr[j >> 7];  // the 4 codes share one 128-column block
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = e4m3_value((c >> (8 * i)) & 0xFFu) * sc;
+    };
+    float amax = 0.0f;
+    for (int64_t j = (int64_t)tid * 4; j < cols; j += 1024) {
+        float v[4];
+        load4(j, v);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+    amax = wave_max_f32(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax / 7.0f;
+    if (tid == 0) scale[r] = s;
+    uint8_t* out = q + r * (cols / 2);
+    for (int64_t j = (int64_t)tid * 4; j < cols; j += 1024) {
+        float v[4];
+        load4(j, v);
+        const uint32_t b = (uint32_t)(int4_code(v[0], s) & 0xF) |
+                           ((uint32_t)(int4_code(v[1], s) & 0xF) << 4) |
+                           ((uint32_t)(int4_code(v[2], s) & 0xF) << 8) |
+                           ((uint32_t)(int4_code(v[3], s) & 0xF) << 12);
+        *reinterpret_cast<uint16_t*>(out + j / 2) = (uint16_t)b;
+    }
+}
+
+// Whether the int4 codes of a row with scale s can be taken from a product
+// instead of the quotient w / s: s in [2^-100, 2^100] keeps 1/s a normal number.
+__device__ __forceinline__ bool int4_fast_ok(float s) {
+    return s >= 0x1p-100f && s <= 0x1p100f;
+}
+
+// Four e4m3 codes of a dword with the NaN codes (magnitude 0x7F) replaced by
+// zero bytes, bytewise without branches: a magnitude byte plus one reaches
+// 0x80 only for 0x7F, and no byte carries into the next.
+__device__ __forceinline__ uint32_t e4m3_zero_nan4(uint32_t c) {
+    const uint32_t nan = ((c & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    return c & ~(nan | (nan - (nan >> 7)));
+}
+
+// FP8 -> int4 for rows whose length is a multiple of 1024 codes, up to 8192:
+// one wave per row (CPL 16-code chunks per lane), or 8 / CPL rows per wave
+// when CPL divides 8, so every lane issues up to eight 16-byte loads at once.
+// No LDS, no barrier. Same result as k_pack_fp8_int4, bit for bit:
+//  * row maximum: e4m3 magnitudes order like their 7-bit codes and fp32
+//    rounding is monotone, so max_j |fl(e_j * bs)| = |fl(max_j |e_j| * bs)|
+//    within a 16-code chunk (one block scale): a packed 16-bit integer
+//    maximum of the magnitude bytes, then one conversion and one product per
+//    chunk, then a wave reduction;
+//  * codes: t = fl(e * m + 8) with m = fl(bs * fl(1/s)) differs from
+//    fl(w / s) + 8 by at most 7 * 4 * 2^-24 (three roundings in m and e * m,
+//    one in w) + 2^-21 (the add) + 7 * 2^-24 (the quotient) < 2.6e-6, so when
+//    t lies 4e-6 or more from every half-integer, rint(t) - 8 is the code.
+//    Otherwise (rare), or when s is outside [2^-100, 2^100], the lane redoes
+//    the chunk as clamp(rint(fl(e * bs) / s)). An all-zero row (s = 0) takes
+//    the product path with 1/s replaced by 0;
+//  * packing: rint(t) in [1, 15] is the offset-binary code, written into its
+//    byte by a float -> u8 conversion (exact on integers); two bytes per nibble
+//    pair are merged with a shift, eight codes gathered with one byte permute,
+//    and xor 8 per nibble turns offset binary into two's complement.
+template <int CPL>
+__global__ __launch_bounds__(256) void k_pack_fp8_int4_wave(const uint8_t* __restrict__ q8,
+                                                            const float* __restrict__ bs,
+                                                            int64_t rows, uint8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    typedef unsigned short v2h __attribute__((ext_vector_type(2)));
+    constexpr int RPW = (8 % CPL == 0) ? 8 / CPL : 1;  // rows per wave
+    constexpr int NCH = RPW * CPL;                       // chunks per lane
+    constexpr int64_t cols = 1024 * CPL;
+    constexpr int nbc = (int)(cols / 128);
+    const int lane = threadIdx.x & 63;
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+    if (r0 >= rows) return;
+    v4u c[NCH];
+    float sc[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+        const int64_t r = min(r0 + i / CPL, rows - 1);  // a ragged last wave rereads its last row
+        const int j = lane + 64 * (i % CPL);            // chunk within the row
+        c[i] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(q8 + r * cols) + j);
+        sc[i] = bs[(r >> 7) * nbc + (j >> 3)];          // 16 codes inside one 128-column block
+    }
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) c[i][d] = e4m3_zero_nan4(c[i][d]);
+#pragma unroll
+    for (int g = 0; g < RPW; ++g) {
+        const int64_t r = r0 + g;
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = g * CPL; i < (g + 1) * CPL; ++i) {
+            v2h ev = {0, 0}, od = {0, 0};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                ev = __builtin_elementwise_max(ev, __builtin_bit_cast(v2h, c[i][d] & 0x007F007Fu));
+                od = __builtin_elementwise_max(od, __builtin_bit_cast(v2h, c[i][d] & 0x7F007F00u));
+            }
+            const uint32_t mag = max(max((uint32_t)ev[0], (uint32_t)ev[1]),
+                                     max((uint32_t)od[0], (uint32_t)od[1]) >> 8);
+            amax = fmaxf(amax, fabsf(__builtin_amdgcn_cvt_f32_fp8((int)mag, 0) * sc[i]));
+        }
+        amax = wave_max_f32(amax);
+        const float s = amax / 7.0f;
+        if (r >= rows) break;
+        if (lane == 0) scale[r] = s;
+        const bool fast = s == 0.0f || int4_fast_ok(s);
+        const float inv = (s == 0.0f || !fast) ? 0.0f : 1.0f / s;
+        uint8_t* out = q + r * (cols / 2);
+#pragma unroll
+        for (int i = g * CPL; i < (g + 1) * CPL; ++i) {
+            // a chunk of zeros may have bs far above s: keep m finite (any
+            // chunk with a nonzero code has m <= 7 / 2^-9)
+            const float m = fminf(sc[i] * inv, 0x1p100f);
+            uint32_t b[4];
+            float dmax = 0.0f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i][d], false);
+                const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i][d], true);
+                const float e4[4] = {lo[0], lo[1], hi[0], hi[1]};
+                uint32_t x = 0;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float t = fmaf(e4[k], m, 8.0f);
+                    const float rt = __builtin_rintf(t);
+                    dmax = fmaxf(dmax, fabsf(t - rt));
+                    x = __builtin_amdgcn_cvt_pk_u8_f32(rt, k, x);
+                }
+                b[d] = x;
+            }
+            if (!fast || dmax > 0.5f - 4e-6f) {  // s != 0 here
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i][d], false);
+                    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[i][d], true);
+                    const float e4[4] = {lo[0], lo[1], hi[0], hi[1]};
+                    uint32_t x = 0;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const float w = e4[k] * sc[i];
+                        const float cq = fminf(fmaxf(__builtin_rintf(w / s), -7.0f), 7.0f);
+                        x = __builtin_amdgcn_cvt_pk_u8_f32(cq + 8.0f, k, x);
+                    }
+                    b[d] = x;
+                }
+            }
+            v2u o;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t zl = b[2 * h] | (b[2 * h] >> 4);
+                const uint32_t zh = b[2 * h + 1] | (b[2 * h + 1] >> 4);
+                o[h] = __builtin_amdgcn_perm(zh, zl, 0x06040200u) ^ 0x88888888u;
+            }
+            reinterpret_cast<v2u*>(out)[lane + 64 * (i % CPL)] = o;
+        }
+    }
+}

@@ -145,3 +145,54 @@ def test_rejects_bad_arguments(C):
     assert e.value.code == C.COLI_E_WORKSPACE
     bad = C.make_cfg(6144, 2048, 4, 8)
     assert C.lib().coli_moe_workspace_bytes(bad, 1, 0) == 0
+
+
+def _fp8_weights(rows, cols, seed, nan_codes):
+    """Seeded FP8 e4m3 codes of normally distributed weights with 128 x 128
+    block scales of a few binades (a block-quantised checkpoint's shape)."""
+    g = torch.Generator().manual_seed(seed)
+    w = torch.randn(rows, cols, generator=g) * 64.0
+    q8 = w.to(torch.float8_e4m3fn).view(torch.uint8)
+    if nan_codes:
+        q8[0, :7] = 0x7F
+        q8[-1, -5:] = 0xFF
+        q8[rows // 2] = 0x80  # a row of negative zeros packs to scale 0
+    nb = ((rows + 127) // 128, (cols + 127) // 128)
+    bs = torch.exp2(torch.randint(-14, -6, nb, generator=g).float()) * \
+        (1.0 + torch.rand(nb, generator=g))
+    return q8.contiguous(), bs.float().contiguous()
+
+
+@pytest.mark.parametrize("rows,cols,nan_codes", [(200, 352, True), (1, 32, False),
+                                                 (130, 8192, True), (3, 8224, True),
+                                                 (13, 2048, True), (5, 3072, False),
+                                                 (9, 1024, True), (129, 4096, False),
+                                                 (2048, 6144, True), (6144, 2048, False)])
+def test_pack_fp8_int4_bit_exact(C, ref, rows, cols, nan_codes):
+    print("[case] pack_fp8_int4", rows, cols, flush=True)
+    q8, bs = _fp8_weights(rows, cols, rows + cols, nan_codes)
+    q = torch.empty(rows, cols // 2, dtype=torch.uint8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    C.coli_pack_fp8_int4(q8.cuda(), bs.cuda(), q, s)
+    torch.cuda.synchronize()
+    rq, rs = ref.pack_fp8_int4(q8.numpy(), bs.numpy())
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("cols", [256, 1024])
+def test_pack_fp8_int4_every_code(C, ref, cols):
+    """Every e4m3 code (subnormals, both zeros, both NaN codes, +-448) in every
+    position of a 16-code chunk, under unit and extreme block scales."""
+    print("[case] pack_fp8_int4 every code", cols, flush=True)
+    rows = 256
+    q8 = ((torch.arange(rows)[:, None] + torch.arange(cols)[None, :]) % 256).to(torch.uint8)
+    bs = torch.tensor([[1.0, 2.0 ** -120], [2.0 ** 100, 3.0]], dtype=torch.float32)
+    bs = bs.repeat(1, cols // 256)
+    q = torch.empty(rows, cols // 2, dtype=torch.uint8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    C.coli_pack_fp8_int4(q8.cuda(), bs.cuda(), q, s)
+    torch.cuda.synchronize()
+    rq, rs = ref.pack_fp8_int4(q8.numpy(), bs.numpy())
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
