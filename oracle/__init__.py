@@ -44,7 +44,7 @@ def lib():
         L.coli_ref_quant_q8.argtypes = [vp, i64, i64, vp, vp]
         L.coli_ref_block_dots.argtypes = [vp, i64, i64, vp, i64, vp]
         L.coli_ref_route.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
-                                     ctypes.c_double, vp, vp, vp]
+                                     ctypes.c_double, i64, i64, vp, vp, vp]
         L.coli_ref_rmsnorm.argtypes = [vp, i64, i64, ctypes.c_double, vp]
         L.coli_ref_moe_forward.argtypes = [vp, vp, i64, vp, vp, vp, ctypes.c_int, vp]
         L.coli_ref_set_threads.argtypes = [ctypes.c_int]
@@ -146,7 +146,10 @@ def block_dots(wq, cols: int, qx) -> np.ndarray:
     return out
 
 
-def route(x, wr, bias, top_k: int, norm: bool = True, rho: float = 2.5):
+def route(x, wr, bias, top_k: int, norm: bool = True, rho: float = 2.5, n_group: int = 1,
+          topk_group: int = 1):
+    """Sigmoid router + top-k; n_group > 1 selects among the topk_group best
+    groups only (group score: sum of its two largest biased scores)."""
     x = _c(x, np.float32)
     wr = _c(wr, np.float32)
     bias = _c(bias, np.float32)
@@ -156,7 +159,8 @@ def route(x, wr, bias, top_k: int, norm: bool = True, rho: float = 2.5):
     w = np.empty((T, top_k), np.float32)
     logits = np.empty((T, E), np.float64)
     _check(lib().coli_ref_route(_p(x), _p(wr), _p(bias), T, H, E, top_k, int(norm),
-                                float(np.float32(rho)), _p(idx), _p(w), _p(logits)), "route")
+                                float(np.float32(rho)), int(n_group), int(topk_group), _p(idx),
+                                _p(w), _p(logits)), "route")
     return idx, w, logits
 
 
@@ -176,7 +180,8 @@ class _Layer(ctypes.Structure):
                 ("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
                 ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p),
                 ("down_q", ctypes.c_void_p), ("gate_s", ctypes.c_void_p),
-                ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p)]
+                ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
+                ("n_group", ctypes.c_int64), ("topk_group", ctypes.c_int64)]
 
 
 class _Taps(ctypes.Structure):
@@ -193,8 +198,9 @@ class OracleLayer:
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, n_shared, norm_topk, rho,
-                 w_router, bias, experts: dict):
+                 w_router, bias, experts: dict, n_group: int = 1, topk_group: int = 1):
         self.hidden, self.inter = int(hidden), int(inter)
+        self.n_group, self.topk_group = int(n_group), int(topk_group)
         self.n_experts, self.top_k, self.n_shared = int(n_experts), int(top_k), int(n_shared)
         self.norm_topk, self.rho = bool(norm_topk), float(np.float32(rho))
         self.w_router = None if w_router is None else _c(w_router, np.float32)
@@ -225,7 +231,8 @@ class OracleLayer:
                    ctypes.cast(arrs["down_q"], ctypes.c_void_p),
                    ctypes.cast(arrs["gate_s"], ctypes.c_void_p),
                    ctypes.cast(arrs["up_s"], ctypes.c_void_p),
-                   ctypes.cast(arrs["down_s"], ctypes.c_void_p))
+                   ctypes.cast(arrs["down_s"], ctypes.c_void_p),
+                   self.n_group, self.topk_group)
         return s, arrs
 
     def forward(self, x, forced_idx=None, forced_w=None, y_in=None, taps: bool = False):

@@ -221,11 +221,18 @@ static float ref_row_dot(const uint8_t* wrow, float s_r, const int8_t* q, const 
 //   pick the K largest c, ties to the lower expert index, in descending order
 //   w_k = s[e_k]; if normalising: w_k = w_k / sum_k w_k; w_k = w_k * rho; fp32
 // Readings: the correction bias only steers selection (the gate value is
-// the unbiased sigmoid, DeepSeek-V3 style); no expert groups (a single group).
+// the unbiased sigmoid, DeepSeek-V3 style).
+// Group-limited selection (the topk_method knob of [A] 路由策略定制, read as
+// DeepSeek-V3's: the pages name the knob, not its algorithm), when
+// n_group > 1: the E experts form n_group consecutive groups of E / n_group;
+// a group's score is the sum of its two largest c (its only c when a group
+// holds one expert); the topk_group groups with the largest scores (ties to
+// the lower group index) stay eligible and the K experts are chosen among
+// their experts only. n_group = 1 is the plain selection above.
 // ---------------------------------------------------------------------------
 static void ref_route_token(const float* x, const float* wr, const float* bias, int64_t H,
-                            int64_t E, int64_t K, int norm, double rho, int32_t* idx,
-                            float* w, double* logits_out) {
+                            int64_t E, int64_t K, int norm, double rho, int64_t n_group,
+                            int64_t topk_group, int32_t* idx, float* w, double* logits_out) {
     std::vector<double> s(E), c(E);
     for (int64_t e = 0; e < E; ++e) {
         double l = 0.0;
@@ -234,12 +241,41 @@ static void ref_route_token(const float* x, const float* wr, const float* bias, 
         s[e] = 1.0 / (1.0 + std::exp(-l));
         c[e] = s[e] + (double)bias[e];
     }
+    std::vector<char> eligible(E, 1);
+    if (n_group > 1) {
+        const int64_t gs = E / n_group;
+        std::vector<double> gscore(n_group);
+        for (int64_t g = 0; g < n_group; ++g) {
+            // the largest and second largest c of the group
+            int64_t first = g * gs;
+            for (int64_t e = g * gs; e < (g + 1) * gs; ++e)
+                if (c[e] > c[first]) first = e;
+            double second = 0.0;
+            bool have_second = false;
+            for (int64_t e = g * gs; e < (g + 1) * gs; ++e) {
+                if (e == first) continue;
+                if (!have_second || c[e] > second) second = c[e];
+                have_second = true;
+            }
+            gscore[g] = have_second ? c[first] + second : c[first];
+        }
+        std::vector<char> kept(n_group, 0);
+        for (int64_t j = 0; j < topk_group; ++j) {
+            int64_t best = -1;
+            for (int64_t g = 0; g < n_group; ++g) {
+                if (kept[g]) continue;
+                if (best < 0 || gscore[g] > gscore[best]) best = g;  // ties: lower group
+            }
+            kept[best] = 1;
+        }
+        for (int64_t e = 0; e < E; ++e) eligible[e] = kept[e / gs];
+    }
     std::vector<char> taken(E, 0);
     std::vector<double> wk(K);
     for (int64_t k = 0; k < K; ++k) {
         int64_t best = -1;
         for (int64_t e = 0; e < E; ++e) {
-            if (taken[e]) continue;
+            if (taken[e] || !eligible[e]) continue;
             if (best < 0 || c[e] > c[best]) best = e;  // strict '>' keeps the lower index on ties
         }
         taken[best] = 1;
@@ -256,15 +292,22 @@ static void ref_route_token(const float* x, const float* wr, const float* bias, 
     }
 }
 
+// n_group >= 1 must divide n_experts; 1 <= topk_group <= n_group; the kept
+// groups must hold at least top_k experts.
+static bool ref_groups_ok(int64_t E, int64_t K, int64_t n_group, int64_t topk_group) {
+    return n_group >= 1 && E % n_group == 0 && topk_group >= 1 && topk_group <= n_group &&
+           (n_group == 1 || topk_group * (E / n_group) >= K);
+}
+
 int coli_ref_route(const float* x, const float* wr, const float* bias, int64_t n_tok,
                    int64_t hidden, int64_t n_experts, int64_t top_k, int norm, double rho,
-                   int32_t* idx, float* w, double* logits) {
+                   int64_t n_group, int64_t topk_group, int32_t* idx, float* w, double* logits) {
     if (!x || !wr || !bias || !idx || !w || n_tok < 0 || hidden <= 0 || n_experts <= 0 ||
-        top_k <= 0 || top_k > n_experts)
+        top_k <= 0 || top_k > n_experts || !ref_groups_ok(n_experts, top_k, n_group, topk_group))
         return REF_EINVAL;
     for (int64_t t = 0; t < n_tok; ++t)
-        ref_route_token(x + t * hidden, wr, bias, hidden, n_experts, top_k, norm, rho,
-                        idx + t * top_k, w + t * top_k,
+        ref_route_token(x + t * hidden, wr, bias, hidden, n_experts, top_k, norm, rho, n_group,
+                        topk_group, idx + t * top_k, w + t * top_k,
                         logits ? logits + t * n_experts : nullptr);
     return REF_OK;
 }
@@ -298,6 +341,7 @@ typedef struct coli_ref_layer {
     const float* const* gate_s;   // [I]
     const float* const* up_s;     // [I]
     const float* const* down_s;   // [H]
+    int64_t n_group, topk_group;  // group-limited selection (1, 1: none)
 } coli_ref_layer;
 
 // Optional intermediate outputs, indexed by token t and slot k (k < K: the
@@ -359,7 +403,7 @@ int coli_ref_moe_forward(const coli_ref_layer* L, const float* x, int64_t n_tok,
     const int64_t H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k,
                   S = L->n_shared;
     if (H <= 0 || I <= 0 || (H % 32) || (I % 32) || E <= 0 || K <= 0 || K > E || S < 0 ||
-        S > 1)
+        S > 1 || !ref_groups_ok(E, K, L->n_group, L->topk_group))
         return REF_EINVAL;
     if ((forced_idx == nullptr) != (forced_w == nullptr)) return REF_EINVAL;
     const int64_t KS = K + S;
@@ -379,7 +423,7 @@ int coli_ref_moe_forward(const coli_ref_layer* L, const float* x, int64_t n_tok,
         } else {
             if (!L->w_router || !L->bias) return REF_EINVAL;
             ref_route_token(xt, L->w_router, L->bias, H, E, K, (int)L->norm_topk, L->rho,
-                            idx.data(), w.data(),
+                            L->n_group, L->topk_group, idx.data(), w.data(),
                             (taps && taps->logits) ? taps->logits + t * E : nullptr);
         }
         coli_ref_quant_q8(xt, 1, H, qx.data(), dx.data());
