@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--sweep", type=str, default="",
                     help="comma-separated token counts: time the layer of --config at each "
                          "(one JSON line per count) instead of the default run")
+    ap.add_argument("--groups", type=str, default="",
+                    help="NG,TG: group-limited expert selection (NG groups, the TG best kept)")
     ap.add_argument("--op", choices=("layer", "pack_fp8"), default="layer",
                     help="pack_fp8: time the FP8 e4m3 (128 x 128 block scales) -> int4 "
                          "conversion of one layer's expert weights instead of the layer")
@@ -103,7 +105,8 @@ def main():
         run_sweep(args, cfg, [int(v) for v in args.sweep.split(",") if v])
         return
     T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
-    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho)
+    ng, tg = (int(v) for v in args.groups.split(",")) if args.groups else (1, 1)
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, ng, tg)
     R = max(1, args.replicas)
     n_steps, n_warm = args.steps, args.warmup
     n_inputs = n_steps + n_warm
@@ -193,8 +196,10 @@ def main():
         "warmup": n_warm, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "int4xint8 (int32 block dots, f64 scales)",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights packed by coli_pack_int4)",
-        "config": {"workload": cfg.name, "tokens_per_step": T, "hidden": H, "inter": I,
+        "config": {"workload": cfg.name + (f" groups {ng}/{tg}" if ng > 1 else ""),
+                   "tokens_per_step": T, "hidden": H, "inter": I,
                    "n_experts": E, "top_k": K, "n_shared": S, "weight_replicas": R,
+                   "n_group": ng, "topk_group": tg,
                    "parallelism": "none (1 GPU)"},
         "expert_weight_gbps": round(weight_gbps, 1),
         "expert_weight_frac_hbm": round(weight_gbps / HBM_PEAK_GBPS, 4),
@@ -328,7 +333,8 @@ def run_sweep(args, cfg, counts):
     import int4_quantized_moe_sigmoid_amd as C
 
     H, I, E, K, S = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
-    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho)
+    ng, tg = (int(v) for v in args.groups.split(",")) if args.groups else (1, 1)
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, ng, tg)
     R = max(1, args.replicas)
     layers = [C.LayerWeights(lc, *cs.build_layer(cfg, r, "cuda",
                                                  lambda w, qv, sv: C.coli_pack_int4(w, qv, sv)))

@@ -68,6 +68,10 @@ typedef struct coli_moe_cfg {
     int32_t n_shared;     /* 0 or 1 shared expert (stored after the routed ones) */
     int32_t norm_topk;    /* norm_topk_prob: 1 = divide the K gate values by their sum */
     float routed_scale;   /* routed_scaling_factor rho, applied after normalisation */
+    int32_t n_group;      /* group-limited selection (topk_method): 0 or 1 = none; else
+                             2..64 groups of n_experts / n_group consecutive experts */
+    int32_t topk_group;   /* groups kept when n_group > 1: 1..n_group, and the kept
+                             groups must hold at least top_k experts */
     int32_t reserved;     /* must be 0 */
 } coli_moe_cfg;
 
@@ -169,6 +173,10 @@ COLI_API int coli_moe_workspace_layout(const coli_moe_cfg* cfg, int64_t n_tok, u
  * MoE的工作原理 and 路由策略定制; Colibri page, 关键特性):
  *   l = x . w_router^T (accumulated in fp64), s = 1/(1+exp(-l)), c = s + bias;
  *   the K largest c in descending order, ties to the lower expert index;
+ *   with cfg->n_group > 1 (the topk_method knob, read as DeepSeek-V3's
+ *   group-limited selection) only the experts of the cfg->topk_group groups
+ *   with the largest group scores compete, a group's score being the sum of
+ *   its two largest c (ties to the lower group index);
  *   w_k = s[e_k], divided by sum_k s[e_k] when cfg->norm_topk, times
  *   cfg->routed_scale, rounded to fp32.
  *   x [n_tok, H] fp32, w_router [E, H], bias [E] (in); topk_idx [n_tok, K]

@@ -40,7 +40,8 @@ class coli_moe_cfg(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
-                ("routed_scale", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("routed_scale", ctypes.c_float), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class coli_moe_weights(ctypes.Structure):
@@ -118,9 +119,12 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_cfg(hidden: int, inter: int, n_experts: int, top_k: int, n_shared: int = 1,
-             norm_topk: bool = True, routed_scale: float = 2.5) -> coli_moe_cfg:
+             norm_topk: bool = True, routed_scale: float = 2.5, n_group: int = 1,
+             topk_group: int = 1) -> coli_moe_cfg:
+    """n_group > 1 selects the experts among the topk_group best of n_group
+    groups (group-limited top-k); 1 is the plain selection."""
     return coli_moe_cfg(hidden, inter, n_experts, top_k, n_shared, int(bool(norm_topk)),
-                        routed_scale, 0)
+                        routed_scale, int(n_group), int(topk_group), 0)
 
 
 class LayerWeights:

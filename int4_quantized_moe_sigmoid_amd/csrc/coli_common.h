@@ -68,3 +68,46 @@ __device__ __forceinline__ float swiglu_f32(float g, float u) {
     const double s = z / (1.0 + exp(-z));
     return (float)(s * (double)u);
 }
+
+// Group-limited expert selection (the topk_method knob of the GLM-5.2-colibri
+// architecture page, section on routing options, read as DeepSeek-V3's
+// group-limited routing). The E experts form ng groups of gs consecutive
+// experts; a group's score is the sum of its two largest biased scores c (its
+// only c when gs = 1); the tg groups with the largest scores stay eligible,
+// ties to the lower group index. Called by one whole wave with the c of the E
+// experts in c_lds (written by this wave); returns, in every lane, the bit
+// mask of the kept groups (ng <= 64).
+struct GroupSel {
+    int ng, gs, tg;  // ng <= 1: no groups
+};
+
+__device__ __forceinline__ unsigned long long group_keep_mask(const double* c_lds, GroupSel g) {
+    const int lane = threadIdx.x & 63;
+    double score = -__builtin_inf();
+    if (lane < g.ng) {
+        const double* p = c_lds + lane * g.gs;
+        double a = -__builtin_inf(), b = -__builtin_inf();
+        for (int i0 = 0; i0 < g.gs; i0 += 8) {  // eight loads in flight per round
+            double v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = p[min(i0 + u, g.gs - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (i0 + u >= g.gs) break;
+                if (v[u] > a) {
+                    b = a;
+                    a = v[u];
+                } else if (v[u] > b) {
+                    b = v[u];
+                }
+            }
+        }
+        score = g.gs > 1 ? a + b : a;
+    }
+    int rank = 0;
+    for (int j = 0; j < g.ng; ++j) {
+        const double o = __shfl(score, j, 64);
+        rank += (o > score || (o == score && j < lane)) ? 1 : 0;
+    }
+    return __ballot(lane < g.ng && rank < g.tg);
+}

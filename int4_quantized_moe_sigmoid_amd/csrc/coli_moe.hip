@@ -36,10 +36,23 @@ int check_cfg(const coli_moe_cfg* c) {
     if (c->n_experts <= 0 || c->top_k <= 0 || c->top_k > c->n_experts) return COLI_E_INVAL;
     if (c->n_shared < 0 || c->n_shared > 1) return COLI_E_INVAL;
     if (!std::isfinite(c->routed_scale)) return COLI_E_INVAL;
+    if (c->n_group < 0) return COLI_E_INVAL;
+    if (c->n_group > 1) {
+        if (c->n_group > 64) return COLI_E_UNSUPPORTED;
+        if (c->n_experts % c->n_group || c->topk_group < 1 || c->topk_group > c->n_group ||
+            (int64_t)c->topk_group * (c->n_experts / c->n_group) < c->top_k)
+            return COLI_E_INVAL;
+    }
     if (c->hidden > kMaxHidden || c->inter > kMaxInter || c->n_experts > kMaxExperts ||
         c->top_k > kMaxTopK)
         return COLI_E_UNSUPPORTED;
     return COLI_OK;
+}
+
+GroupSel group_sel(const coli_moe_cfg& c) {
+    GroupSel g{1, c.n_experts, 1};
+    if (c.n_group > 1) g = GroupSel{c.n_group, c.n_experts / c.n_group, c.topk_group};
+    return g;
 }
 
 struct Layout {
@@ -184,16 +197,19 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
     const unsigned gb = (unsigned)((T + 3) / 4);
     const double rho = (double)c.routed_scale;
     const int norm = c.norm_topk ? 1 : 0;
+    const GroupSel gsel = group_sel(c);
+    // with groups, each wave stages its token's biased scores in LDS
+    const size_t tk_lds = gsel.ng > 1 ? (size_t)4 * E * sizeof(double) : 0;
     if (E <= 64)
-        k_topk<1><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+        k_topk<1><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else if (E <= 128)
-        k_topk<2><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+        k_topk<2><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else if (E <= 256)
-        k_topk<4><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+        k_topk<4><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else if (E <= 512)
-        k_topk<8><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+        k_topk<8><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else
-        k_topk<16><<<gb, 256, 0, s>>>(logits, bias, (int)T, E, K, norm, rho, idx, wts);
+        k_topk<16><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
 }
 
 // Template selection for the fused few-token path.
@@ -290,6 +306,7 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         a.blob_q = blob_q; a.blob_s = blob_s;
         a.T = (int)T; a.H = H; a.I = I; a.E = E; a.K = K; a.S = S; a.norm = c.norm_topk ? 1 : 0;
         a.rho = (double)c.routed_scale;
+        a.gsel = group_sel(c);
         a.logits = logits; a.qx = qx; a.dx = dx; a.idx = idx; a.wts = wts; a.counts = counts;
         a.offs = offs; a.slot_of = slot_of; a.slot_tok = slot_tok;
         a.uinfo = reinterpret_cast<int32_t*>(base + L.uinfo);

@@ -104,7 +104,10 @@ struct Route {
 
 // LDS scratch of the top-k, dead once the routing is done.
 struct TopkScratch {
-    unsigned long long gmax[kMaxTok][8];  // max key of each 32-expert group
+    unsigned long long gmax[kMaxTok][8];   // max key of each 32-expert group
+    unsigned long long gmax8[kMaxTok][32]; // max key of each 8-expert group (groups only)
+    unsigned long long keep[kMaxTok];      // kept routing groups (group-limited selection)
+    unsigned long long gthr[kMaxTok];      // key threshold from the kept groups (0: none)
     int ncand[kMaxTok];
     unsigned long long ckey[kMaxTok][256];
     int ce[kMaxTok][256];
@@ -118,6 +121,16 @@ __device__ __forceinline__ unsigned long long order_key(double c) {
     return (b < 0) ? ~(unsigned long long)b : ((unsigned long long)b | 0x8000000000000000ull);
 }
 
+// The two largest of the values held by n aligned lanes (n a power of two,
+// <= 64), merged with xor shuffles; every lane of the n ends with the pair.
+__device__ __forceinline__ void top2_lanes(double& a, double& b, int n) {
+    for (int o = 1; o < n; o <<= 1) {
+        const double oa = __shfl_xor(a, o, 64), ob = __shfl_xor(b, o, 64);
+        b = fmax(fmin(a, oa), fmax(b, ob));
+        a = fmax(a, oa);
+    }
+}
+
 // Sigmoid + bias + top-k + gate weights of T <= 4 tokens by the whole
 // workgroup (thread e owns expert e, E <= blockDim.x). Selection order is c
 // descending, expert index ascending among equal c; an expert's position is
@@ -126,11 +139,14 @@ __device__ __forceinline__ unsigned long long order_key(double c) {
 // (when there are >= K groups those maxima are >= K distinct experts), so
 // positions are counted among those few candidates only.
 __device__ __forceinline__ void topk_wg(const double* logits, const float* bias, int T, int E, int K,
-                                        int norm, double rho, Route& R, TopkScratch& Z) {
+                                        int norm, double rho, GroupSel gsel, Route& R,
+                                        TopkScratch& Z) {
     const int e = threadIdx.x;
-    const int G = (E + 31) >> 5;
-    const bool filt = G >= K;
+    const int G = (E + 31) >> 5, G8 = (E + 7) >> 3;
+    const bool grouped = gsel.ng > 1;
+    const bool filt = G >= K || (grouped && G8 >= K);
     if (threadIdx.x < kMaxTok * 8) (&Z.gmax[0][0])[threadIdx.x] = 0ull;
+    if (threadIdx.x < kMaxTok * 32) (&Z.gmax8[0][0])[threadIdx.x] = 0ull;
     if (threadIdx.x < kMaxTok) Z.ncand[threadIdx.x] = 0;
     double l[kMaxTok];
     float bb = 0.0f;
@@ -146,20 +162,110 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
         key[t] = 0ull;
         if (t < T) {  // uniform: no fp64 exp for absent tokens
             s[t] = 1.0 / (1.0 + exp(-l[t]));
-            key[t] = order_key(s[t] + (double)bb);
-            if (filt && e < E) atomicMax(&Z.gmax[t][e >> 5], key[t]);
+            key[t] = e < E ? order_key(s[t] + (double)bb) : 0ull;
+        }
+    }
+    // group-limited selection: the experts of dropped groups get key 0 (below
+    // every real key). With groups of 2..64 experts (a power of two: a group
+    // never straddles a wave) the group maxima come from lane shuffles, and the
+    // smallest second-largest c of the kept groups (2 tg >= K experts at or
+    // above it) bounds the K-th largest from below; otherwise the scores go
+    // through LDS and the expert-group maxima below give the bound.
+    const bool gshfl = grouped && gsel.gs >= 2 && gsel.gs <= 64 && !(gsel.gs & (gsel.gs - 1));
+    if (grouped) {
+        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+        if (gshfl) {
+#pragma unroll
+            for (int t = 0; t < kMaxTok; ++t) {
+                if (t < T) {  // uniform
+                    double a = e < E ? s[t] + (double)bb : -__builtin_inf(), b2 = -__builtin_inf();
+                    top2_lanes(a, b2, gsel.gs);
+                    if (e < E && (e & (gsel.gs - 1)) == 0) {
+                        Z.cs[t][e / gsel.gs] = a + b2;  // group score (cs is free until later)
+                        Z.cs[t][64 + e / gsel.gs] = b2;
+                    }
+                }
+            }
+            __syncthreads();
+            if (wv < T) {
+                const bool in = lane < gsel.ng;
+                const double sc = in ? Z.cs[wv][lane] : -__builtin_inf();
+                const double bq = in ? Z.cs[wv][64 + lane] : 0.0;
+                int rank = 0;
+                for (int j = 0; j < gsel.ng; ++j) {
+                    const double o = __shfl(sc, j, 64);
+                    rank += (o > sc || (o == sc && j < lane)) ? 1 : 0;
+                }
+                const bool kept = in && rank < gsel.tg;
+                const unsigned long long keep = __ballot(kept);
+                double tb = kept ? bq : __builtin_inf();
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) tb = fmin(tb, __shfl_xor(tb, o, 64));
+                if (lane == 0) {
+                    Z.keep[wv] = keep;
+                    Z.gthr[wv] = 2 * gsel.tg >= K ? order_key(tb) : 0ull;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < kMaxTok; ++t)
+                if (t < T && e < E) Z.cs[t][e] = s[t] + (double)bb;
+            __syncthreads();
+            if (wv < T) {
+                const unsigned long long keep = group_keep_mask(Z.cs[wv], gsel);
+                if (lane == 0) {
+                    Z.keep[wv] = keep;
+                    Z.gthr[wv] = 0ull;
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < kMaxTok; ++t)
+            if (t < T && e < E && !((Z.keep[t] >> (e / gsel.gs)) & 1ull)) key[t] = 0ull;
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxTok; ++t) {
+        if (t < T && filt && !gshfl && key[t]) {
+            atomicMax(&Z.gmax[t][e >> 5], key[t]);
+            if (grouped) atomicMax(&Z.gmax8[t][e >> 3], key[t]);
         }
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kMaxTok; ++t) {
         if (t < T && e < E) {
+            // the smallest maximum of >= K non-empty expert groups bounds the
+            // K-th largest key from below (32-expert groups, else 8-expert)
             unsigned long long thr = 0ull;
-            if (filt) {
-                thr = ~0ull;
-                for (int g = 0; g < G; ++g) thr = min(thr, Z.gmax[t][g]);
+            if (gshfl) {
+                thr = Z.gthr[t];
+            } else if (filt) {
+                unsigned long long mn = ~0ull;
+                int cnt = 0;
+                for (int g = 0; g < G; ++g) {
+                    const unsigned long long v = Z.gmax[t][g];
+                    if (v) {
+                        mn = min(mn, v);
+                        ++cnt;
+                    }
+                }
+                if (cnt >= K) {
+                    thr = mn;
+                } else if (grouped) {
+                    mn = ~0ull;
+                    cnt = 0;
+                    for (int g = 0; g < G8; ++g) {
+                        const unsigned long long v = Z.gmax8[t][g];
+                        if (v) {
+                            mn = min(mn, v);
+                            ++cnt;
+                        }
+                    }
+                    if (cnt >= K) thr = mn;
+                }
             }
-            if (key[t] >= thr) {
+            if (key[t] && key[t] >= thr) {
                 const int p = atomicAdd(&Z.ncand[t], 1);
                 Z.ckey[t][p] = key[t];
                 Z.ce[t][p] = e;
@@ -215,8 +321,8 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
 // Fills R (in LDS) for T tokens; must be called by the whole workgroup
 // (blockDim.x >= E).
 __device__ __forceinline__ void route_small(const double* logits, const float* bias, int T, int E, int K, int S,
-                            int norm, double rho, Route& R, TopkScratch& Z) {
-    topk_wg(logits, bias, T, E, K, norm, rho, R, Z);
+                            int norm, double rho, GroupSel gsel, Route& R, TopkScratch& Z) {
+    topk_wg(logits, bias, T, E, K, norm, rho, gsel, R, Z);
     __syncthreads();
     // entries j = t K + k in (token, k) order; entry j belongs to an earlier
     // token than entry i exactly when j < t_i K
@@ -289,11 +395,12 @@ __device__ __forceinline__ void route_small(const double* logits, const float* b
 // (c descending, index ascending). All LDS traffic stays within the wave,
 // whose LDS operations complete in program order.
 __device__ __forceinline__ void route_one(const double* logits, const float* bias, int E, int K,
-                                          int S, int norm, double rho, Route& R, TopkScratch& Z) {
+                                          int S, int norm, double rho, GroupSel gsel, Route& R,
+                                          TopkScratch& Z) {
     const int lane = threadIdx.x & 63;
     if (threadIdx.x < 64) {
         unsigned long long key[4];
-        double sv[4];
+        double sv[4], cv[4];
         bool ok[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -303,18 +410,86 @@ __device__ __forceinline__ void route_one(const double* logits, const float* bia
             const float b = ok[j] ? bias[e] : 0.0f;
             sv[j] = 1.0 / (1.0 + exp(-l));
             key[j] = ok[j] ? order_key(sv[j] + (double)b) : 0ull;
+            cv[j] = ok[j] ? sv[j] + (double)b : -__builtin_inf();
         }
-        const int G = (E + 31) >> 5;
-        unsigned long long thr = 0ull;
-        if (G >= K) {
-            // group maximum over the 8 lanes of a group, then minimum over groups
-            unsigned long long gm = max(max(key[0], key[1]), max(key[2], key[3]));
+        // group-limited selection: the experts of dropped groups leave the race.
+        // Groups of 4 lpg experts (lpg a power of two: whole lanes) take their
+        // two largest c from lane shuffles, and the smallest second-largest c
+        // of the kept groups (2 tg >= K experts at or above it) bounds the K-th
+        // largest from below; other group sizes go through LDS.
+        unsigned long long gthr = 0ull;
+        if (gsel.ng > 1) {
+            const int lpg = gsel.gs >> 2;
+            if ((gsel.gs & 3) == 0 && !(lpg & (lpg - 1))) {
+                double a = fmax(cv[0], cv[1]), b2 = fmin(cv[0], cv[1]);
+#pragma unroll
+                for (int j = 2; j < 4; ++j) {
+                    b2 = fmax(b2, fmin(a, cv[j]));
+                    a = fmax(a, cv[j]);
+                }
+                top2_lanes(a, b2, lpg);
+                const int g = lane / lpg;
+                const bool head = (lane & (lpg - 1)) == 0 && g < gsel.ng;
+                const double sc = head ? a + b2 : -__builtin_inf();
+                int rank = 0;
+                for (int j = 0; j < gsel.ng; ++j) {
+                    const double o = __shfl(sc, j * lpg, 64);
+                    rank += (o > sc || (o == sc && j < g)) ? 1 : 0;
+                }
+                const bool kept = head && rank < gsel.tg;
+                const unsigned long long keepl = __ballot(kept);
+                double tb = kept ? b2 : __builtin_inf();
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) tb = fmin(tb, __shfl_xor(tb, o, 64));
+                if (2 * gsel.tg >= K) gthr = order_key(tb);
+                if (!((keepl >> (lane & ~(lpg - 1))) & 1ull)) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        ok[j] = false;
+                        key[j] = 0ull;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (ok[j]) Z.cs[1][4 * lane + j] = cv[j];  // row 1 is free here
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const unsigned long long keep = group_keep_mask(Z.cs[1], gsel);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (ok[j] && !((keep >> ((4 * lane + j) / gsel.gs)) & 1ull)) {
+                        ok[j] = false;
+                        key[j] = 0ull;
+                    }
+            }
+        }
+        // the smallest maximum of >= K non-empty expert groups bounds the K-th
+        // largest key from below: 32-expert groups (8 lanes), else with groups
+        // 8-expert groups (2 lanes)
+        const int G = (E + 31) >> 5, G8 = (E + 7) >> 3;
+        unsigned long long thr = gthr;
+        const unsigned long long m4 = max(max(key[0], key[1]), max(key[2], key[3]));
+        if (thr == 0ull && G >= K) {
+            unsigned long long gm = m4;
 #pragma unroll
             for (int o = 1; o < 8; o <<= 1) gm = max(gm, (unsigned long long)__shfl_xor(gm, o, 64));
-            if ((lane >> 3) >= G) gm = ~0ull;  // no experts in this group
+            const bool live = (lane >> 3) < G && gm != 0ull;
+            const int cnt = __popcll(__ballot(live && (lane & 7) == 0));
+            if (!live) gm = ~0ull;  // no (eligible) experts in this group
 #pragma unroll
             for (int o = 8; o < 64; o <<= 1) gm = min(gm, (unsigned long long)__shfl_xor(gm, o, 64));
-            thr = gm;
+            if (cnt >= K) thr = gm;
+        }
+        if (thr == 0ull && gsel.ng > 1 && G8 >= K) {
+            unsigned long long gm = max(m4, (unsigned long long)__shfl_xor(m4, 1, 64));
+            const bool live = (lane >> 1) < G8 && gm != 0ull;
+            const int cnt = __popcll(__ballot(live && (lane & 1) == 0));
+            if (!live) gm = ~0ull;
+#pragma unroll
+            for (int o = 2; o < 64; o <<= 1) gm = min(gm, (unsigned long long)__shfl_xor(gm, o, 64));
+            if (cnt >= K) thr = gm;
         }
         int base = 0;
 #pragma unroll
@@ -401,6 +576,7 @@ struct DecArgs {
     int64_t blob_q, blob_s;
     int T, H, I, E, K, S, norm;
     double rho;
+    GroupSel gsel;  // group-limited selection (ng <= 1: none)
     // workspace
     double* logits;
     int8_t* qx;
@@ -786,9 +962,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
         b -= nw;
     }
     if (NT == 1)
-        route_one(a.logits, a.bias, a.E, a.K, a.S, a.norm, a.rho, R, U.z);
+        route_one(a.logits, a.bias, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
     else
-        route_small(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, R, U.z);
+        route_small(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
     if (b == 0) publish_route(a, R);
     const int u = b / nw, hw = b - u * nw;
     if (u >= R.n_uniq) return;

@@ -128,8 +128,10 @@ __global__ __launch_bounds__(256) void k_router_reduce(const double* __restrict_
 template <int EPL>
 __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
                                               const float* __restrict__ bias, int T, int E, int K,
-                                              int norm, double rho, int32_t* __restrict__ idx,
+                                              int norm, double rho, GroupSel gsel,
+                                              int32_t* __restrict__ idx,
                                               float* __restrict__ wout) {
+    extern __shared__ double c_stage[];  // [4][E] when gsel.ng > 1
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wave leaves together
@@ -144,6 +146,22 @@ __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
         } else {
             s[j] = 0.0;
             c[j] = -__builtin_inf();
+        }
+    }
+    if (gsel.ng > 1) {
+        // group-limited selection: the experts of dropped groups leave the race
+        double* cw = c_stage + (threadIdx.x >> 6) * E;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+            if (lane + 64 * j < E) cw[lane + 64 * j] = c[j];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const unsigned long long keep = group_keep_mask(cw, gsel);
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+            const int e = lane + 64 * j;
+            if (e < E && !((keep >> (e / gsel.gs)) & 1ull)) c[j] = -__builtin_inf();
         }
     }
     uint32_t taken = 0;

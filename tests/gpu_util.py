@@ -16,9 +16,9 @@ def unperm8(q: np.ndarray) -> np.ndarray:
     return out.reshape(q.shape)
 
 
-def lib_cfg(C, cfg):
+def lib_cfg(C, cfg, n_group=1, topk_group=1):
     return C.make_cfg(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
-                      cfg.norm_topk, cfg.rho)
+                      cfg.norm_topk, cfg.rho, n_group, topk_group)
 
 
 def gpu_layer(C, cfg, layer=0):
@@ -36,19 +36,20 @@ def layer_input(ref, cfg, layer=0, n_tok=None, first_tok=0):
     return np.ascontiguousarray(x, np.float32)
 
 
-def oracle_layer_for(ref, cfg, layer, x, forced_idx=None, draw_device="cuda"):
+def oracle_layer_for(ref, cfg, layer, x, forced_idx=None, draw_device="cuda", n_group=1,
+                     topk_group=1):
     """OracleLayer holding only the experts that tokens x select (plus shared),
     each drawn as fp32 by coli_synth (on draw_device, bit-identical to the CPU
     draw) and packed by the oracle."""
     wr, b = cs.router(cfg, layer, "cpu")
     wr, b = wr.numpy(), b.numpy()
     if forced_idx is None:
-        idx, _, _ = ref.route(x, wr, b, cfg.top_k, cfg.norm_topk, cfg.rho)
+        idx, _, _ = ref.route(x, wr, b, cfg.top_k, cfg.norm_topk, cfg.rho, n_group, topk_group)
     else:
         idx = forced_idx
     need = sorted(set(int(e) for e in np.unique(idx)) | ({cfg.n_experts} if cfg.n_shared else set()))
     L = ref.OracleLayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
-                        cfg.norm_topk, cfg.rho, wr, b, {})
+                        cfg.norm_topk, cfg.rho, wr, b, {}, n_group, topk_group)
     for e in need:
         mats = [cs.expert_matrix(cfg, layer, e, w, draw_device).cpu().numpy()
                 for w in ("gate", "up", "down")]
