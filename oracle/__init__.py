@@ -37,6 +37,9 @@ def lib():
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         L.coli_ref_pack_int4.argtypes = [vp, i64, i64, vp, vp]
         L.coli_ref_unpack_int4.argtypes = [vp, i64, i64, vp]
+        L.coli_ref_pack.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
+        L.coli_ref_unpack.argtypes = [vp, i64, i64, ctypes.c_int, vp]
+        L.coli_ref_block_dots_bits.argtypes = [vp, i64, i64, ctypes.c_int, vp, i64, vp]
         L.coli_ref_e4m3_to_f32.argtypes = [ctypes.c_uint8]
         L.coli_ref_e4m3_to_f32.restype = ctypes.c_float
         L.coli_ref_fp8_to_f32.argtypes = [vp, vp, i64, i64, vp]
@@ -81,6 +84,24 @@ def pack_int4(w) -> tuple[np.ndarray, np.ndarray]:
     s = np.empty(rows, np.float32)
     _check(lib().coli_ref_pack_int4(_p(w), rows, cols, _p(q), _p(s)), "pack_int4")
     return q, s
+
+
+def pack_weights(w, bits: int) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric b-bit pack (b in 2, 4, 8): codes [rows, cols b/8] u8, scale [rows]."""
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    q = np.empty((rows, cols * bits // 8), np.uint8)
+    s = np.empty(rows, np.float32)
+    _check(lib().coli_ref_pack(_p(w), rows, cols, int(bits), _p(q), _p(s)), "pack")
+    return q, s
+
+
+def unpack(q, cols: int, bits: int) -> np.ndarray:
+    q = _c(q, np.uint8)
+    rows = q.shape[0]
+    out = np.empty((rows, cols), np.int8)
+    _check(lib().coli_ref_unpack(_p(q), rows, cols, int(bits), _p(out)), "unpack")
+    return out
 
 
 def e4m3_to_f32(b: int) -> float:
@@ -134,15 +155,15 @@ def quant_q8(x) -> tuple[np.ndarray, np.ndarray]:
     return q, d
 
 
-def block_dots(wq, cols: int, qx) -> np.ndarray:
+def block_dots(wq, cols: int, qx, bits: int = 4) -> np.ndarray:
     wq = _c(wq, np.uint8)
     qx = _c(qx, np.int8)
     if qx.ndim == 1:
         qx = qx[None]
     rows = wq.shape[0]
     out = np.empty((qx.shape[0], rows, cols // 32), np.int32)
-    _check(lib().coli_ref_block_dots(_p(wq), rows, cols, _p(qx), qx.shape[0], _p(out)),
-           "block_dots")
+    _check(lib().coli_ref_block_dots_bits(_p(wq), rows, cols, int(bits), _p(qx), qx.shape[0],
+                                          _p(out)), "block_dots")
     return out
 
 
@@ -181,7 +202,8 @@ class _Layer(ctypes.Structure):
                 ("gate_q", ctypes.c_void_p), ("up_q", ctypes.c_void_p),
                 ("down_q", ctypes.c_void_p), ("gate_s", ctypes.c_void_p),
                 ("up_s", ctypes.c_void_p), ("down_s", ctypes.c_void_p),
-                ("n_group", ctypes.c_int64), ("topk_group", ctypes.c_int64)]
+                ("n_group", ctypes.c_int64), ("topk_group", ctypes.c_int64),
+                ("weight_bits", ctypes.c_int64)]
 
 
 class _Taps(ctypes.Structure):
@@ -198,9 +220,11 @@ class OracleLayer:
     """
 
     def __init__(self, hidden, inter, n_experts, top_k, n_shared, norm_topk, rho,
-                 w_router, bias, experts: dict, n_group: int = 1, topk_group: int = 1):
+                 w_router, bias, experts: dict, n_group: int = 1, topk_group: int = 1,
+                 weight_bits: int = 4):
         self.hidden, self.inter = int(hidden), int(inter)
         self.n_group, self.topk_group = int(n_group), int(topk_group)
+        self.weight_bits = int(weight_bits)
         self.n_experts, self.top_k, self.n_shared = int(n_experts), int(top_k), int(n_shared)
         self.norm_topk, self.rho = bool(norm_topk), float(np.float32(rho))
         self.w_router = None if w_router is None else _c(w_router, np.float32)
@@ -232,7 +256,7 @@ class OracleLayer:
                    ctypes.cast(arrs["gate_s"], ctypes.c_void_p),
                    ctypes.cast(arrs["up_s"], ctypes.c_void_p),
                    ctypes.cast(arrs["down_s"], ctypes.c_void_p),
-                   self.n_group, self.topk_group)
+                   self.n_group, self.topk_group, self.weight_bits)
         return s, arrs
 
     def forward(self, x, forced_idx=None, forced_w=None, y_in=None, taps: bool = False):
@@ -263,9 +287,9 @@ class OracleLayer:
         return (y, t) if taps else y
 
 
-def pack_expert(gate: np.ndarray, up: np.ndarray, down: np.ndarray) -> dict:
+def pack_expert(gate: np.ndarray, up: np.ndarray, down: np.ndarray, bits: int = 4) -> dict:
     """Oracle-packed expert from fp32 matrices gate/up [I,H], down [H,I]."""
-    gq, gs = pack_int4(gate)
-    uq, us = pack_int4(up)
-    dq, ds = pack_int4(down)
+    gq, gs = pack_weights(gate, bits)
+    uq, us = pack_weights(up, bits)
+    dq, ds = pack_weights(down, bits)
     return {"gate_q": gq, "gate_s": gs, "up_q": uq, "up_s": us, "down_q": dq, "down_s": ds}

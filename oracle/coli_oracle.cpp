@@ -15,7 +15,8 @@
 //      norm_topk_prob); section "量化保留模块" (some modules stay F32).
 //  [C] "Colibri：在笔记本上跑744B参数的AI模型", feature list (关键特性):
 //      DeepSeek-V3-style sigmoid router plus shared expert; integer dot
-//      kernel over Q8_0-style int8 activations.
+//      kernel over Q8_0-style int8 activations; quantisation kernels for
+//      int8, int4 and int2 weights.
 //  [E] hn mirror of the project summary, feature list: batched MoE — an
 //      expert used by several positions of a batch is read once.
 // Where the pages are silent the reading taken is stated at the function.
@@ -44,25 +45,37 @@ extern "C" {
 enum { REF_OK = 0, REF_EINVAL = -1 };
 
 // ---------------------------------------------------------------------------
-// int4 weight quantisation  ([A] section 量化流程)
-//   s_r  = fp32( max_j |W_rj| / 7 )                 (IEEE single division)
-//   q_rj = clamp( rint(W_rj / s_r), -7, 7 )        (round half to even, the
+// Symmetric b-bit weight quantisation, b = 4 ([A] section 量化流程), and the
+// sibling int8 and int2 formats the engine's kernels also handle ([C] feature
+// list, 关键特性: quantisation kernels for int8, int4 and int2):
+//   Q    = 2^(b-1) - 1                          (7 for int4, 127 int8, 1 int2)
+//   s_r  = fp32( max_j |W_rj| / Q )             (IEEE single division)
+//   q_rj = clamp( rint(W_rj / s_r), -Q, Q )     (round half to even, the
 //          behaviour of both np.rint and lrintf in the default rounding mode)
 //   s_r == 0  ->  q_rj = 0
-//   byte j of row r = (q_{r,2j} & 0xF) | (q_{r,2j+1} & 0xF) << 4
-// Readings: divide (not multiply by 1/s); symmetric range +-7 (scale
-// max|row|/7); a "row" is an output channel; low nibble holds the even
-// element; nibbles are 4-bit two's complement.
+//   codes are b-bit two's complement, packed little end first: element j of
+//   a row sits in byte (j b) / 8 at bit (j b) % 8 (int4: the even element in
+//   the low nibble; int2: element 4i + k at bits 2k of byte i).
+// Readings: divide (not multiply by 1/s); symmetric range +-Q (int4's
+// max|row|/7 carried over to the other widths, so int2 is ternary); a "row"
+// is an output channel.
 // ---------------------------------------------------------------------------
-static int ref_int4_code(float w, float s) {
+static bool ref_bits_ok(int bits) { return bits == 2 || bits == 4 || bits == 8; }
+
+static int ref_code(float w, float s, int qmax) {
     float r = rintf(w / s);
-    if (r > 7.0f) r = 7.0f;
-    if (r < -7.0f) r = -7.0f;
+    if (r > (float)qmax) r = (float)qmax;
+    if (r < -(float)qmax) r = -(float)qmax;
     return (int)r;
 }
 
-int coli_ref_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* scale) {
-    if (!w || !q || !scale || rows < 0 || cols <= 0 || (cols % 2) != 0) return REF_EINVAL;
+int coli_ref_pack(const float* w, int64_t rows, int64_t cols, int bits, uint8_t* q,
+                  float* scale) {
+    if (!w || !q || !scale || rows < 0 || cols <= 0 || !ref_bits_ok(bits) ||
+        (cols * bits) % 8 != 0)
+        return REF_EINVAL;
+    const int qmax = (1 << (bits - 1)) - 1;
+    const int64_t row_bytes = cols * bits / 8;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         const float* row = w + r * cols;
@@ -71,19 +84,21 @@ int coli_ref_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q, f
             float a = std::fabs(row[j]);
             if (a > amax) amax = a;
         }
-        float s = amax / 7.0f;
+        float s = amax / (float)qmax;
         scale[r] = s;
-        uint8_t* out = q + r * (cols / 2);
-        for (int64_t j = 0; j < cols; j += 2) {
-            int lo = 0, hi = 0;
-            if (s != 0.0f) {
-                lo = ref_int4_code(row[j], s);
-                hi = ref_int4_code(row[j + 1], s);
-            }
-            out[j / 2] = (uint8_t)((lo & 0xF) | ((hi & 0xF) << 4));
+        uint8_t* out = q + r * row_bytes;
+        std::memset(out, 0, (size_t)row_bytes);
+        for (int64_t j = 0; j < cols; ++j) {
+            const int c = (s != 0.0f) ? ref_code(row[j], s, qmax) : 0;
+            const int64_t bit = j * bits;
+            out[bit / 8] |= (uint8_t)((c & ((1 << bits) - 1)) << (bit % 8));
         }
     }
     return REF_OK;
+}
+
+int coli_ref_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* scale) {
+    return coli_ref_pack(w, rows, cols, 4, q, scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -125,18 +140,25 @@ int coli_ref_pack_fp8_int4(const uint8_t* q8, const float* bs, int64_t rows, int
     return coli_ref_pack_int4(w.data(), rows, cols, q, scale);
 }
 
-// Signed value of a 4-bit two's complement nibble (0x8 decodes to -8).
-static int ref_nibble_value(int v) { return v >= 8 ? v - 16 : v; }
+// Signed value of element j of a packed b-bit row (b-bit two's complement:
+// the most negative code, e.g. 0x8 for int4, decodes to -2^(b-1)).
+static int ref_code_at(const uint8_t* row, int64_t j, int bits) {
+    const int64_t bit = j * bits;
+    const int v = (row[bit / 8] >> (bit % 8)) & ((1 << bits) - 1);
+    return v >= (1 << (bits - 1)) ? v - (1 << bits) : v;
+}
+
+int coli_ref_unpack(const uint8_t* q, int64_t rows, int64_t cols, int bits, int8_t* codes) {
+    if (!q || !codes || rows < 0 || cols <= 0 || !ref_bits_ok(bits) || (cols * bits) % 8 != 0)
+        return REF_EINVAL;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t j = 0; j < cols; ++j)
+            codes[r * cols + j] = (int8_t)ref_code_at(q + r * (cols * bits / 8), j, bits);
+    return REF_OK;
+}
 
 int coli_ref_unpack_int4(const uint8_t* q, int64_t rows, int64_t cols, int8_t* codes) {
-    if (!q || !codes || rows < 0 || cols <= 0 || (cols % 2) != 0) return REF_EINVAL;
-    for (int64_t r = 0; r < rows; ++r)
-        for (int64_t j = 0; j < cols; j += 2) {
-            uint8_t b = q[r * (cols / 2) + j / 2];
-            codes[r * cols + j] = (int8_t)ref_nibble_value(b & 0xF);
-            codes[r * cols + j + 1] = (int8_t)ref_nibble_value(b >> 4);
-        }
-    return REF_OK;
+    return coli_ref_unpack(q, rows, cols, 4, codes);
 }
 
 // ---------------------------------------------------------------------------
@@ -178,38 +200,42 @@ int coli_ref_quant_q8(const float* x, int64_t n_tok, int64_t dim, int8_t* q, flo
 // ---------------------------------------------------------------------------
 // Exact int32 dot of one 32-wide block: sum_i code(w_i) * q_i.
 // ---------------------------------------------------------------------------
-static int32_t ref_block_dot(const uint8_t* wrow, int64_t b, const int8_t* q) {
+static int32_t ref_block_dot(const uint8_t* wrow, int64_t b, const int8_t* q, int bits) {
     int32_t acc = 0;
     for (int i = 0; i < 32; ++i) {
         int64_t j = b * 32 + i;
-        uint8_t byte = wrow[j / 2];
-        int code = ref_nibble_value((j % 2 == 0) ? (byte & 0xF) : (byte >> 4));
-        acc += code * (int32_t)q[j];
+        acc += ref_code_at(wrow, j, bits) * (int32_t)q[j];
     }
     return acc;
 }
 
 // dots[t, r, b] for every token t, weight row r and block b (debug reference).
-int coli_ref_block_dots(const uint8_t* wq, int64_t rows, int64_t cols, const int8_t* qx,
-                        int64_t n_tok, int32_t* dots) {
-    if (!wq || !qx || !dots || rows < 0 || cols <= 0 || (cols % 32) != 0 || n_tok < 0)
+int coli_ref_block_dots_bits(const uint8_t* wq, int64_t rows, int64_t cols, int bits,
+                             const int8_t* qx, int64_t n_tok, int32_t* dots) {
+    if (!wq || !qx || !dots || rows < 0 || cols <= 0 || (cols % 32) != 0 || n_tok < 0 ||
+        !ref_bits_ok(bits))
         return REF_EINVAL;
     const int64_t nb = cols / 32;
     for (int64_t t = 0; t < n_tok; ++t)
         for (int64_t r = 0; r < rows; ++r)
             for (int64_t b = 0; b < nb; ++b)
                 dots[(t * rows + r) * nb + b] =
-                    ref_block_dot(wq + r * (cols / 2), b, qx + t * cols);
+                    ref_block_dot(wq + r * (cols * bits / 8), b, qx + t * cols, bits);
     return REF_OK;
 }
 
-// Row r of an int4 matrix times a Q8_0 vector, in double:
+int coli_ref_block_dots(const uint8_t* wq, int64_t rows, int64_t cols, const int8_t* qx,
+                        int64_t n_tok, int32_t* dots) {
+    return coli_ref_block_dots_bits(wq, rows, cols, 4, qx, n_tok, dots);
+}
+
+// Row r of a packed weight matrix times a Q8_0 vector, in double:
 //   D_r = sum_b d_b * I_b            (each product exact in double)
 // followed by the row scale, rounded once to fp32:  fp32( s_r * D_r ).
 static float ref_row_dot(const uint8_t* wrow, float s_r, const int8_t* q, const float* d,
-                         int64_t nb) {
+                         int64_t nb, int bits) {
     double acc = 0.0;
-    for (int64_t b = 0; b < nb; ++b) acc += (double)d[b] * (double)ref_block_dot(wrow, b, q);
+    for (int64_t b = 0; b < nb; ++b) acc += (double)d[b] * (double)ref_block_dot(wrow, b, q, bits);
     return (float)((double)s_r * acc);
 }
 
@@ -335,13 +361,14 @@ typedef struct coli_ref_layer {
     double rho;
     const float* w_router;        // [E, H]
     const float* bias;            // [E]
-    const uint8_t* const* gate_q; // per expert (E + n_shared; shared last): [I, H/2] or NULL
-    const uint8_t* const* up_q;   // [I, H/2]
-    const uint8_t* const* down_q; // [H, I/2]
+    const uint8_t* const* gate_q; // per expert (E + n_shared; shared last): [I, H b/8] or NULL
+    const uint8_t* const* up_q;   // [I, H b/8]
+    const uint8_t* const* down_q; // [H, I b/8]
     const float* const* gate_s;   // [I]
     const float* const* up_s;     // [I]
     const float* const* down_s;   // [H]
     int64_t n_group, topk_group;  // group-limited selection (1, 1: none)
+    int64_t weight_bits;          // 2, 4 or 8 (0 reads as 4)
 } coli_ref_layer;
 
 // Optional intermediate outputs, indexed by token t and slot k (k < K: the
@@ -370,6 +397,7 @@ typedef struct coli_ref_taps {
 static void ref_expert(const coli_ref_layer* L, int64_t e, const int8_t* qx, const float* dx,
                        float* g, float* u, float* h, int8_t* qh, float* dh, float* ye) {
     const int64_t H = L->hidden, I = L->inter;
+    const int bits = L->weight_bits ? (int)L->weight_bits : 4;
     const uint8_t* gq = L->gate_q[e];
     const uint8_t* uq = L->up_q[e];
     const uint8_t* dq = L->down_q[e];
@@ -378,8 +406,8 @@ static void ref_expert(const coli_ref_layer* L, int64_t e, const int8_t* qx, con
     const float* ds = L->down_s[e];
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < I; ++r) {
-        float gr = ref_row_dot(gq + r * (H / 2), gs[r], qx, dx, H / 32);
-        float ur = ref_row_dot(uq + r * (H / 2), us[r], qx, dx, H / 32);
+        float gr = ref_row_dot(gq + r * (H * bits / 8), gs[r], qx, dx, H / 32, bits);
+        float ur = ref_row_dot(uq + r * (H * bits / 8), us[r], qx, dx, H / 32, bits);
         double zg = (double)gr;
         double silu = zg / (1.0 + std::exp(-zg));
         g[r] = gr;
@@ -388,7 +416,8 @@ static void ref_expert(const coli_ref_layer* L, int64_t e, const int8_t* qx, con
     }
     for (int64_t b = 0; b < I / 32; ++b) ref_q8_block(h + b * 32, qh + b * 32, dh + b);
 #pragma omp parallel for schedule(static)
-    for (int64_t c = 0; c < H; ++c) ye[c] = ref_row_dot(dq + c * (I / 2), ds[c], qh, dh, I / 32);
+    for (int64_t c = 0; c < H; ++c)
+        ye[c] = ref_row_dot(dq + c * (I * bits / 8), ds[c], qh, dh, I / 32, bits);
 }
 
 // y[t] = fp32( sum_k w[t,k] * y_{e_k}[t] + y_shared[t] )   (double, k ascending, shared last)
@@ -403,7 +432,8 @@ int coli_ref_moe_forward(const coli_ref_layer* L, const float* x, int64_t n_tok,
     const int64_t H = L->hidden, I = L->inter, E = L->n_experts, K = L->top_k,
                   S = L->n_shared;
     if (H <= 0 || I <= 0 || (H % 32) || (I % 32) || E <= 0 || K <= 0 || K > E || S < 0 ||
-        S > 1 || !ref_groups_ok(E, K, L->n_group, L->topk_group))
+        S > 1 || !ref_groups_ok(E, K, L->n_group, L->topk_group) ||
+        (L->weight_bits != 0 && !ref_bits_ok((int)L->weight_bits)))
         return REF_EINVAL;
     if ((forced_idx == nullptr) != (forced_w == nullptr)) return REF_EINVAL;
     const int64_t KS = K + S;

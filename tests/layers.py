@@ -19,16 +19,17 @@ def layer_inputs(cfg, layer=0, n_tok=None, first_tok=0):
     return x, wr.numpy(), b.numpy()
 
 
-def oracle_layer(ref, cfg, layer=0, experts=None, wr=None, b=None):
-    """OracleLayer with the given experts packed by the oracle (all when None)."""
+def oracle_layer(ref, cfg, layer=0, experts=None, wr=None, b=None, bits=4):
+    """OracleLayer with the given experts packed by the oracle (all when None)
+    with bits-wide weight codes."""
     if wr is None:
         wr_t, b_t = cs.router(cfg, layer, "cpu")
         wr, b = wr_t.numpy(), b_t.numpy()
     L = ref.OracleLayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
-                        cfg.norm_topk, cfg.rho, wr, b, {})
+                        cfg.norm_topk, cfg.rho, wr, b, {}, weight_bits=bits)
     ids = range(cfg.n_experts + cfg.n_shared) if experts is None else experts
     for e in ids:
-        L.add_expert(e, ref.pack_expert(*expert_fp32(cfg, layer, e)))
+        L.add_expert(e, ref.pack_expert(*expert_fp32(cfg, layer, e), bits=bits))
     return L
 
 

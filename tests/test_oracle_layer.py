@@ -14,14 +14,14 @@ def _sig(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
-def dense_expert(ref, ex, qx, dx):
+def dense_expert(ref, ex, qx, dx, bits=4):
     """One expert on one Q8_0 token as dense float64 matmuls of dequantised operands."""
     H = qx.shape[0]
     I = ex["gate_s"].shape[0]
     xd = qx.astype(np.float64) * np.repeat(dx.astype(np.float64), 32)
-    cg = ref.unpack_int4(ex["gate_q"], H).astype(np.float64)
-    cu = ref.unpack_int4(ex["up_q"], H).astype(np.float64)
-    cd = ref.unpack_int4(ex["down_q"], I).astype(np.float64)
+    cg = ref.unpack(ex["gate_q"], H, bits).astype(np.float64)
+    cu = ref.unpack(ex["up_q"], H, bits).astype(np.float64)
+    cd = ref.unpack(ex["down_q"], I, bits).astype(np.float64)
     g = (ex["gate_s"].astype(np.float64) * (cg @ xd)).astype(np.float32)
     u = (ex["up_s"].astype(np.float64) * (cu @ xd)).astype(np.float32)
     g64 = g.astype(np.float64)
