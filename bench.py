@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--sweep", type=str, default="",
                     help="comma-separated token counts: time the layer of --config at each "
                          "(one JSON line per count) instead of the default run")
+    ap.add_argument("--bits", type=int, default=4, choices=(2, 4, 8),
+                    help="width of the expert weight codes (int8 and int2 run on the grouped "
+                         "MFMA kernels at every token count)")
     ap.add_argument("--groups", type=str, default="",
                     help="NG,TG: group-limited expert selection (NG groups, the TG best kept)")
     ap.add_argument("--op", choices=("layer", "pack_fp8"), default="layer",
@@ -106,16 +109,17 @@ def main():
         return
     T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
     ng, tg = (int(v) for v in args.groups.split(",")) if args.groups else (1, 1)
-    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, ng, tg)
+    bits = args.bits
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, ng, tg, bits)
     R = max(1, args.replicas)
     n_steps, n_warm = args.steps, args.warmup
     n_inputs = n_steps + n_warm
 
     t_setup = time.time()
-    pack = lambda w, qv, sv: C.coli_pack_int4(w, qv, sv)
+    pack = lambda w, qv, sv: C.coli_pack_weights(w, bits, qv, sv)
     layers = []
     for r in range(R):
-        wr, b, q, s = cs.build_layer(cfg, r, "cuda", pack)
+        wr, b, q, s = cs.build_layer(cfg, r, "cuda", pack, bits=bits)
         layers.append(C.LayerWeights(lc, wr, b, q, s))
         print(f"[bench] replica {r} packed ({(q.numel() + 4 * s.numel()) / 1e9:.2f} GB)",
               file=sys.stderr, flush=True)
@@ -151,7 +155,7 @@ def main():
     # bytes that must cross HBM per step: unique experts' packed weights + scales,
     # the router weight, activations in and out
     lay = C.coli_moe_workspace_layout(lc, T, 0)
-    eb = 3 * I * H // 2 + 4 * (2 * I + H)
+    eb = 3 * I * H * bits // 8 + 4 * (2 * I + H)
 
     # ---- per-kernel durations with HIP events on the same stream -------------
     kern = {}
@@ -179,12 +183,12 @@ def main():
     # algorithmic HBM bytes of the gate/up launch: the packed gate and up rows and
     # their scales of every expert in use, Q8_0(x) in, Q8_0(h) out (+ the fp64
     # router logits the decode kernel reads to redo the top-k)
-    gate_up_bytes = uniq_avg * (2 * I * H // 2 + 4 * 2 * I) + T * (H + H // 8) + \
+    gate_up_bytes = uniq_avg * (2 * I * H * bits // 8 + 4 * 2 * I) + T * (H + H // 8) + \
         T * (K + S) * (I + I // 8)
     step_bytes = uniq_avg * eb + 4 * E * H + 4 * E + 8 * T * H
     weight_gbps = uniq_avg * eb / (ms_per_step * 1e-3) / 1e9
 
-    roofline = gateup_roofline(kern, cfg, gate_up_bytes, T)
+    roofline = gateup_roofline(kern, cfg, gate_up_bytes, T, bits)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -194,12 +198,15 @@ def main():
         "metric": "MoE-layer tokens/s; decode int4 expert-weight GB/s as % of HBM peak",
         "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": n_steps,
         "warmup": n_warm, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "int4xint8 (int32 block dots, f64 scales)",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights packed by coli_pack_int4)",
-        "config": {"workload": cfg.name + (f" groups {ng}/{tg}" if ng > 1 else ""),
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": f"int{bits}xint8 (int32 block dots, f64 scales)",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights packed by "
+                "coli_pack_weights)",
+        "config": {"workload": cfg.name + (f" groups {ng}/{tg}" if ng > 1 else "") +
+                   (f" int{bits} weights" if bits != 4 else ""),
                    "tokens_per_step": T, "hidden": H, "inter": I,
                    "n_experts": E, "top_k": K, "n_shared": S, "weight_replicas": R,
-                   "n_group": ng, "topk_group": tg,
+                   "n_group": ng, "topk_group": tg, "weight_bits": bits,
                    "parallelism": "none (1 GPU)"},
         "expert_weight_gbps": round(weight_gbps, 1),
         "expert_weight_frac_hbm": round(weight_gbps / HBM_PEAK_GBPS, 4),
@@ -299,9 +306,10 @@ def run_pack_fp8(args, cfg):
     }), flush=True)
 
 
-def gateup_roofline(kern, cfg, gate_up_bytes, T):
+def gateup_roofline(kern, cfg, gate_up_bytes, T, bits=4):
     """Roofline of the gate/up kernel (the dominant launch of every path):
-    algorithmic HBM bytes per launch / its mean event-timed duration."""
+    algorithmic HBM bytes per launch / its mean event-timed duration. The
+    stored traffic figures are those of the int4 kernels."""
     gk = next((k for k in ("dec_gateup", "pf_gateup", "gateup") if k in kern), None)
     if gk is None:
         return None
@@ -311,7 +319,8 @@ def gateup_roofline(kern, cfg, gate_up_bytes, T):
     ach = gate_up_bytes / (ms * 1e-3) / 1e9
     out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-           "traffic": (int(TRAFFIC[(gk, cfg.name)]) if (gk, cfg.name) in TRAFFIC else None),
+           "traffic": (int(TRAFFIC[(gk, cfg.name)])
+                       if bits == 4 and (gk, cfg.name) in TRAFFIC else None),
            "kernel": gk, "bytes_per_launch": int(gate_up_bytes),
            "avg_launch_us": round(ms * 1e3, 2)}
     if gk == "pf_gateup":
@@ -334,11 +343,12 @@ def run_sweep(args, cfg, counts):
 
     H, I, E, K, S = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
     ng, tg = (int(v) for v in args.groups.split(",")) if args.groups else (1, 1)
-    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, ng, tg)
+    bits = args.bits
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, ng, tg, bits)
     R = max(1, args.replicas)
-    layers = [C.LayerWeights(lc, *cs.build_layer(cfg, r, "cuda",
-                                                 lambda w, qv, sv: C.coli_pack_int4(w, qv, sv)))
-              for r in range(R)]
+    layers = [C.LayerWeights(lc, *cs.build_layer(
+        cfg, r, "cuda", lambda w, qv, sv: C.coli_pack_weights(w, bits, qv, sv), bits=bits))
+        for r in range(R)]
     Tmax = max(counts)
     ws = torch.empty(C.coli_moe_workspace_bytes(lc, Tmax), dtype=torch.uint8, device="cuda")
     lay_counts = None
@@ -368,8 +378,10 @@ def run_sweep(args, cfg, counts):
         uniq = int((cnt[:E] > 0).sum().item()) + S
         print(json.dumps({"sweep": cfg.name, "tokens": T, "us_per_call": round(dt * 1e6, 2),
                           "tokens_per_s": round(T / dt, 1), "experts_in_use": uniq,
-                          "path": "few-token" if T <= 3 else "grouped-mfma",
-                          "expert_weight_gbps": round(uniq * cfg.expert_bytes() / dt / 1e9, 1)}),
+                          "path": "few-token" if T <= 3 and bits == 4 else "grouped-mfma",
+                          "weight_bits": bits,
+                          "expert_weight_gbps": round(
+                              uniq * (3 * I * H * bits // 8 + 4 * (2 * I + H)) / dt / 1e9, 1)}),
               flush=True)
 
 
@@ -384,12 +396,15 @@ def run_stack(args, cfg):
 
     T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
     NL = cfg.n_layers
-    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho)
+    bits = args.bits
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, weight_bits=bits)
     n_steps, n_warm = args.steps, args.warmup
     t_setup = time.time()
     layers = []
     for l in range(NL):
-        wr, b, q, s = cs.build_layer(cfg, l, "cuda", lambda w, qv, sv: C.coli_pack_int4(w, qv, sv))
+        wr, b, q, s = cs.build_layer(cfg, l, "cuda",
+                                     lambda w, qv, sv: C.coli_pack_weights(w, bits, qv, sv),
+                                     bits=bits)
         layers.append(C.LayerWeights(lc, wr, b, q, s))
         print(f"[bench] layer {l} packed", file=sys.stderr, flush=True)
     xs = [cs.activations(cfg, 0, "cuda", n_tok=T, first_tok=i * T) for i in range(n_steps + n_warm)]
@@ -432,22 +447,23 @@ def run_stack(args, cfg):
                 kern[names[j]] = kern.get(names[j], 0.0) + evs[j].elapsed_time(evs[j + 1]) / NL
             uniq.append(int((counts_view[:E] > 0).sum().item()) + S)
     uniq_avg = float(np.mean(uniq)) if uniq else float(E + S)
-    gate_up_bytes = uniq_avg * (2 * I * H // 2 + 4 * 2 * I) + T * (H + H // 8) + \
+    gate_up_bytes = uniq_avg * (2 * I * H * bits // 8 + 4 * 2 * I) + T * (H + H // 8) + \
         T * (K + S) * (I + I // 8)
     out = {
         "metric": "MoE-stack tokens/s (8 pre-norm residual MoE layers)",
         "value": round(T * n_steps / elapsed, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": n_steps, "warmup": n_warm, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4xint8 (int32 block dots, f64 scales)",
-        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed by coli_pack_int4)",
-        "config": {"workload": cfg.name, "tokens_per_step": T, "layers": NL, "hidden": H,
-                   "inter": I, "n_experts": E, "top_k": K, "n_shared": S,
+        "dtype": f"int{bits}xint8 (int32 block dots, f64 scales)",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed by coli_pack_weights)",
+        "config": {"workload": cfg.name + (f" int{bits} weights" if bits != 4 else ""),
+                   "tokens_per_step": T, "layers": NL, "hidden": H,
+                   "inter": I, "n_experts": E, "top_k": K, "n_shared": S, "weight_bits": bits,
                    "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_per_step / NL, 4),
         "unique_experts_per_layer": round(uniq_avg, 2),
         "kernel_avg_us_per_layer": {k: round(v * 1e3, 2) for k, v in kern.items()},
-        "roofline": gateup_roofline(kern, cfg, gate_up_bytes, T),
+        "roofline": gateup_roofline(kern, cfg, gate_up_bytes, T, bits),
         "cpu_baseline": None,
         "setup_s": round(setup_s, 1),
     }

@@ -232,28 +232,31 @@ def activations(cfg: MoEConfig, layer: int = 0, device="cpu", n_tok: Optional[in
     return x.contiguous()
 
 
-def build_layer(cfg: MoEConfig, layer: int, device, pack_into, experts=None):
+def build_layer(cfg: MoEConfig, layer: int, device, pack_into, experts=None, bits: int = 4):
     """Draw a layer's expert weights matrix by matrix on `device` and hand each
     fp32 matrix to the caller's packer, pack_into(w, q_view, s_view), which
-    fills the boundary blobs. This module does no packing itself.
+    fills the boundary blobs (q_view holds `bits`-wide codes: cols * bits / 8
+    bytes per row). This module does no packing itself.
 
-    Returns (w_router [E,H], bias [E], experts_q u8 [(E+S)*3*I*H/2],
+    Returns (w_router [E,H], bias [E], experts_q u8 [(E+S)*3*I*H*bits/8],
     experts_scale f32 [(E+S)*(2I+H)]). Experts not in `experts` stay unset.
     """
     dev = torch.device(device)
     H, I = cfg.hidden, cfg.inter
     n = cfg.n_experts + cfg.n_shared
-    bq, bs = 3 * I * H // 2, 2 * I + H
+    mb = I * H * bits // 8  # bytes of one packed matrix
+    bq, bs = 3 * mb, 2 * I + H
     q = torch.empty(n * bq, dtype=torch.uint8, device=dev)
     s = torch.empty(n * bs, dtype=torch.float32, device=dev)
     buf_gu = torch.empty((I, H), dtype=torch.float32, device=dev)
     buf_d = torch.empty((H, I), dtype=torch.float32, device=dev)
-    parts = (("gate", I, H, 0, 0, buf_gu), ("up", I, H, I * H // 2, I, buf_gu),
-             ("down", H, I, I * H, 2 * I, buf_d))
+    parts = (("gate", I, H, 0, 0, buf_gu), ("up", I, H, mb, I, buf_gu),
+             ("down", H, I, 2 * mb, 2 * I, buf_d))
     for e in (range(n) if experts is None else experts):
         for which, rows, cols, qo, so, buf in parts:
             w = expert_matrix(cfg, layer, e, which, dev, out=buf)
-            qv = q[e * bq + qo:e * bq + qo + rows * cols // 2].view(rows, cols // 2)
+            rb = cols * bits // 8
+            qv = q[e * bq + qo:e * bq + qo + rows * rb].view(rows, rb)
             sv = s[e * bs + so:e * bs + so + rows]
             pack_into(w, qv, sv)
     wr, b = router(cfg, layer, dev)

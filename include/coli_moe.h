@@ -72,6 +72,8 @@ typedef struct coli_moe_cfg {
                              2..64 groups of n_experts / n_group consecutive experts */
     int32_t topk_group;   /* groups kept when n_group > 1: 1..n_group, and the kept
                              groups must hold at least top_k experts */
+    int32_t weight_bits;  /* expert weight codes: 4 (0 reads as 4), 8 or 2; int8 and
+                             int2 need hidden and inter multiples of 64 */
     int32_t reserved;     /* must be 0 */
 } coli_moe_cfg;
 
@@ -79,10 +81,12 @@ typedef struct coli_moe_cfg {
  *  w_router      [E, H] fp32 router weight (kept in F32, not quantised)
  *  bias          [E] fp32 correction bias: added to the sigmoid score for
  *                expert selection only; the gate value is the unbiased score
- *  experts_q     E + n_shared contiguous expert blobs of 3*I*H/2 bytes, blob e =
- *                [gate I x H/2 | up I x H/2 | down H x I/2], rows = output
- *                channels, byte j of a row = code(2j) | code(2j+1) << 4 with
- *                4-bit two's complement codes in -7..7 (coli_pack_int4 format);
+ *  experts_q     E + n_shared contiguous expert blobs of 3*I*H*b/8 bytes (b =
+ *                weight_bits), blob e = [gate I x H b/8 | up I x H b/8 |
+ *                down H x I b/8], rows = output channels, in the
+ *                coli_pack_weights format of width b (int4: byte j of a row =
+ *                code(2j) | code(2j+1) << 4 with 4-bit two's complement codes
+ *                in -7..7, the coli_pack_int4 format);
  *                the shared expert is blob E. One blob is the unit the engine
  *                reads with a single pread (devtrends.cc page, section
  *                引擎是如何工作的).
@@ -125,6 +129,19 @@ typedef struct coli_moe_ws_layout {
 
 /* Message for a return code (static string, never NULL). */
 COLI_API const char* coli_strerror(int code);
+
+/* Pack an fp32 matrix [rows, cols] into symmetric b-bit codes, b = 4 as
+ * coli_pack_int4 below, or its int8 / int2 siblings (Colibri page, feature
+ * list 关键特性: quantisation kernels for int8, int4 and int2): per row
+ * s = fp32(max|w|/Q), Q = 2^(b-1) - 1 (127, 7, 1); code = clamp(rint(w/s),
+ * -Q, Q) with round-half-to-even and IEEE division; s == 0 gives code 0;
+ * codes are b-bit two's complement packed little end first (element j of a
+ * row in byte j b / 8 at bit (j b) % 8).
+ *   w [rows, cols] fp32 (in), q [rows, cols b/8] u8 (out), scale [rows] fp32
+ *   (out). cols must be a positive multiple of 32, rows >= 0 (0: no-op), b
+ *   in {2, 4, 8} (else COLI_E_INVAL). Bit-exact with the plain definition. */
+COLI_API int coli_pack_weights(const float* w, int64_t rows, int64_t cols, int bits, uint8_t* q,
+                               float* scale, void* stream);
 
 /* Pack an fp32 matrix [rows, cols] into symmetric int4 (wmrh.cn page,
  * section 量化流程): per row s = fp32(max|w|/7); code = clamp(rint(w/s), -7, 7)

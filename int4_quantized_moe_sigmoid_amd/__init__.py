@@ -25,7 +25,8 @@ COLI_E_UNSUPPORTED = -5
 COLI_FWD_ACCUM = 1
 COLI_FWD_DEBUG_TAPS = 2
 
-EXPORTS = ("coli_strerror", "coli_pack_int4", "coli_pack_fp8_int4", "coli_quant_q8", "coli_moe_workspace_bytes",
+EXPORTS = ("coli_strerror", "coli_pack_weights", "coli_pack_int4", "coli_pack_fp8_int4",
+           "coli_quant_q8", "coli_moe_workspace_bytes",
            "coli_moe_workspace_layout", "coli_moe_route", "coli_moe_forward",
            "coli_moe_forward_profiled", "coli_rmsnorm")
 
@@ -41,7 +42,8 @@ class coli_moe_cfg(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("norm_topk", ctypes.c_int32),
                 ("routed_scale", ctypes.c_float), ("n_group", ctypes.c_int32),
-                ("topk_group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("topk_group", ctypes.c_int32), ("weight_bits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class coli_moe_weights(ctypes.Structure):
@@ -69,6 +71,7 @@ def _load():
     L.coli_strerror.restype = ctypes.c_char_p
     L.coli_pack_int4.argtypes = [vp, i64, i64, vp, vp, vp]
     L.coli_pack_fp8_int4.argtypes = [vp, vp, i64, i64, vp, vp, vp]
+    L.coli_pack_weights.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     L.coli_quant_q8.argtypes = [vp, i64, i64, vp, vp, vp]
     L.coli_moe_workspace_bytes.argtypes = [ctypes.POINTER(coli_moe_cfg), i64, u32]
     L.coli_moe_workspace_bytes.restype = sz
@@ -120,11 +123,12 @@ def _stream(stream) -> Optional[int]:
 
 def make_cfg(hidden: int, inter: int, n_experts: int, top_k: int, n_shared: int = 1,
              norm_topk: bool = True, routed_scale: float = 2.5, n_group: int = 1,
-             topk_group: int = 1) -> coli_moe_cfg:
+             topk_group: int = 1, weight_bits: int = 4) -> coli_moe_cfg:
     """n_group > 1 selects the experts among the topk_group best of n_group
-    groups (group-limited top-k); 1 is the plain selection."""
+    groups (group-limited top-k); 1 is the plain selection. weight_bits: width
+    of the expert weight codes (4, 8 or 2)."""
     return coli_moe_cfg(hidden, inter, n_experts, top_k, n_shared, int(bool(norm_topk)),
-                        routed_scale, int(n_group), int(topk_group), 0)
+                        routed_scale, int(n_group), int(topk_group), int(weight_bits), 0)
 
 
 class LayerWeights:
@@ -134,9 +138,11 @@ class LayerWeights:
                  experts_q: torch.Tensor, experts_scale: torch.Tensor):
         n = cfg.n_experts + cfg.n_shared
         H, I = cfg.hidden, cfg.inter
+        bits = cfg.weight_bits or 4
         if tuple(w_router.shape) != (cfg.n_experts, H) or tuple(bias.shape) != (cfg.n_experts,):
             raise ValueError("router weight / bias shape mismatch")
-        if experts_q.numel() != n * 3 * I * H // 2 or experts_scale.numel() != n * (2 * I + H):
+        if experts_q.numel() != n * 3 * I * H * bits // 8 or \
+                experts_scale.numel() != n * (2 * I + H):
             raise ValueError("expert blob sizes do not match the config")
         self.cfg = cfg
         self.w_router, self.bias = w_router, bias
@@ -151,12 +157,14 @@ class LayerWeights:
                    e: int):
         """(gate_q, up_q, down_q, gate_s, up_s, down_s) views of expert e's blobs."""
         H, I = cfg.hidden, cfg.inter
-        bq = 3 * I * H // 2
+        bits = cfg.weight_bits or 4
+        mb = I * H * bits // 8
+        bq = 3 * mb
         q = experts_q.view(-1)[e * bq:(e + 1) * bq]
         bs = 2 * I + H
         s = experts_scale.view(-1)[e * bs:(e + 1) * bs]
-        return (q[:I * H // 2].view(I, H // 2), q[I * H // 2:I * H].view(I, H // 2),
-                q[I * H:].view(H, I // 2), s[:I], s[I:2 * I], s[2 * I:])
+        return (q[:mb].view(I, H * bits // 8), q[mb:2 * mb].view(I, H * bits // 8),
+                q[2 * mb:].view(H, I * bits // 8), s[:I], s[I:2 * I], s[2 * I:])
 
 
 # --------------------------------------------------------------------------
@@ -168,6 +176,14 @@ def coli_pack_int4(w: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream
     _check(_lib.coli_pack_int4(_dev(w, "w", torch.float32), rows, cols,
                                _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
                                _stream(stream)), "coli_pack_int4")
+
+
+def coli_pack_weights(w: torch.Tensor, bits: int, q: torch.Tensor, scale: torch.Tensor,
+                      stream=None):
+    rows, cols = w.shape
+    _check(_lib.coli_pack_weights(_dev(w, "w", torch.float32), rows, cols, int(bits),
+                                  _dev(q, "q", torch.uint8), _dev(scale, "scale", torch.float32),
+                                  _stream(stream)), "coli_pack_weights")
 
 
 def coli_pack_fp8_int4(q8: torch.Tensor, block_scale: torch.Tensor, q: torch.Tensor,

@@ -37,6 +37,8 @@ int check_cfg(const coli_moe_cfg* c) {
     if (c->n_shared < 0 || c->n_shared > 1) return COLI_E_INVAL;
     if (!std::isfinite(c->routed_scale)) return COLI_E_INVAL;
     if (c->n_group < 0) return COLI_E_INVAL;
+    if (c->weight_bits != 0 && c->weight_bits != 2 && c->weight_bits != 4 && c->weight_bits != 8)
+        return COLI_E_INVAL;
     if (c->n_group > 1) {
         if (c->n_group > 64) return COLI_E_UNSUPPORTED;
         if (c->n_experts % c->n_group || c->topk_group < 1 || c->topk_group > c->n_group ||
@@ -48,6 +50,9 @@ int check_cfg(const coli_moe_cfg* c) {
         return COLI_E_UNSUPPORTED;
     return COLI_OK;
 }
+
+// Width of the expert weight codes (0 reads as 4).
+inline int weight_bits(const coli_moe_cfg& c) { return c.weight_bits ? c.weight_bits : 4; }
 
 GroupSel group_sel(const coli_moe_cfg& c) {
     GroupSel g{1, c.n_experts, 1};
@@ -216,7 +221,7 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
 // Few-token path: three fused kernels (k_decode.h). Shapes it covers:
 // hidden <= 6144, intermediate <= 2048, <= 256 routed experts.
 bool small_path_fits(const coli_moe_cfg& c, int64_t T) {
-    return T <= 3 && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
+    return weight_bits(c) == 4 && T <= 3 && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
            c.inter <= 2048 && c.inter % 64 == 0 && c.n_experts <= 256;
 }
 
@@ -279,7 +284,12 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
     if (ws_bytes < L.pub.total) return COLI_E_WORKSPACE;
 
     const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, S = c.n_shared;
-    const int64_t blob_q = 3ll * I * H / 2, blob_s = 2ll * I + H;
+    const int bits = weight_bits(c);
+    const int64_t blob_q = 3ll * I * H * bits / 8, blob_s = 2ll * I + H;
+    // grouped MFMA path when the row tiles divide the shapes, else the GEMV
+    // path; int8 and int2 weights run on the MFMA kernels only
+    const bool mfma = (H % pf::kRows) == 0 && (I % pf::kRows) == 0;
+    if (bits != 4 && !mfma) return COLI_E_UNSUPPORTED;
     char* base = static_cast<char*>(ws);
     int8_t* qx = reinterpret_cast<int8_t*>(base + L.pub.qx);
     float* dx = reinterpret_cast<float*>(base + L.pub.dx);
@@ -321,13 +331,15 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
 
     mk.mark("quant_x");
     const int64_t nblk = T * (H / 32);
-    k_quant_q8<true><<<(unsigned)((nblk * 4 + 255) / 256), 256, 0, s>>>(x, nblk, qx, dx);
+    // activations in the element order of the weight width's operand
+    const unsigned qg = (unsigned)((nblk * 4 + 255) / 256);
+    if (bits == 4) k_quant_q8<1><<<qg, 256, 0, s>>>(x, nblk, qx, dx);
+    else if (bits == 2) k_quant_q8<2><<<qg, 256, 0, s>>>(x, nblk, qx, dx);
+    else k_quant_q8<0><<<qg, 256, 0, s>>>(x, nblk, qx, dx);
 
     launch_route(c, x, w->w_router, w->bias, T, logits,
                  reinterpret_cast<double*>(base + L.rpart), idx, wts, s, mk);
 
-    // grouped MFMA path when the row tiles divide the shapes, else the GEMV path
-    const bool mfma = (H % pf::kRows) == 0 && (I % pf::kRows) == 0;
     const int ch = mfma ? pf::kTok : L.ch;
     const int64_t n_it = max_items_for(c, T, ch);
     mk.mark("bucket_lists");
@@ -347,10 +359,23 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         pa.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
         mk.mark("pf_gateup");
         const dim3 g1((unsigned)((I / pf::kRows) * n_it));
-        if (tap) pf::k_pf_gateup<true><<<g1, 256, 0, s>>>(pa);
-        else pf::k_pf_gateup<false><<<g1, 256, 0, s>>>(pa);
-        mk.mark("pf_down");
-        pf::k_pf_down<<<dim3((unsigned)((H / pf::kRows) * n_it)), 256, 0, s>>>(pa);
+        const dim3 g2((unsigned)((H / pf::kRows) * n_it));
+        if (bits == 4) {
+            if (tap) pf::k_pf_gateup<4, true><<<g1, 256, 0, s>>>(pa);
+            else pf::k_pf_gateup<4, false><<<g1, 256, 0, s>>>(pa);
+            mk.mark("pf_down");
+            pf::k_pf_down<4><<<g2, 256, 0, s>>>(pa);
+        } else if (bits == 8) {
+            if (tap) pf::k_pf_gateup<8, true><<<g1, 256, 0, s>>>(pa);
+            else pf::k_pf_gateup<8, false><<<g1, 256, 0, s>>>(pa);
+            mk.mark("pf_down");
+            pf::k_pf_down<8><<<g2, 256, 0, s>>>(pa);
+        } else {
+            if (tap) pf::k_pf_gateup<2, true><<<g1, 256, 0, s>>>(pa);
+            else pf::k_pf_gateup<2, false><<<g1, 256, 0, s>>>(pa);
+            mk.mark("pf_down");
+            pf::k_pf_down<2><<<g2, 256, 0, s>>>(pa);
+        }
     } else {
     const int nt = (T >= L.ch) ? L.ch : (int)T;  // tokens per item at most
     const int nbj_h = (H / 32 + 63) / 64;
@@ -406,15 +431,24 @@ COLI_API const char* coli_strerror(int code) {
     }
 }
 
-COLI_API int coli_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* scale,
-                            void* stream) {
-    if (rows < 0 || cols <= 0 || cols % 32) return COLI_E_INVAL;
+COLI_API int coli_pack_weights(const float* w, int64_t rows, int64_t cols, int bits, uint8_t* q,
+                               float* scale, void* stream) {
+    if (rows < 0 || cols <= 0 || cols % 32 || (bits != 2 && bits != 4 && bits != 8))
+        return COLI_E_INVAL;
     if (rows == 0) return COLI_OK;
     if (!w || !q || !scale) return COLI_E_INVAL;
     if (misaligned(w) || misaligned(q) || misaligned(scale)) return COLI_E_ALIGN;
     if (rows > 0x7fffffffll) return COLI_E_UNSUPPORTED;
-    k_pack_int4<<<(unsigned)rows, 256, 0, (hipStream_t)stream>>>(w, cols, q, scale);
+    const hipStream_t st = (hipStream_t)stream;
+    if (bits == 4) k_pack_bits<4><<<(unsigned)rows, 256, 0, st>>>(w, cols, q, scale);
+    else if (bits == 8) k_pack_bits<8><<<(unsigned)rows, 256, 0, st>>>(w, cols, q, scale);
+    else k_pack_bits<2><<<(unsigned)rows, 256, 0, st>>>(w, cols, q, scale);
     return hip_status();
+}
+
+COLI_API int coli_pack_int4(const float* w, int64_t rows, int64_t cols, uint8_t* q, float* scale,
+                            void* stream) {
+    return coli_pack_weights(w, rows, cols, 4, q, scale, stream);
 }
 
 COLI_API int coli_pack_fp8_int4(const uint8_t* q8, const float* block_scale, int64_t rows,
@@ -453,7 +487,7 @@ COLI_API int coli_quant_q8(const float* x, int64_t n_tok, int64_t dim, int8_t* q
     const int64_t nblk = n_tok * (dim / 32);
     const int64_t nthr = nblk * 4;
     if ((nthr + 255) / 256 > 0x7fffffffll) return COLI_E_UNSUPPORTED;
-    k_quant_q8<false><<<(unsigned)((nthr + 255) / 256), 256, 0, (hipStream_t)stream>>>(x, nblk, q,
+    k_quant_q8<0><<<(unsigned)((nthr + 255) / 256), 256, 0, (hipStream_t)stream>>>(x, nblk, q,
                                                                                        d);
     return hip_status();
 }

@@ -19,12 +19,21 @@
 // e3 e5 e7) in which activations are stored, so B is 8 plain bytes of the
 // activation row.
 //
-// Both operands go through LDS in chunks of 16 blocks, loaded one chunk
+// The int8 and int2 weight formats use the same kernels: an int8 row is its
+// own A operand (8 plain bytes, activations in natural order); for int2 a
+// dword holds 16 codes and (x << s) & 0xC0C0C0C0, s = 6, 4, 2, 0, holds 64 *
+// the elements 4j + (6 - s) / 2 of bytes j, i.e. the 16-element order (e0 e4
+// e8 e12 e1 e5 e9 e13 e2 e6 e10 e14 e3 e7 e11 e15) of the activations. The
+// x16 / x64 leave the fp64 epilogue as an exact power-of-two scale.
+//
+// Both operands go through LDS in chunks of 16 blocks (8 for int8), loaded one chunk
 // ahead into registers with coalesced 16-byte loads: weight rows per wave
 // (each wave reads only its own rows), the item's activation rows and block
 // scales once per workgroup (all four waves use the same tokens). Pitches
 // are padded so the operand reads hit distinct banks.
 #pragma once
+
+#include <type_traits>
 
 #include "coli_common.h"
 
@@ -37,12 +46,23 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kTok = 32;              // tokens per work item
 constexpr int kRows = 64;             // output rows per workgroup
-constexpr int kChunk = 16;            // blocks staged per step
-constexpr int kPitch = kChunk * 16 + 8;  // LDS bytes per staged row
-constexpr int kActPitch = kChunk * 32 + 16;  // LDS bytes per staged activation row
-constexpr int kDPitch = kChunk + 1;          // floats per staged scale row
-constexpr int kActBytes = kTok * kActPitch;
-constexpr int kDBytes = kTok * kDPitch * 4;
+
+// Staging geometry and operand form of one weight width (2, 4 or 8 bits).
+template <int BITS>
+struct WFmt {
+    static constexpr int CH = BITS == 8 ? 8 : 16;  // blocks staged per step
+    static constexpr int WB = 4 * BITS;            // bytes of a 32-wide block of a row
+    static constexpr int RB = CH * WB;             // bytes of a row per chunk
+    static constexpr int PB = RB / 16;             // bytes per lane (16 lanes per row)
+    static constexpr int Pitch = RB + 8;           // LDS bytes per staged row
+    static constexpr int ActPitch = CH * 32 + 16;  // LDS bytes per staged activation row
+    static constexpr int DPitch = CH + 1;          // floats per staged scale row
+    static constexpr int ActBytes = kTok * ActPitch;
+    static constexpr int DBytes = kTok * DPitch * 4;
+    static constexpr int Scale = BITS == 4 ? 16 : BITS == 2 ? 64 : 1;  // code multiplier
+    static constexpr double InvScale = 1.0 / Scale;                    // exact
+    static constexpr int Layout = BITS == 4 ? 1 : BITS == 2 ? 2 : 0;   // activation order
+};
 
 struct PfArgs {
     const uint8_t* eq;
@@ -71,75 +91,100 @@ __device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
     return *reinterpret_cast<const uint32_t*>(p);
 }
 
-// Stages NR rows of one chunk: lane l loads 16 bytes of staged row
-// (l >> 4) + 4k at block (l & 15) of the chunk. Staged rows 16m .. 16m+15
+// A operand (8 int8 values, k = 8q .. 8q+7 of the block's k order) of the
+// staged block starting at blk, for lane group q.
+template <int BITS>
+__device__ __forceinline__ long a_op(const uint8_t* blk, int q) {
+    if (BITS == 4) return a_operand(lds_u32(blk + 4 * q));
+    if (BITS == 8) return *reinterpret_cast<const long*>(blk + 8 * q);
+    const uint32_t x = lds_u32(blk + 4 * (q >> 1));
+    const int s1 = (q & 1) ? 2 : 6;
+    const uint32_t lo = (x << s1) & 0xC0C0C0C0u, hi = (x << (s1 - 2)) & 0xC0C0C0C0u;
+    return (long)lo | ((long)hi << 32);
+}
+
+// Stages NR rows of one chunk: lane l loads PB bytes (16, int2: 8) of staged
+// row (l >> 4) + 4k at piece (l & 15) of the chunk. Staged rows 16m .. 16m+15
 // are rows 0..15 of matrix m, starting at base[m] (this lane's row l >> 4)
-// with `stride` bytes between rows.
-template <int NR>
+// with `stride` bytes between rows, `rowb` bytes per row.
+template <int NR, int BITS>
 struct Stager {
+    typedef WFmt<BITS> F;
+    typedef unsigned v2u __attribute__((ext_vector_type(2)));
+    typedef typename std::conditional<F::PB == 16, v4u, v2u>::type piece_t;
     const uint8_t* base[NR / 16];
     int64_t stride;
-    __device__ __forceinline__ void issue(int c, int BH, v4u (&v)[NR / 4]) const {
-        const int b = min(c * kChunk + (int)(threadIdx.x & 15), BH - 1);
+    int rowb;
+    __device__ __forceinline__ void issue(int c, piece_t (&v)[NR / 4]) const {
+        const int off = min(c * F::RB + (int)(threadIdx.x & 15) * F::PB, rowb - F::PB);
 #pragma unroll
         for (int k = 0; k < NR / 4; ++k)
-            v[k] = *reinterpret_cast<const v4u*>(base[k / 4] + (int64_t)(4 * (k % 4)) * stride +
-                                                 b * 16);
+            v[k] = *reinterpret_cast<const piece_t*>(base[k / 4] + (int64_t)(4 * (k % 4)) * stride +
+                                                     off);
     }
-    __device__ __forceinline__ void commit(uint8_t* lds, const v4u (&v)[NR / 4]) const {
+    __device__ __forceinline__ void commit(uint8_t* lds, const piece_t (&v)[NR / 4]) const {
         const int r0 = (threadIdx.x & 63) >> 4, bi = threadIdx.x & 15;
-        typedef unsigned v2u __attribute__((ext_vector_type(2)));
 #pragma unroll
         for (int k = 0; k < NR / 4; ++k) {
-            uint8_t* d = lds + (r0 + 4 * k) * kPitch + bi * 16;
-            *reinterpret_cast<v2u*>(d) = v[k].xy;
-            *reinterpret_cast<v2u*>(d + 8) = v[k].zw;
+            uint8_t* d = lds + (r0 + 4 * k) * F::Pitch + bi * F::PB;
+            if constexpr (F::PB == 16) {
+                *reinterpret_cast<v2u*>(d) = v[k].xy;
+                *reinterpret_cast<v2u*>(d + 8) = v[k].zw;
+            } else {
+                *reinterpret_cast<v2u*>(d) = v[k];
+            }
         }
     }
 };
 
 // Activation rows of the item's 32 tokens (rows of a [*, NB * 32] int8
-// matrix in 8-group order, with NB block scales per row), one chunk of 16
-// blocks: thread tid loads the 16-byte half (tid & 1) of block (tid & 31) >> 1
-// of token rows (tid >> 5) + 8k, and threads < 128 four block scales.
+// matrix in the width's element order, with NB block scales per row), one
+// chunk of CH blocks: thread tid loads the 16-byte half (tid & 1) of block
+// (tid % 2CH) / 2 of token rows tid / 2CH + (256 / 2CH) k, and threads below
+// 8 CH four block scales each.
+template <int CH>
 struct ActStager {
-    const int8_t* row[4];
+    static constexpr int TPR = 2 * CH;        // threads per token row
+    static constexpr int RPP = 256 / TPR;     // token rows per pass
+    static constexpr int NP = kTok / RPP;     // passes
+    static constexpr int ActPitch = CH * 32 + 16, DPitch = CH + 1;
+    const int8_t* row[NP];
     const float* drow;
     __device__ __forceinline__ void init(const int8_t* base, const float* dbase, int64_t pitch,
                                          int NB, const int32_t* rows_of, int n) {
         const int half = threadIdx.x & 1;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int j = min((int)(threadIdx.x >> 5) + 8 * k, n - 1);
+        for (int k = 0; k < NP; ++k) {
+            const int j = min((int)(threadIdx.x / TPR) + RPP * k, n - 1);
             row[k] = base + (int64_t)rows_of[j] * pitch + 16 * half;
         }
-        const int jd = min((int)((threadIdx.x & 127) >> 2), n - 1);
+        const int jd = min((int)((threadIdx.x % (8 * CH)) / (CH / 4)), n - 1);
         drow = dbase + (int64_t)rows_of[jd] * NB;
     }
-    __device__ __forceinline__ void issue(int c, int NB, v4u (&v)[4], float (&dv)[4]) const {
-        const int b = min(c * kChunk + (int)((threadIdx.x & 31) >> 1), NB - 1);
+    __device__ __forceinline__ void issue(int c, int NB, v4u (&v)[NP], float (&dv)[4]) const {
+        const int b = min(c * CH + (int)((threadIdx.x % TPR) >> 1), NB - 1);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const v4u*>(row[k] + b * 32);
-        // every thread loads (threads >= 128 repeat rows of the first 128, in
-        // bounds), so the values stay in registers; only threads < 128 store
-        const int b0 = c * kChunk + (threadIdx.x & 3) * 4;
+        for (int k = 0; k < NP; ++k) v[k] = *reinterpret_cast<const v4u*>(row[k] + b * 32);
+        // every thread loads (threads >= 8 CH repeat rows of the first 8 CH, in
+        // bounds), so the values stay in registers; only threads < 8 CH store
+        const int b0 = c * CH + (threadIdx.x % (CH / 4)) * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dv[i] = drow[min(b0 + i, NB - 1)];
     }
     // Scales of blocks past NB are stored as 0, so those blocks add nothing.
     __device__ __forceinline__ void commit(int c, int NB, uint8_t* act, float* dbuf,
-                                           const v4u (&v)[4], const float (&dv)[4]) const {
-        const int blk = (threadIdx.x & 31) >> 1, half = threadIdx.x & 1;
+                                           const v4u (&v)[NP], const float (&dv)[4]) const {
+        const int blk = (threadIdx.x % TPR) >> 1, half = threadIdx.x & 1;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int j = (threadIdx.x >> 5) + 8 * k;
-            *reinterpret_cast<v4u*>(act + j * kActPitch + blk * 32 + 16 * half) = v[k];
+        for (int k = 0; k < NP; ++k) {
+            const int j = threadIdx.x / TPR + RPP * k;
+            *reinterpret_cast<v4u*>(act + j * ActPitch + blk * 32 + 16 * half) = v[k];
         }
-        if (threadIdx.x < 128) {
-            const int j = threadIdx.x >> 2, b0 = (threadIdx.x & 3) * 4;
+        if (threadIdx.x < 8 * CH) {
+            const int j = threadIdx.x / (CH / 4), b0 = (threadIdx.x % (CH / 4)) * 4;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                dbuf[j * kDPitch + b0 + i] = (c * kChunk + b0 + i < NB) ? dv[i] : 0.0f;
+                dbuf[j * DPitch + b0 + i] = (c * CH + b0 + i < NB) ? dv[i] : 0.0f;
         }
     }
 };
@@ -148,20 +193,24 @@ struct ActStager {
 // group, fp64 epilogue. Inside a chunk there are no branches, so the
 // compiler can overlap the next block's LDS reads and MFMAs with the current
 // block's epilogue.
-template <int NG, bool TAP>
-__device__ __forceinline__ void gateup_loop(const PfArgs& a, const Stager<32>& st, const ActStager& as,
-                                            uint8_t* lds, uint8_t* act, float* dbuf,
-                                            double (&accg)[2][4], double (&accu)[2][4], int BH,
-                                            int r0, int q, int lr, int s0, int n) {
+template <int BITS, int NG, bool TAP>
+__device__ __forceinline__ void gateup_loop(const PfArgs& a, const Stager<32, BITS>& st,
+                                            const ActStager<WFmt<BITS>::CH>& as, uint8_t* lds,
+                                            uint8_t* act, float* dbuf, double (&accg)[2][4],
+                                            double (&accu)[2][4], int BH, int r0, int q, int lr,
+                                            int s0, int n) {
+    typedef WFmt<BITS> F;
+    constexpr int CH = F::CH;
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int i = 0; i < 4; ++i) accg[g][i] = accu[g][i] = 0.0;
     const v4i zero = {0, 0, 0, 0};
-    const int nch = (BH + kChunk - 1) / kChunk;
-    v4u wv[8], av[4];
+    const int nch = (BH + CH - 1) / CH;
+    typename Stager<32, BITS>::piece_t wv[8];
+    v4u av[ActStager<CH>::NP];
     float adv[4];
-    st.issue(0, BH, wv);
+    st.issue(0, wv);
     as.issue(0, BH, av, adv);
     st.commit(lds, wv);
     as.commit(0, BH, act, dbuf, av, adv);
@@ -171,17 +220,18 @@ __device__ __forceinline__ void gateup_loop(const PfArgs& a, const Stager<32>& s
         // unconditional (keeps the staging registers out of memory); after
         // the last chunk this re-reads that chunk, from cache
         const int cn = min(c + 1, nch - 1);
-        st.issue(cn, BH, wv);
+        st.issue(cn, wv);
         as.issue(cn, BH, av, adv);
 #pragma unroll
-        for (int bi = 0; bi < kChunk; ++bi) {
-            const long ag = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
-            const long au = a_operand(lds_u32(lds + (16 + lr) * kPitch + bi * 16 + 4 * q));
+        for (int bi = 0; bi < CH; ++bi) {
+            const long ag = a_op<BITS>(lds + lr * F::Pitch + bi * F::WB, q);
+            const long au = a_op<BITS>(lds + (16 + lr) * F::Pitch + bi * F::WB, q);
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int j = 16 * g + lr;
-                const long bv = *reinterpret_cast<const long*>(act + j * kActPitch + bi * 32 + 8 * q);
-                const double dd = (double)dbuf[j * kDPitch + bi];
+                const long bv =
+                    *reinterpret_cast<const long*>(act + j * F::ActPitch + bi * 32 + 8 * q);
+                const double dd = (double)dbuf[j * F::DPitch + bi];
                 const v4i cg = __builtin_amdgcn_mfma_i32_16x16x32_i8(ag, bv, zero, 0, 0, 0);
                 const v4i cu = __builtin_amdgcn_mfma_i32_16x16x32_i8(au, bv, zero, 0, 0, 0);
 #pragma unroll
@@ -191,13 +241,13 @@ __device__ __forceinline__ void gateup_loop(const PfArgs& a, const Stager<32>& s
                     asm volatile("" : "+v"(accg[g][i]), "+v"(accu[g][i]));
                 }
                 if (TAP) {
-                    const int b = c * kChunk + bi;
+                    const int b = c * CH + bi;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = r0 + 4 * q + i;
                         if (j < n && b < BH && (r % a.tap_stride) == 0)
                             a.tap[((int64_t)(s0 + j) * a.tap_rows + r / a.tap_stride) * BH + b] =
-                                cg[i] / 16;
+                                cg[i] / F::Scale;
                     }
                 }
             }
@@ -209,11 +259,22 @@ __device__ __forceinline__ void gateup_loop(const PfArgs& a, const Stager<32>& s
     }
 }
 
-// Gate/up + SwiGLU + Q8_0(h) for one item and 64 intermediate rows.
-template <bool TAP>
+// Element of a 32-block stored at byte p in activation order L (0 natural,
+// 1 int4's 8-group order, 2 int2's 16-group order).
+template <int L>
+__device__ __forceinline__ constexpr int act_elem(int p) {
+    return L == 0 ? p
+         : L == 1 ? (p & ~7) + 2 * (p & 3) + ((p >> 2) & 1)
+                  : (p & ~15) + 4 * (p & 3) + ((p >> 2) & 3);
+}
+
+// Gate/up + SwiGLU + Q8_0(h) for one item and 64 intermediate rows; Q8_0(h)
+// is stored in the activation order of the down weights' width.
+template <int BITS, bool TAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_pf_gateup(PfArgs a) {
-    constexpr int kW = 32 * kPitch;  // per-wave weight staging (16 gate + 16 up rows)
-    __shared__ __align__(16) uint8_t smem[4 * kW + kActBytes + kDBytes];
+    typedef WFmt<BITS> F;
+    constexpr int kW = 32 * F::Pitch;  // per-wave weight staging (16 gate + 16 up rows)
+    __shared__ __align__(16) uint8_t smem[4 * kW + F::ActBytes + F::DBytes];
     const int nrt = a.I / kRows;
     const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
     if (it >= *a.n_items) return;
@@ -223,25 +284,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, q = lane >> 4;
     const int ng = (n + 15) >> 4;  // 16-token groups in use (1 or 2)
+    const int64_t rowb = (int64_t)H * BITS / 8;
     const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
-    const uint8_t* up = gate + (int64_t)I * (H >> 1);
+    const uint8_t* up = gate + (int64_t)I * rowb;
     const int r0 = rt * kRows + wave * 16;
     uint8_t* lds = smem + wave * kW;
     uint8_t* act = smem + 4 * kW;
-    float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + kActBytes);
+    float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + F::ActBytes);
+    static_assert(F::ActBytes >= kTok * (kRows + 1) * 4, "h reuses the activation area");
 
-    Stager<32> st;  // staged rows 0..15: gate rows r0.., 16..31: up rows r0..
-    st.stride = H >> 1;
-    st.base[0] = gate + (int64_t)(r0 + q) * (H >> 1);
-    st.base[1] = up + (int64_t)(r0 + q) * (H >> 1);
-    ActStager as;
+    Stager<32, BITS> st;  // staged rows 0..15: gate rows r0.., 16..31: up rows r0..
+    st.stride = rowb;
+    st.rowb = (int)rowb;
+    st.base[0] = gate + (int64_t)(r0 + q) * rowb;
+    st.base[1] = up + (int64_t)(r0 + q) * rowb;
+    ActStager<F::CH> as;
     as.init(a.qx, a.dx, H, BH, a.slot_tok + s0, n);
 
     double accg[2][4], accu[2][4];
     if (ng == 1)
-        gateup_loop<1, TAP>(a, st, as, lds, act, dbuf, accg, accu, BH, r0, q, lr, s0, n);
+        gateup_loop<BITS, 1, TAP>(a, st, as, lds, act, dbuf, accg, accu, BH, r0, q, lr, s0, n);
     else
-        gateup_loop<2, TAP>(a, st, as, lds, act, dbuf, accg, accu, BH, r0, q, lr, s0, n);
+        gateup_loop<BITS, 2, TAP>(a, st, as, lds, act, dbuf, accg, accu, BH, r0, q, lr, s0, n);
     __syncthreads();  // the activation area is reused for h below
     float (*hbuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(act);
 
@@ -254,9 +318,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const float gsr = gs[r], usr = us[r];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-            // the sums carry the x16 of the weight codes: scale by 1/16 (exact)
-            const float gv = (float)((double)gsr * (accg[g][i] * 0.0625));
-            const float uv = (float)((double)usr * (accu[g][i] * 0.0625));
+            // the sums carry the multiplier of the weight codes: scale it away (exact)
+            const float gv = (float)((double)gsr * (accg[g][i] * F::InvScale));
+            const float uv = (float)((double)usr * (accu[g][i] * F::InvScale));
             hbuf[16 * g + lr][wave * 16 + 4 * q + i] = swiglu_f32(gv, uv);
         }
     }
@@ -270,34 +334,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const float d = amax / 127.0f;
         uint32_t w[8];
 #pragma unroll
-        for (int g8 = 0; g8 < 4; ++g8) {
-            const float* v = hv + 8 * g8;
-            w[2 * g8] = pack4_i8(q8_code(v[0], d), q8_code(v[2], d), q8_code(v[4], d),
-                                 q8_code(v[6], d));
-            w[2 * g8 + 1] = pack4_i8(q8_code(v[1], d), q8_code(v[3], d), q8_code(v[5], d),
-                                     q8_code(v[7], d));
-        }
-        uint4* o = reinterpret_cast<uint4*>(a.qh + (int64_t)(s0 + j) * I + rt * kRows + 32 * kb);
-        o[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        o[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        for (int i = 0; i < 8; ++i)
+            w[i] = pack4_i8(q8_code(hv[act_elem<F::Layout>(4 * i)], d),
+                            q8_code(hv[act_elem<F::Layout>(4 * i + 1)], d),
+                            q8_code(hv[act_elem<F::Layout>(4 * i + 2)], d),
+                            q8_code(hv[act_elem<F::Layout>(4 * i + 3)], d));
+        v4u* o = reinterpret_cast<v4u*>(a.qh + (int64_t)(s0 + j) * I + rt * kRows + 32 * kb);
+        o[0] = v4u{w[0], w[1], w[2], w[3]};
+        o[1] = v4u{w[4], w[5], w[6], w[7]};
         a.dh[(int64_t)(s0 + j) * (I >> 5) + rt * 2 + kb] = d;
     }
 }
 
 // K loop of the down kernel (as gateup_loop, one weight matrix).
-template <int NG>
-__device__ __forceinline__ void down_loop(const Stager<16>& st, const ActStager& as, uint8_t* lds,
+template <int BITS, int NG>
+__device__ __forceinline__ void down_loop(const Stager<16, BITS>& st,
+                                          const ActStager<WFmt<BITS>::CH>& as, uint8_t* lds,
                                           uint8_t* act, float* dbuf, double (&acc)[2][4],
                                           int BI, int q, int lr) {
+    typedef WFmt<BITS> F;
+    constexpr int CH = F::CH;
 #pragma unroll
     for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[g][i] = 0.0;
     const v4i zero = {0, 0, 0, 0};
-    const int nch = (BI + kChunk - 1) / kChunk;
-    v4u wv[4], av[4];
+    const int nch = (BI + CH - 1) / CH;
+    typename Stager<16, BITS>::piece_t wv[4];
+    v4u av[ActStager<CH>::NP];
     float adv[4];
-    st.issue(0, BI, wv);
+    st.issue(0, wv);
     as.issue(0, BI, av, adv);
     st.commit(lds, wv);
     as.commit(0, BI, act, dbuf, av, adv);
@@ -307,16 +373,17 @@ __device__ __forceinline__ void down_loop(const Stager<16>& st, const ActStager&
         // unconditional (keeps the staging registers out of memory); after
         // the last chunk this re-reads that chunk, from cache
         const int cn = min(c + 1, nch - 1);
-        st.issue(cn, BI, wv);
+        st.issue(cn, wv);
         as.issue(cn, BI, av, adv);
 #pragma unroll
-        for (int bi = 0; bi < kChunk; ++bi) {
-            const long aw = a_operand(lds_u32(lds + lr * kPitch + bi * 16 + 4 * q));
+        for (int bi = 0; bi < CH; ++bi) {
+            const long aw = a_op<BITS>(lds + lr * F::Pitch + bi * F::WB, q);
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
                 const int j = 16 * g + lr;
-                const long bv = *reinterpret_cast<const long*>(act + j * kActPitch + bi * 32 + 8 * q);
-                const double dd = (double)dbuf[j * kDPitch + bi];
+                const long bv =
+                    *reinterpret_cast<const long*>(act + j * F::ActPitch + bi * 32 + 8 * q);
+                const double dd = (double)dbuf[j * F::DPitch + bi];
                 const v4i cd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw, bv, zero, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -334,9 +401,11 @@ __device__ __forceinline__ void down_loop(const Stager<16>& st, const ActStager&
 
 // Down projection for one item and 64 output rows: ye[slot, row] =
 // fp32(s_down[row] * sum_b d_h,b * I_b).
+template <int BITS>
 __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
-    constexpr int kW = 16 * kPitch;
-    __shared__ __align__(16) uint8_t smem[4 * kW + kActBytes + kDBytes];
+    typedef WFmt<BITS> F;
+    constexpr int kW = 16 * F::Pitch;
+    __shared__ __align__(16) uint8_t smem[4 * kW + F::ActBytes + F::DBytes];
     const int nrt = a.H / kRows;
     const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
     if (it >= *a.n_items) return;
@@ -346,27 +415,30 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, q = lane >> 4;
     const int ng = (n + 15) >> 4;
-    const uint8_t* down = a.eq + (int64_t)e * a.blob_q + (int64_t)I * H;
+    const int64_t rowb = (int64_t)I * BITS / 8;
+    const uint8_t* down = a.eq + (int64_t)e * a.blob_q + 2 * (int64_t)H * I * BITS / 8;
     const int r0 = rt * kRows + wave * 16;
     uint8_t* lds = smem + wave * kW;
     uint8_t* act = smem + 4 * kW;
-    float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + kActBytes);
+    float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + F::ActBytes);
+    static_assert(F::ActBytes >= kTok * (kRows + 1) * 4, "y reuses the activation area");
 
-    Stager<16> st;
-    st.stride = I >> 1;
-    st.base[0] = down + (int64_t)(r0 + q) * (I >> 1);
+    Stager<16, BITS> st;
+    st.stride = rowb;
+    st.rowb = (int)rowb;
+    st.base[0] = down + (int64_t)(r0 + q) * rowb;
     // the item's slots are consecutive rows of q_h
     __shared__ int s_rows[kTok];
     if (threadIdx.x < kTok) s_rows[threadIdx.x] = s0 + threadIdx.x;
     __syncthreads();
-    ActStager as;
+    ActStager<F::CH> as;
     as.init(a.qh, a.dh, I, BI, s_rows, n);
 
     double acc[2][4];
     if (ng == 1)
-        down_loop<1>(st, as, lds, act, dbuf, acc, BI, q, lr);
+        down_loop<BITS, 1>(st, as, lds, act, dbuf, acc, BI, q, lr);
     else
-        down_loop<2>(st, as, lds, act, dbuf, acc, BI, q, lr);
+        down_loop<BITS, 2>(st, as, lds, act, dbuf, acc, BI, q, lr);
     __syncthreads();  // the activation area is reused for y below
     float (*ybuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(act);
 
@@ -376,8 +448,8 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
         const int rl = wave * 16 + 4 * q + i;
         const float dsr = ds[rt * kRows + rl];
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
-            ybuf[16 * g + lr][rl] = (float)((double)dsr * (acc[g][i] * 0.0625));  // undo x16
+        for (int g = 0; g < 2; ++g)  // undo the multiplier of the weight codes
+            ybuf[16 * g + lr][rl] = (float)((double)dsr * (acc[g][i] * F::InvScale));
     }
     __syncthreads();
     for (int v = threadIdx.x; v < n * kRows; v += 256) {

@@ -6,9 +6,11 @@
 
 // Q8_0 over blocks of 32 consecutive fp32 values (a [T, dim] row-major array
 // is a flat run of T*dim/32 blocks). Four lanes share a block, eight values
-// each; the block max is a 2-step butterfly. PERM stores each group of 8 as
-// (e0,e2,e4,e6,e1,e3,e5,e7), the order the int4 dot kernels consume.
-template <bool PERM>
+// each; the block max is a 2-step butterfly. LAYOUT 0 keeps the natural
+// order (int8 weights); 1 stores each group of 8 as (e0,e2,e4,e6,e1,e3,e5,e7),
+// the order the int4 dot kernels consume; 2 each group of 16 as (e0,e4,e8,
+// e12,e1,e5,e9,e13,e2,e6,e10,e14,e3,e7,e11,e15), the int2 order.
+template <int LAYOUT>
 __global__ __launch_bounds__(256) void k_quant_q8(const float* __restrict__ x, int64_t nblk,
                                                   int8_t* __restrict__ q, float* __restrict__ d) {
     const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -33,11 +35,28 @@ __global__ __launch_bounds__(256) void k_quant_q8(const float* __restrict__ x, i
     int c[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) c[i] = q8_code(v[i], dd);
+    // LAYOUT 2: a 16-element group spans this lane (part even: elements
+    // 0..7, odd: 8..15) and its neighbour; the group's order is (e0 e4 e8 e12
+    // e1 e5 e9 e13 | e2 e6 e10 e14 e3 e7 e11 e15), the even part writing the
+    // first eight bytes
+    int p[8];
+    if (LAYOUT == 2) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = __shfl_xor(c[i], 1, 64);
+    }
     if (blk < nblk) {
         uint2 o;
-        if (PERM) {
+        if (LAYOUT == 1) {
             o.x = pack4_i8(c[0], c[2], c[4], c[6]);
             o.y = pack4_i8(c[1], c[3], c[5], c[7]);
+        } else if (LAYOUT == 2) {
+            if ((part & 1) == 0) {
+                o.x = pack4_i8(c[0], c[4], p[0], p[4]);
+                o.y = pack4_i8(c[1], c[5], p[1], p[5]);
+            } else {
+                o.x = pack4_i8(p[2], p[6], c[2], c[6]);
+                o.y = pack4_i8(p[3], p[7], c[3], c[7]);
+            }
         } else {
             o.x = pack4_i8(c[0], c[1], c[2], c[3]);
             o.y = pack4_i8(c[4], c[5], c[6], c[7]);
@@ -54,10 +73,24 @@ __device__ __forceinline__ int int4_code(float w, float s) {
     return (int)r;
 }
 
-// One workgroup per row: block max |w|, s = max/7, then 4 codes -> 2 bytes per lane.
-__global__ __launch_bounds__(256) void k_pack_int4(const float* __restrict__ w, int64_t cols,
+// Symmetric BITS-wide code of w under row scale s: clamp(rint(w / s), +-Q),
+// Q = 2^(BITS-1) - 1; 0 when s = 0.
+template <int BITS>
+__device__ __forceinline__ int wcode(float w, float s) {
+    constexpr float Q = (float)((1 << (BITS - 1)) - 1);
+    if (s == 0.0f) return 0;
+    float r = __builtin_rintf(w / s);
+    r = fminf(fmaxf(r, -Q), Q);
+    return (int)r;
+}
+
+// One workgroup per row: block max |w|, s = max / Q, then 4 codes per lane
+// packed little end first (int4: 2 bytes, int8: 4 bytes, int2: 1 byte).
+template <int BITS>
+__global__ __launch_bounds__(256) void k_pack_bits(const float* __restrict__ w, int64_t cols,
                                                    uint8_t* __restrict__ q,
                                                    float* __restrict__ scale) {
+    constexpr uint32_t M = (1u << BITS) - 1u;
     __shared__ float red[4];
     const int64_t r = blockIdx.x;
     const float* row = w + r * cols;
@@ -71,16 +104,19 @@ __global__ __launch_bounds__(256) void k_pack_int4(const float* __restrict__ w, 
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = amax / 7.0f;
+    const float s = amax / (float)((1 << (BITS - 1)) - 1);
     if (tid == 0) scale[r] = s;
-    uint8_t* out = q + r * (cols / 2);
+    uint8_t* out = q + r * (cols * BITS / 8);
     for (int64_t j = (int64_t)tid * 4; j < cols; j += 1024) {
         const float4 v = *reinterpret_cast<const float4*>(row + j);
-        const uint32_t b = (uint32_t)(int4_code(v.x, s) & 0xF) |
-                           ((uint32_t)(int4_code(v.y, s) & 0xF) << 4) |
-                           ((uint32_t)(int4_code(v.z, s) & 0xF) << 8) |
-                           ((uint32_t)(int4_code(v.w, s) & 0xF) << 12);
-        *reinterpret_cast<uint16_t*>(out + j / 2) = (uint16_t)b;
+        const uint32_t b = ((uint32_t)wcode<BITS>(v.x, s) & M) |
+                           (((uint32_t)wcode<BITS>(v.y, s) & M) << BITS) |
+                           (((uint32_t)wcode<BITS>(v.z, s) & M) << (2 * BITS)) |
+                           (((uint32_t)wcode<BITS>(v.w, s) & M) << (3 * BITS));
+        uint8_t* o = out + j * BITS / 8;
+        if (BITS == 8) *reinterpret_cast<uint32_t*>(o) = b;
+        else if (BITS == 4) *reinterpret_cast<uint16_t*>(o) = (uint16_t)b;
+        else *o = (uint8_t)b;
     }
 }
 
@@ -114,7 +150,7 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
 }
 
 // FP8 -> fp32 -> int4 for one row per workgroup: w = e4m3(q8) * bs[r/128][c/128]
-// (one fp32 rounding), then the pack of k_pack_int4. Four codes per thread.
+// (one fp32 rounding), then the pack of k_pack_bits<4>. Four codes per thread.
 __global__ __launch_bounds__(256) void k_pack_fp8_int4(const uint8_t* __restrict__ q8,
                                                        const float* __restrict__ bs,
                                                        int64_t cols, uint8_t* __restrict__ q,

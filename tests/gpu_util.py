@@ -16,9 +16,20 @@ def unperm8(q: np.ndarray) -> np.ndarray:
     return out.reshape(q.shape)
 
 
-def lib_cfg(C, cfg, n_group=1, topk_group=1):
+def unperm16(q: np.ndarray) -> np.ndarray:
+    """Undo the int2 weights' 16-group order (e0,e4,e8,e12,e1,...,e15) along the last axis."""
+    q = np.asarray(q)
+    g = q.reshape(*q.shape[:-1], -1, 4, 4)          # [..., groups, a, b] holds element 4b + a
+    return np.swapaxes(g, -1, -2).reshape(q.shape)
+
+
+def unperm_for(bits):
+    return {4: unperm8, 8: lambda q: np.asarray(q), 2: unperm16}[bits]
+
+
+def lib_cfg(C, cfg, n_group=1, topk_group=1, bits=4):
     return C.make_cfg(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
-                      cfg.norm_topk, cfg.rho, n_group, topk_group)
+                      cfg.norm_topk, cfg.rho, n_group, topk_group, bits)
 
 
 def gpu_layer(C, cfg, layer=0):
@@ -37,7 +48,7 @@ def layer_input(ref, cfg, layer=0, n_tok=None, first_tok=0):
 
 
 def oracle_layer_for(ref, cfg, layer, x, forced_idx=None, draw_device="cuda", n_group=1,
-                     topk_group=1):
+                     topk_group=1, bits=4):
     """OracleLayer holding only the experts that tokens x select (plus shared),
     each drawn as fp32 by coli_synth (on draw_device, bit-identical to the CPU
     draw) and packed by the oracle."""
@@ -49,11 +60,11 @@ def oracle_layer_for(ref, cfg, layer, x, forced_idx=None, draw_device="cuda", n_
         idx = forced_idx
     need = sorted(set(int(e) for e in np.unique(idx)) | ({cfg.n_experts} if cfg.n_shared else set()))
     L = ref.OracleLayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
-                        cfg.norm_topk, cfg.rho, wr, b, {}, n_group, topk_group)
+                        cfg.norm_topk, cfg.rho, wr, b, {}, n_group, topk_group, bits)
     for e in need:
         mats = [cs.expert_matrix(cfg, layer, e, w, draw_device).cpu().numpy()
                 for w in ("gate", "up", "down")]
-        L.add_expert(e, ref.pack_expert(*mats))
+        L.add_expert(e, ref.pack_expert(*mats, bits=bits))
     return L
 
 

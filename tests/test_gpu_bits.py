@@ -1,0 +1,153 @@
+"""GPU parity of the int8 and int2 weight formats (coli_pack_weights, and the
+layer on the grouped MFMA kernels, which serve every token count for these
+widths): packing bit-exact; Q8_0(x) codes in each width's element order,
+per-block gate dots bit-exact through the debug tap; Q8_0(h) codes equal;
+outputs within 1e-4 rel-L2 of the oracle (tiny workload on every token; full
+decode and prefill shapes on sampled tokens)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import coli_synth as cs
+from gpu_util import layer_input, lib_cfg, oracle_layer_for, rel_l2, unperm_for
+
+pytestmark = pytest.mark.gpu
+
+TOL_REL_L2 = 1e-4
+
+
+@pytest.fixture(scope="module")
+def C():
+    import int4_quantized_moe_sigmoid_amd as C
+    assert torch.cuda.is_available()
+    return C
+
+
+def _note(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 256), (2048, 6144), (6144, 2048)])
+def test_pack_weights_bit_exact(C, ref, bits, rows, cols):
+    _note("pack", bits, rows, cols)
+    w = (cs.normal(cs.stream_key(31 + bits, rows, cs.T_X), (rows, cols), 0.02).numpy())
+    w[rows // 2] = 0.0
+    q = torch.empty((rows, cols * bits // 8), dtype=torch.uint8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    C.coli_pack_weights(torch.from_numpy(w).cuda(), bits, q, s)
+    torch.cuda.synchronize()
+    rq, rs = ref.pack_weights(w, bits)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+def _layer(C, cfg, bits):
+    wr, b, q, s = cs.build_layer(cfg, 0, "cuda",
+                                 lambda w, qv, sv: C.coli_pack_weights(w, bits, qv, sv), bits=bits)
+    return C.LayerWeights(lib_cfg(C, cfg, bits=bits), wr, b, q, s)
+
+
+def _run(C, W, x):
+    T = x.shape[0]
+    lc = W.cfg
+    fl = C.COLI_FWD_DEBUG_TAPS
+    ws = torch.empty(C.coli_moe_workspace_bytes(lc, T, fl), dtype=torch.uint8, device="cuda")
+    y = torch.empty((T, lc.hidden), dtype=torch.float32, device="cuda")
+    C.coli_moe_forward(W, torch.from_numpy(x).cuda(), y, ws, fl)
+    torch.cuda.synchronize()
+    L = C.coli_moe_workspace_layout(lc, T, fl)
+    wsn = ws.cpu().numpy()
+    H, I, K, S = lc.hidden, lc.inter, lc.top_k, lc.n_shared
+
+    def arr(off, dtype, shape):
+        n = int(np.prod(shape))
+        return np.frombuffer(wsn[off:off + n * np.dtype(dtype).itemsize].tobytes(),
+                             dtype=dtype).reshape(shape)
+    NS = int(L.n_slots)
+    un = unperm_for(lc.weight_bits)
+    return y.cpu().numpy(), {
+        "qx": un(arr(L.qx, np.int8, (T, H))), "dx": arr(L.dx, np.float32, (T, H // 32)),
+        "idx": arr(L.topk_idx, np.int32, (T, K)), "w": arr(L.topk_w, np.float32, (T, K)),
+        "slot_of": arr(L.slot_of, np.int32, (T, K + S)),
+        "qh": un(arr(L.qh, np.int8, (NS, I))), "dh": arr(L.dh, np.float32, (NS, I // 32)),
+        "tap": arr(L.tap, np.int32, (NS, int(L.tap_rows), H // 32)),
+        "tap_stride": int(L.tap_stride)}
+
+
+def _compare(ref, cfg, bits, x, y, taps, tokens):
+    OL = oracle_layer_for(ref, cfg, 0, x[tokens], bits=bits)
+    xs = x[tokens]
+    yo, to = OL.forward(xs, taps=True)
+    np.testing.assert_array_equal(taps["qx"][tokens], to["qx"])
+    np.testing.assert_array_equal(taps["dx"][tokens], to["dx"])
+    K, S, H, I = cfg.top_k, cfg.n_shared, cfg.hidden, cfg.inter
+    flips = 0
+    for j, t in enumerate(tokens):
+        assert list(taps["idx"][t]) == list(to["idx"][j])
+        np.testing.assert_allclose(taps["w"][t], to["w"][j], rtol=1e-6)
+        for k in range(K + S):
+            sl = taps["slot_of"][t, k]
+            flips += int(np.sum(taps["qh"][sl] != to["qh"][j, k]))
+            e = int(taps["idx"][t, k]) if k < K else cfg.n_experts
+            rows = np.arange(0, I, taps["tap_stride"])
+            want = ref.block_dots(OL.experts[e]["gate_q"][rows], H, to["qx"][j:j + 1], bits)[0]
+            np.testing.assert_array_equal(taps["tap"][sl][:len(rows)], want)
+    err = rel_l2(y[tokens], yo)
+    _note("rel_l2", err, "q_h flips", flips)
+    assert err <= TOL_REL_L2
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("n_tok", [1, 2, 5, 33])
+def test_tiny_layer_every_token(C, ref, bits, n_tok):
+    cfg = cs.with_tokens(cs.CONFIGS[0], n_tok)
+    _note("tiny", bits, n_tok)
+    W = _layer(C, cfg, bits)
+    x = layer_input(ref, cfg)
+    y, taps = _run(C, W, x)
+    _compare(ref, cfg, bits, x, y, taps, list(range(n_tok)))
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("cid,n_tok,sample", [(1, 1, None), (3, 512, 4)])
+def test_full_size_layers(C, ref, bits, cid, n_tok, sample):
+    cfg = cs.with_tokens(cs.CONFIGS[cid], n_tok)
+    _note("full", bits, cfg.name, n_tok)
+    W = _layer(C, cfg, bits)
+    x = layer_input(ref, cfg)
+    y, taps = _run(C, W, x)
+    tokens = list(range(n_tok)) if sample is None else \
+        sorted(set(np.random.RandomState(9).choice(n_tok, sample, replace=False).tolist()) |
+               {0, n_tok - 1})
+    _compare(ref, cfg, bits, x, y, taps, tokens)
+    del W
+    torch.cuda.empty_cache()
+
+
+def test_rejects_unsupported_widths(C):
+    cfg = dataclasses.replace(cs.CONFIGS[0], hidden=288, n_tok=1)  # 288 = 9 x 32, not 64k
+    for bits, code in [(8, C.COLI_E_UNSUPPORTED), (3, C.COLI_E_INVAL)]:
+        lc = lib_cfg(C, cfg, bits=bits)
+        n = cfg.n_experts + cfg.n_shared
+        wb = 8 if bits == 3 else bits
+        q = torch.zeros(n * 3 * cfg.inter * cfg.hidden * wb // 8, dtype=torch.uint8, device="cuda")
+        s = torch.zeros(n * (2 * cfg.inter + cfg.hidden), dtype=torch.float32, device="cuda")
+        wr = torch.zeros((cfg.n_experts, cfg.hidden), device="cuda")
+        b = torch.zeros(cfg.n_experts, device="cuda")
+        if bits == 3:
+            with pytest.raises(Exception):
+                C.LayerWeights(lc, wr, b, q, s)
+            continue
+        W = C.LayerWeights(lc, wr, b, q, s)
+        ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+        y = torch.empty((1, cfg.hidden), device="cuda")
+        with pytest.raises(C.ColiError) as ei:
+            C.coli_moe_forward(W, torch.zeros((1, cfg.hidden), device="cuda"), y, ws)
+        assert ei.value.code == code
+    w = torch.zeros((2, 64), device="cuda")
+    with pytest.raises(C.ColiError):
+        C.coli_pack_weights(w, 3, torch.empty((2, 32), dtype=torch.uint8, device="cuda"),
+                            torch.empty(2, device="cuda"))
