@@ -32,9 +32,9 @@ HBM_PEAK_GBPS = 8000.0
 # workload); dropped whenever that kernel changes.
 TRAFFIC = {
     # profiles/dec_kernels_decode_T1.txt
-    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55685.5 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55678.7 * 2 + 38.4) * 1024,
     # profiles/pf_kernels_prefill_T512.txt
-    ("pf_gateup", "prefill T512 zipf-bias"): (1750193.6 * 2 + 14446.1) * 1024,
+    ("pf_gateup", "prefill T512 zipf-bias"): (1749219.2 * 2 + 14454.1) * 1024,
     # profiles/pack_fp8_int4_layer.txt (the gate/up launch)
     ("pack_fp8_gateup", "pack_fp8 layer H6144 I2048 experts257"): (3164334.8 * 2 + 3166240.7) * 1024,
 }
@@ -334,8 +334,8 @@ def gateup_roofline(kern, cfg, gate_up_bytes, T, bits=4):
 
 def run_sweep(args, cfg, counts):
     """Layer time against the number of tokens per call, on the weights and
-    input recipe of `cfg` (the few-token kernels serve T <= 3, the grouped
-    MFMA kernels T >= 4)."""
+    input recipe of `cfg` (the few-token kernels serve T <= 4 with int4
+    weights, the grouped MFMA kernels the rest)."""
     import torch
 
     import coli_synth as cs
@@ -378,7 +378,7 @@ def run_sweep(args, cfg, counts):
         uniq = int((cnt[:E] > 0).sum().item()) + S
         print(json.dumps({"sweep": cfg.name, "tokens": T, "us_per_call": round(dt * 1e6, 2),
                           "tokens_per_s": round(T / dt, 1), "experts_in_use": uniq,
-                          "path": "few-token" if T <= 3 and bits == 4 else "grouped-mfma",
+                          "path": "few-token" if T <= 4 and bits == 4 else "grouped-mfma",
                           "weight_bits": bits,
                           "expert_weight_gbps": round(
                               uniq * (3 * I * H * bits // 8 + 4 * (2 * I + H)) / dt / 1e9, 1)}),

@@ -221,7 +221,7 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
 // Few-token path: three fused kernels (k_decode.h). Shapes it covers:
 // hidden <= 6144, intermediate <= 2048, <= 256 routed experts.
 bool small_path_fits(const coli_moe_cfg& c, int64_t T) {
-    return weight_bits(c) == 4 && T <= 3 && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
+    return weight_bits(c) == 4 && T <= 4 && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
            c.inter <= 2048 && c.inter % 64 == 0 && c.n_experts <= 256;
 }
 

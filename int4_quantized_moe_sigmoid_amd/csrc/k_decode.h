@@ -43,8 +43,13 @@ __device__ __forceinline__ double wave_reduce_tr(double* v, int lane) {
         const bool upper = (lane & mask) != 0;
 #pragma unroll
         for (int i = 0; i < h / 2; ++i) {
-            const double keep = upper ? v[i + h / 2] : v[i];
-            const double send = upper ? v[i] : v[i + h / 2];
+            // the two candidates pass through an empty asm, so the compiler
+            // cannot turn the lane-dependent choice into an array access with
+            // a per-lane index (which puts the array in scratch memory)
+            double lo = v[i], hi = v[i + h / 2];
+            asm volatile("" : "+v"(lo), "+v"(hi));
+            const double keep = upper ? hi : lo;
+            const double send = upper ? lo : hi;
             v[i] = keep + __shfl_xor(send, mask, 64);
         }
         ++step;
