@@ -62,7 +62,7 @@ GroupSel group_sel(const coli_moe_cfg& c) {
 
 struct Layout {
     coli_moe_ws_layout pub;
-    size_t lists, items, n_items, uinfo, rpart;
+    size_t lists, items, n_items, uinfo, rpart, sig;
     int64_t max_items;
     int ch;
 };
@@ -102,6 +102,7 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
     L->n_items = take(4);
     L->uinfo = take(4 * (1 + 4 * dec::kMaxEntries + 64));
     L->rpart = take(T > 8 ? (size_t)kMaxRouterSplit * T * E * 8 : 0);
+    L->sig = take(T <= dec::kMaxTok ? (size_t)2 * T * E * 8 : 0);  // s and c of the few-token path
 
     P.qh = take(NS * I);
     P.dh = take(NS * (I / 32) * 4);
@@ -320,6 +321,8 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         a.logits = logits; a.qx = qx; a.dx = dx; a.idx = idx; a.wts = wts; a.counts = counts;
         a.offs = offs; a.slot_of = slot_of; a.slot_tok = slot_tok;
         a.uinfo = reinterpret_cast<int32_t*>(base + L.uinfo);
+        a.sig = reinterpret_cast<double*>(base + L.sig);
+        a.cval = a.sig + T * E;
         a.qh = qh; a.dh = dh; a.tap = tap;
         a.tap_rows = (int)L.pub.tap_rows;
         a.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);

@@ -143,7 +143,7 @@ __device__ __forceinline__ void top2_lanes(double& a, double& b, int n) {
 // least the smallest of the 32-expert group maxima can be among the K largest
 // (when there are >= K groups those maxima are >= K distinct experts), so
 // positions are counted among those few candidates only.
-__device__ __forceinline__ void topk_wg(const double* logits, const float* bias, int T, int E, int K,
+__device__ __forceinline__ void topk_wg(const double* sig, const double* cval, int T, int E, int K,
                                         int norm, double rho, GroupSel gsel, Route& R,
                                         TopkScratch& Z) {
     const int e = threadIdx.x;
@@ -153,23 +153,18 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
     if (threadIdx.x < kMaxTok * 8) (&Z.gmax[0][0])[threadIdx.x] = 0ull;
     if (threadIdx.x < kMaxTok * 32) (&Z.gmax8[0][0])[threadIdx.x] = 0ull;
     if (threadIdx.x < kMaxTok) Z.ncand[threadIdx.x] = 0;
-    double l[kMaxTok];
-    float bb = 0.0f;
-#pragma unroll
-    for (int t = 0; t < kMaxTok; ++t) l[t] = (t < T && e < E) ? logits[(int64_t)t * E + e] : 0.0;
-    if (e < E) bb = bias[e];
-    __syncthreads();
-    unsigned long long key[kMaxTok];
-    double s[kMaxTok];
+    // sigmoid s and selection score c = s + bias, from the router kernel
+    double s[kMaxTok], cs[kMaxTok];
 #pragma unroll
     for (int t = 0; t < kMaxTok; ++t) {
-        s[t] = 0.0;
-        key[t] = 0ull;
-        if (t < T) {  // uniform: no fp64 exp for absent tokens
-            s[t] = 1.0 / (1.0 + exp(-l[t]));
-            key[t] = e < E ? order_key(s[t] + (double)bb) : 0ull;
-        }
+        const bool in = t < T && e < E;
+        s[t] = in ? sig[(int64_t)t * E + e] : 0.0;
+        cs[t] = in ? cval[(int64_t)t * E + e] : 0.0;
     }
+    __syncthreads();
+    unsigned long long key[kMaxTok];
+#pragma unroll
+    for (int t = 0; t < kMaxTok; ++t) key[t] = (t < T && e < E) ? order_key(cs[t]) : 0ull;
     // group-limited selection: the experts of dropped groups get key 0 (below
     // every real key). With groups of 2..64 experts (a power of two: a group
     // never straddles a wave) the group maxima come from lane shuffles, and the
@@ -183,7 +178,7 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
 #pragma unroll
             for (int t = 0; t < kMaxTok; ++t) {
                 if (t < T) {  // uniform
-                    double a = e < E ? s[t] + (double)bb : -__builtin_inf(), b2 = -__builtin_inf();
+                    double a = e < E ? cs[t] : -__builtin_inf(), b2 = -__builtin_inf();
                     top2_lanes(a, b2, gsel.gs);
                     if (e < E && (e & (gsel.gs - 1)) == 0) {
                         Z.cs[t][e / gsel.gs] = a + b2;  // group score (cs is free until later)
@@ -214,7 +209,7 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
         } else {
 #pragma unroll
             for (int t = 0; t < kMaxTok; ++t)
-                if (t < T && e < E) Z.cs[t][e] = s[t] + (double)bb;
+                if (t < T && e < E) Z.cs[t][e] = cs[t];
             __syncthreads();
             if (wv < T) {
                 const unsigned long long keep = group_keep_mask(Z.cs[wv], gsel);
@@ -325,9 +320,9 @@ __device__ __forceinline__ void topk_wg(const double* logits, const float* bias,
 
 // Fills R (in LDS) for T tokens; must be called by the whole workgroup
 // (blockDim.x >= E).
-__device__ __forceinline__ void route_small(const double* logits, const float* bias, int T, int E, int K, int S,
+__device__ __forceinline__ void route_small(const double* sig, const double* cval, int T, int E, int K, int S,
                             int norm, double rho, GroupSel gsel, Route& R, TopkScratch& Z) {
-    topk_wg(logits, bias, T, E, K, norm, rho, gsel, R, Z);
+    topk_wg(sig, cval, T, E, K, norm, rho, gsel, R, Z);
     __syncthreads();
     // entries j = t K + k in (token, k) order; entry j belongs to an earlier
     // token than entry i exactly when j < t_i K
@@ -392,6 +387,22 @@ __device__ __forceinline__ void route_small(const double* logits, const float* b
     __syncthreads();
 }
 
+// Cross-lane moves of 64-bit values without LDS: a DPP move (CTRL: quad
+// permute, half-row or row mirror) or a read of one lane into all lanes.
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long v) {
+    const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)v, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((unsigned long long)(unsigned)hi << 32) | (unsigned)lo;
+}
+__device__ __forceinline__ unsigned long long readlane64(unsigned long long v, int l) {
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)v, l);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(v >> 32), l);
+    return ((unsigned long long)hi << 32) | lo;
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E;  // quad permutes [1,0,3,2], [2,3,0,1]
+constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141;
+
 // Routing of a single token by one wave (wave 0), the other waves waiting
 // at one barrier; same selection rule and results as route_small. Lane L
 // holds experts 4L .. 4L+3 (E <= 256). The smallest of the 32-expert group
@@ -399,7 +410,7 @@ __device__ __forceinline__ void route_small(const double* logits, const float* b
 // above it are compacted into LDS with ballots and ranked by who is ahead
 // (c descending, index ascending). All LDS traffic stays within the wave,
 // whose LDS operations complete in program order.
-__device__ __forceinline__ void route_one(const double* logits, const float* bias, int E, int K,
+__device__ __forceinline__ void route_one(const double* sig, const double* cval, int E, int K,
                                           int S, int norm, double rho, GroupSel gsel, Route& R,
                                           TopkScratch& Z) {
     const int lane = threadIdx.x & 63;
@@ -411,11 +422,10 @@ __device__ __forceinline__ void route_one(const double* logits, const float* bia
         for (int j = 0; j < 4; ++j) {
             const int e = 4 * lane + j;
             ok[j] = e < E;
-            const double l = ok[j] ? logits[e] : 0.0;
-            const float b = ok[j] ? bias[e] : 0.0f;
-            sv[j] = 1.0 / (1.0 + exp(-l));
-            key[j] = ok[j] ? order_key(sv[j] + (double)b) : 0ull;
-            cv[j] = ok[j] ? sv[j] + (double)b : -__builtin_inf();
+            sv[j] = ok[j] ? sig[e] : 0.0;
+            const double c = ok[j] ? cval[e] : 0.0;
+            key[j] = ok[j] ? order_key(c) : 0ull;
+            cv[j] = ok[j] ? c : -__builtin_inf();
         }
         // group-limited selection: the experts of dropped groups leave the race.
         // Groups of 4 lpg experts (lpg a power of two: whole lanes) take their
@@ -473,29 +483,39 @@ __device__ __forceinline__ void route_one(const double* logits, const float* bia
         // the smallest maximum of >= K non-empty expert groups bounds the K-th
         // largest key from below: 32-expert groups (8 lanes), else with groups
         // 8-expert groups (2 lanes)
+        // the smallest maximum of >= K non-empty expert groups bounds the K-th
+        // largest key from below: 32-expert groups (8 lanes), else with groups
+        // 8-expert groups (2 lanes). Group maxima by DPP moves (quad permutes,
+        // then the half-row mirror pairs the two quads of 8 lanes), the
+        // minimum by the row mirror (two groups of a 16-lane row) and one read
+        // of each row.
         const int G = (E + 31) >> 5, G8 = (E + 7) >> 3;
         unsigned long long thr = gthr;
         const unsigned long long m4 = max(max(key[0], key[1]), max(key[2], key[3]));
+        const unsigned long long q2 = max(m4, dpp64<kDppXor1>(m4));  // 2-lane maxima
         if (thr == 0ull && G >= K) {
-            unsigned long long gm = m4;
-#pragma unroll
-            for (int o = 1; o < 8; o <<= 1) gm = max(gm, (unsigned long long)__shfl_xor(gm, o, 64));
+            unsigned long long gm = max(q2, dpp64<kDppXor2>(q2));
+            gm = max(gm, dpp64<kDppHalfMirror>(gm));
             const bool live = (lane >> 3) < G && gm != 0ull;
             const int cnt = __popcll(__ballot(live && (lane & 7) == 0));
-            if (!live) gm = ~0ull;  // no (eligible) experts in this group
-#pragma unroll
-            for (int o = 8; o < 64; o <<= 1) gm = min(gm, (unsigned long long)__shfl_xor(gm, o, 64));
-            if (cnt >= K) thr = gm;
+            unsigned long long v = live ? gm : ~0ull;  // no (eligible) experts in this group
+            v = min(v, dpp64<kDppRowMirror>(v));
+            v = min(min(readlane64(v, 0), readlane64(v, 16)), min(readlane64(v, 32), readlane64(v, 48)));
+            if (cnt >= K) thr = v;
         }
         if (thr == 0ull && gsel.ng > 1 && G8 >= K) {
-            unsigned long long gm = max(m4, (unsigned long long)__shfl_xor(m4, 1, 64));
-            const bool live = (lane >> 1) < G8 && gm != 0ull;
+            const bool live = (lane >> 1) < G8 && q2 != 0ull;
             const int cnt = __popcll(__ballot(live && (lane & 1) == 0));
-            if (!live) gm = ~0ull;
-#pragma unroll
-            for (int o = 2; o < 64; o <<= 1) gm = min(gm, (unsigned long long)__shfl_xor(gm, o, 64));
-            if (cnt >= K) thr = gm;
+            unsigned long long v = live ? q2 : ~0ull;
+            v = min(v, dpp64<kDppXor2>(v));
+            v = min(v, dpp64<kDppHalfMirror>(v));
+            v = min(v, dpp64<kDppRowMirror>(v));
+            v = min(min(readlane64(v, 0), readlane64(v, 16)), min(readlane64(v, 32), readlane64(v, 48)));
+            if (cnt >= K) thr = v;
         }
+        // candidates (keys at or above the threshold) compacted into LDS, then
+        // each candidate's position = the number of candidates ahead of it (c
+        // descending, index ascending)
         int base = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -510,59 +530,104 @@ __device__ __forceinline__ void route_one(const double* logits, const float* bia
             base += __popcll(bal);
         }
         const int m = base;
-        for (int i = lane; i < m; i += 64) {
-            const unsigned long long ki = Z.ckey[0][i];
-            const int ei = Z.ce[0][i];
+        if (m <= 64) {
+            // one candidate per lane; the others broadcast from their lanes
+            const bool has = lane < m;
+            const unsigned long long ki = has ? Z.ckey[0][lane] : 0ull;
+            const int ei = has ? Z.ce[0][lane] : 0x7fffffff;
+            const double si = has ? Z.cs[0][lane] : 0.0;
             int rank = 0;
-            for (int j0 = 0; j0 < m; j0 += 8) {
-                unsigned long long kj[8];
-                int ej[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = min(j0 + u, m - 1);
-                    kj[u] = Z.ckey[0][j];
-                    ej[u] = Z.ce[0][j];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    rank += (j0 + u < m && (kj[u] > ki || (kj[u] == ki && ej[u] < ei))) ? 1 : 0;
+            for (int j = 0; j < m; ++j) {  // uniform
+                const unsigned long long kj = readlane64(ki, j);
+                const int ej = __builtin_amdgcn_readlane(ei, j);
+                rank += (kj > ki || (kj == ki && ej < ei)) ? 1 : 0;
             }
-            if (rank < K) {
+            const bool sel = has && rank < K;
+            // gate values summed in position order (k ascending)
+            double sum = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const int src = __builtin_ctzll(__ballot(sel && rank == k));
+                const long long sb = (long long)readlane64((unsigned long long)__double_as_longlong(si), src);
+                sum += __longlong_as_double(sb);
+            }
+            // the K experts are distinct: slot = number of chosen experts below
+            const unsigned long long selm = __ballot(sel);
+            int slot = 0;
+            for (unsigned long long mm = selm; mm; mm &= mm - 1ull) {  // uniform, K steps
+                const int ej = __builtin_amdgcn_readlane(ei, __builtin_ctzll(mm));
+                slot += ej < ei ? 1 : 0;
+            }
+            if (sel) {
+                double v = si;
+                if (norm) v = v / sum;
+                v = v * rho;
+                const float w = (float)v;
                 R.idx[0][rank] = ei;
                 R.flat[rank] = ei;
-                Z.ssel[0][rank] = Z.cs[0][i];
+                R.w[0][rank] = w;
+                R.ent_e[slot] = ei;
+                R.ent_t[slot] = 0;
+                R.ent_w[slot] = w;
+                R.slot_of[0][rank] = slot;
+                R.u_e[slot] = ei;
+                R.u_s0[slot] = slot;
+                R.u_n[slot] = 1;
             }
-        }
-        if (lane < K) {
-            double ss[16];
-            int ix[16];
+        } else {
+            for (int i = lane; i < m; i += 64) {
+                const unsigned long long ki = Z.ckey[0][i];
+                const int ei = Z.ce[0][i];
+                int rank = 0;
+                for (int j0 = 0; j0 < m; j0 += 8) {
+                    unsigned long long kj[8];
+                    int ej[8];
 #pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                ss[kk] = Z.ssel[0][min(kk, K - 1)];
-                ix[kk] = R.idx[0][min(kk, K - 1)];
+                    for (int u = 0; u < 8; ++u) {
+                        const int j = min(j0 + u, m - 1);
+                        kj[u] = Z.ckey[0][j];
+                        ej[u] = Z.ce[0][j];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        rank += (j0 + u < m && (kj[u] > ki || (kj[u] == ki && ej[u] < ei))) ? 1 : 0;
+                }
+                if (rank < K) {
+                    R.idx[0][rank] = ei;
+                    R.flat[rank] = ei;
+                    Z.ssel[0][rank] = Z.cs[0][i];
+                }
             }
-            double sum = 0.0;
+            if (lane < K) {
+                double ss[16];
+                int ix[16];
 #pragma unroll
-            for (int kk = 0; kk < 16; ++kk)
-                if (kk < K) sum += ss[kk];  // k ascending
-            double v = Z.ssel[0][lane];
-            if (norm) v = v / sum;
-            v = v * rho;
-            const float w = (float)v;
-            R.w[0][lane] = w;
-            // the K experts are distinct: slot = number of chosen experts below
-            const int e = R.idx[0][lane];
-            int slot = 0;
+                for (int kk = 0; kk < 16; ++kk) {
+                    ss[kk] = Z.ssel[0][min(kk, K - 1)];
+                    ix[kk] = R.idx[0][min(kk, K - 1)];
+                }
+                double sum = 0.0;
 #pragma unroll
-            for (int kk = 0; kk < 16; ++kk)
-                if (kk < K && ix[kk] < e) ++slot;
-            R.ent_e[slot] = e;
-            R.ent_t[slot] = 0;
-            R.ent_w[slot] = w;
-            R.slot_of[0][lane] = slot;
-            R.u_e[slot] = e;
-            R.u_s0[slot] = slot;
-            R.u_n[slot] = 1;
+                for (int kk = 0; kk < 16; ++kk)
+                    if (kk < K) sum += ss[kk];  // k ascending
+                double v = Z.ssel[0][lane];
+                if (norm) v = v / sum;
+                v = v * rho;
+                const float w = (float)v;
+                R.w[0][lane] = w;
+                // the K experts are distinct: slot = number of chosen experts below
+                const int e = R.idx[0][lane];
+                int slot = 0;
+#pragma unroll
+                for (int kk = 0; kk < 16; ++kk)
+                    if (kk < K && ix[kk] < e) ++slot;
+                R.ent_e[slot] = e;
+                R.ent_t[slot] = 0;
+                R.ent_w[slot] = w;
+                R.slot_of[0][lane] = slot;
+                R.u_e[slot] = e;
+                R.u_s0[slot] = slot;
+                R.u_n[slot] = 1;
+            }
         }
         if (lane == 0) {
             R.n_uniq = K;
@@ -584,6 +649,8 @@ struct DecArgs {
     GroupSel gsel;  // group-limited selection (ng <= 1: none)
     // workspace
     double* logits;
+    double* sig;   // [T, E] sigmoid of the logits (written by the router kernel)
+    double* cval;  // [T, E] s + bias, the selection scores
     int8_t* qx;
     float* dx;
     int32_t* idx;
@@ -924,7 +991,14 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
     __syncthreads();
     if (router && (int)threadIdx.x < T) {
         const double* r = red[threadIdx.x];
-        a.logits[(int64_t)threadIdx.x * a.E + e] = (r[0] + r[1]) + (r[2] + r[3]);
+        const double l = (r[0] + r[1]) + (r[2] + r[3]);
+        const int64_t i = (int64_t)threadIdx.x * a.E + e;
+        a.logits[i] = l;
+        // the sigmoid and the selection score once per expert here, not in
+        // every gate/up workgroup
+        const double sg = 1.0 / (1.0 + exp(-l));
+        a.sig[i] = sg;
+        a.cval[i] = sg + (double)a.bias[e];
     }
 }
 
@@ -967,9 +1041,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
         b -= nw;
     }
     if (NT == 1)
-        route_one(a.logits, a.bias, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
+        route_one(a.sig, a.cval, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
     else
-        route_small(a.logits, a.bias, a.T, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
+        route_small(a.sig, a.cval, a.T, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
     if (b == 0) publish_route(a, R);
     const int u = b / nw, hw = b - u * nw;
     if (u >= R.n_uniq) return;
