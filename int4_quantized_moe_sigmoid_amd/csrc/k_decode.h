@@ -1040,10 +1040,14 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
         }
         b -= nw;
     }
+    // the routing waves win issue slots over co-resident streaming waves:
+    // routing latency sits on the path to this workgroup's first weight load
+    __builtin_amdgcn_s_setprio(3);
     if (NT == 1)
         route_one(a.sig, a.cval, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
     else
         route_small(a.sig, a.cval, a.T, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
+    __builtin_amdgcn_s_setprio(0);
     if (b == 0) publish_route(a, R);
     const int u = b / nw, hw = b - u * nw;
     if (u >= R.n_uniq) return;
@@ -1068,137 +1072,156 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
 // ascending expert order with the shared expert last.
 template <int NT, int NBJ, int RPW, int NB>
 __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
-    __shared__ int s_e[kMaxEntries + 1], s_s0[kMaxEntries + 1], s_n[kMaxEntries + 1];
+    __shared__ int s_e[kMaxEntries], s_s0[kMaxEntries], s_n[kMaxEntries];
     __shared__ float s_w[kMaxEntries + kMaxTok];
     __shared__ int s_t[kMaxEntries + kMaxTok];
     __shared__ double s_acc[4 * RPW][NT];
-    __shared__ int s_nu;
     const int T = a.T, K = a.K, E = a.E, S = a.S, H = a.H, I = a.I;
     const int BI = I >> 5;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n_ent = T * K;
-    if (threadIdx.x == 0) {
-        int nu = a.uinfo[0];
-        for (int v = 0; v < nu; ++v) {
-            s_e[v] = a.uinfo[1 + 3 * v];
-            s_s0[v] = a.uinfo[2 + 3 * v];
-            s_n[v] = a.uinfo[3 + 3 * v];
-        }
-        if (S) {
-            s_e[nu] = E;
-            s_s0[nu] = n_ent;
-            s_n[nu] = T;
-            ++nu;
-        }
-        s_nu = nu;
-    }
-    for (int i = threadIdx.x; i < n_ent + S * T; i += 256) {
-        s_w[i] = (i < n_ent) ? reinterpret_cast<const float*>(a.uinfo + kUinfoW)[i] : 1.0f;
-        s_t[i] = a.slot_tok[i];
-    }
-    if (threadIdx.x < 4 * RPW * NT) (&s_acc[0][0])[threadIdx.x] = 0.0;
-    __syncthreads();
     const int c0 = blockIdx.x * (4 * RPW) + wave * RPW;
-    const int nu = __builtin_amdgcn_readfirstlane(s_nu);
     int bcl[NBJ];
 #pragma unroll
     for (int j = 0; j < NBJ; ++j) bcl[j] = min(lane + 64 * j, BI - 1);
     constexpr int V = RPW * NT;
     constexpr int kLog = (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : (V >= 2) ? 1 : 0;
     constexpr int kShift = 6 - kLog;
-    // experts in batches of NB, the next batch's loads issued before the
-    // current batch's arithmetic (two register buffers)
+    // one expert's operands for this wave's rows: weights, Q8_0(h) of its
+    // tokens, row scales
+    struct Operands {
+        uint4 w[RPW][NBJ];
+        uint4 ha[NT][NBJ][2];
+        float hdf[NT][NBJ];
+        float dsv[RPW];
+    };
+    auto load_w = [&](int ev, Operands& o) {
+        const uint8_t* down = a.eq + (int64_t)ev * a.blob_q + (int64_t)I * H;
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int j = 0; j < NBJ; ++j)
+                o.w[r][j] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl[j] * 16);
+    };
+    auto load_h = [&](int ev, int s0, int n, Operands& o) {
+        const float* ds = a.es + (int64_t)ev * a.blob_s + 2 * I;
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) o.dsv[r] = ds[c0 + r];
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int sl = s0 + min(i, n - 1);
+#pragma unroll
+            for (int j = 0; j < NBJ; ++j) {
+                const uint4* p = reinterpret_cast<const uint4*>(a.qh + (int64_t)sl * I + bcl[j] * 32);
+                o.ha[i][j][0] = p[0];
+                o.ha[i][j][1] = p[1];
+                o.hdf[i][j] = a.dh[(int64_t)sl * BI + bcl[j]];
+            }
+        }
+    };
+    // y_e of this wave's rows for the n tokens of one expert, added into
+    // s_acc with the slot weights (callers go in ascending expert order,
+    // the shared expert last)
+    auto compute = [&](const Operands& o, int s0, int n) {
+        double vals[V];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r)
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                double p = 0.0;
+#pragma unroll
+                for (int j = 0; j < NBJ; ++j) {
+                    const bool ok = i < n && lane + 64 * j < BI;
+                    const double hd = ok ? (double)o.hdf[i][j] * 0.0625 : 0.0;
+                    p += hd * (double)dot_block16(o.w[r][j], o.ha[i][j][0], o.ha[i][j][1]);
+                }
+                vals[r * NT + i] = p;
+            }
+        const double sum = wave_reduce_tr<V>(vals, lane);
+        const int vi = lane >> kShift;
+        if (lane == (vi << kShift)) {
+            const int r = vi / NT, i = vi - r * NT;
+            if (i < n) {
+                float dsr = o.dsv[0];
+#pragma unroll
+                for (int rr = 1; rr < RPW; ++rr)
+                    if (r == rr) dsr = o.dsv[rr];
+                const float yv = (float)((double)dsr * sum);
+                s_acc[wave * RPW + r][s_t[s0 + i]] += (double)s_w[s0 + i] * (double)yv;
+            }
+        }
+    };
+    // The published route (routed experts in use, their slots and weights)
+    // comes in one round trip, which the shared expert's loads (its slots
+    // follow the routed ones) overlap; they are issued after it so that the
+    // wait for the route does not also wait for them.
+    // Every load here is unconditional (no branch for the counter wait to
+    // merge over); lanes past the used entries read in-bounds leftovers.
+    const int nr = __builtin_amdgcn_readfirstlane(a.uinfo[0]);
+    const int n_sl = n_ent + S * T;
+    const int ue = a.uinfo[1 + 3 * lane];
+    const int us0 = a.uinfo[2 + 3 * lane];
+    const int un = a.uinfo[3 + 3 * lane];
+    const int ti = threadIdx.x;
+    const float wv = reinterpret_cast<const float*>(a.uinfo + kUinfoW)[min(ti, n_ent - 1)];
+    const int tv = a.slot_tok[min(ti, n_sl - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+    Operands sh;
+    load_w(S ? E : 0, sh);
+    load_h(S ? E : 0, n_ent, T, sh);
+    __builtin_amdgcn_sched_barrier(0);
+    if (wave == 0) {
+        s_e[lane] = ue;
+        s_s0[lane] = us0;
+        s_n[lane] = un;
+    }
+    if (ti < n_sl) {
+        s_w[ti] = (ti < n_ent) ? wv : 1.0f;
+        s_t[ti] = tv;
+    }
+    if (ti < 4 * RPW * NT) (&s_acc[0][0])[ti] = 0.0;
+    __syncthreads();
+    // routed experts in batches of NB, the next batch's loads issued before
+    // the current batch's arithmetic (two register buffers)
     struct Batch {
-        uint4 w[NB][RPW][NBJ];
-        uint4 ha[NB][NT][NBJ][2];
-        float hdf[NB][NT][NBJ];
-        float dsv[NB][RPW];
+        Operands o[NB];
     };
     auto load = [&](int v0, Batch& bt) {
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi) {
-            const int v = min(v0 + bi, nu - 1);
-            const int ev = __builtin_amdgcn_readfirstlane(s_e[v]);
-            const uint8_t* down = a.eq + (int64_t)ev * a.blob_q + (int64_t)I * H;
-#pragma unroll
-            for (int r = 0; r < RPW; ++r)
-#pragma unroll
-                for (int j = 0; j < NBJ; ++j)
-                    bt.w[bi][r][j] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl[j] * 16);
+            const int v = min(v0 + bi, nr - 1);
+            load_w(__builtin_amdgcn_readfirstlane(s_e[v]), bt.o[bi]);
         }
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi) {
-            const int v = min(v0 + bi, nu - 1);
-            const int ev = __builtin_amdgcn_readfirstlane(s_e[v]);
-            const int s0 = __builtin_amdgcn_readfirstlane(s_s0[v]);
-            const int n = __builtin_amdgcn_readfirstlane(s_n[v]);
-            const float* ds = a.es + (int64_t)ev * a.blob_s + 2 * I;
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) bt.dsv[bi][r] = ds[c0 + r];
-#pragma unroll
-            for (int i = 0; i < NT; ++i) {
-                const int sl = s0 + min(i, n - 1);
-#pragma unroll
-                for (int j = 0; j < NBJ; ++j) {
-                    const uint4* p = reinterpret_cast<const uint4*>(a.qh + (int64_t)sl * I + bcl[j] * 32);
-                    bt.ha[bi][i][j][0] = p[0];
-                    bt.ha[bi][i][j][1] = p[1];
-                    bt.hdf[bi][i][j] = a.dh[(int64_t)sl * BI + bcl[j]];
-                }
-            }
+            const int v = min(v0 + bi, nr - 1);
+            load_h(__builtin_amdgcn_readfirstlane(s_e[v]), __builtin_amdgcn_readfirstlane(s_s0[v]),
+                   __builtin_amdgcn_readfirstlane(s_n[v]), bt.o[bi]);
         }
     };
-    auto compute = [&](int v0, const Batch& bt) {
+    auto compute_batch = [&](int v0, const Batch& bt) {
 #pragma unroll
         for (int bi = 0; bi < NB; ++bi) {
             const int v = v0 + bi;
-            if (v >= nu) break;
-            const int s0 = __builtin_amdgcn_readfirstlane(s_s0[v]);
-            const int n = __builtin_amdgcn_readfirstlane(s_n[v]);
-            double vals[V];
-#pragma unroll
-            for (int r = 0; r < RPW; ++r)
-#pragma unroll
-                for (int i = 0; i < NT; ++i) {
-                    double p = 0.0;
-#pragma unroll
-                    for (int j = 0; j < NBJ; ++j) {
-                        const bool ok = i < n && lane + 64 * j < BI;
-                        const double hd = ok ? (double)bt.hdf[bi][i][j] * 0.0625 : 0.0;
-                        p += hd * (double)dot_block16(bt.w[bi][r][j], bt.ha[bi][i][j][0],
-                                                      bt.ha[bi][i][j][1]);
-                    }
-                    vals[r * NT + i] = p;
-                }
-            const double sum = wave_reduce_tr<V>(vals, lane);
-            const int vi = lane >> kShift;
-            if (lane == (vi << kShift)) {
-                const int r = vi / NT, i = vi - r * NT;
-                if (i < n) {
-                    float dsr = bt.dsv[bi][0];
-#pragma unroll
-                    for (int rr = 1; rr < RPW; ++rr)
-                        if (r == rr) dsr = bt.dsv[bi][rr];
-                    const float yv = (float)((double)dsr * sum);
-                    s_acc[wave * RPW + r][s_t[s0 + i]] += (double)s_w[s0 + i] * (double)yv;
-                }
-            }
+            if (v >= nr) break;
+            compute(bt.o[bi], __builtin_amdgcn_readfirstlane(s_s0[v]),
+                    __builtin_amdgcn_readfirstlane(s_n[v]));
         }
     };
-    // two batches per iteration with fixed buffer roles (no dynamic indexing)
     Batch b0, b1;
-    load(0, b0);
+    if (nr > 0) load(0, b0);
 #pragma unroll 1
-    for (int v0 = 0; v0 < nu; v0 += 2 * NB) {
-        if (v0 + NB < nu) load(v0 + NB, b1);
+    for (int v0 = 0; v0 < nr; v0 += 2 * NB) {
+        if (v0 + NB < nr) load(v0 + NB, b1);
         __builtin_amdgcn_sched_barrier(0);
-        compute(v0, b0);
-        if (v0 + NB >= nu) break;
-        if (v0 + 2 * NB < nu) load(v0 + 2 * NB, b0);
+        compute_batch(v0, b0);
+        if (v0 + NB >= nr) break;
+        if (v0 + 2 * NB < nr) load(v0 + 2 * NB, b0);
         __builtin_amdgcn_sched_barrier(0);
-        compute(v0 + NB, b1);
+        compute_batch(v0 + NB, b1);
     }
+    if (S) compute(sh, n_ent, T);
     if (lane < RPW * NT) {
         const int r = lane / NT, t = lane - r * NT;
         if (t < T) {
