@@ -334,8 +334,8 @@ def gateup_roofline(kern, cfg, gate_up_bytes, T, bits=4):
 
 def run_sweep(args, cfg, counts):
     """Layer time against the number of tokens per call, on the weights and
-    input recipe of `cfg` (the few-token kernels serve T <= 4 with int4
-    weights, the grouped MFMA kernels the rest)."""
+    input recipe of `cfg` (the few-token kernels serve T <= 4, with int2
+    weights T <= 2; the grouped MFMA kernels the rest)."""
     import torch
 
     import coli_synth as cs
@@ -378,7 +378,7 @@ def run_sweep(args, cfg, counts):
         uniq = int((cnt[:E] > 0).sum().item()) + S
         print(json.dumps({"sweep": cfg.name, "tokens": T, "us_per_call": round(dt * 1e6, 2),
                           "tokens_per_s": round(T / dt, 1), "experts_in_use": uniq,
-                          "path": "few-token" if T <= 4 and bits == 4 else "grouped-mfma",
+                          "path": "few-token" if T <= (2 if bits == 2 else 4) else "grouped-mfma",
                           "weight_bits": bits,
                           "expert_weight_gbps": round(
                               uniq * (3 * I * H * bits // 8 + 4 * (2 * I + H)) / dt / 1e9, 1)}),

@@ -72,8 +72,10 @@ typedef struct coli_moe_cfg {
                              2..64 groups of n_experts / n_group consecutive experts */
     int32_t topk_group;   /* groups kept when n_group > 1: 1..n_group, and the kept
                              groups must hold at least top_k experts */
-    int32_t weight_bits;  /* expert weight codes: 4 (0 reads as 4), 8 or 2; int8 and
-                             int2 need hidden and inter multiples of 64 */
+    int32_t weight_bits;  /* expert weight codes: 4 (0 reads as 4), 8 or 2; beyond the
+                             few-token path (up to 4 tokens, int2: 2, with H <= 6144,
+                             I <= 2048 and I a multiple of 64) int8 and int2 need hidden
+                             and inter multiples of 64, else COLI_E_UNSUPPORTED */
     int32_t reserved;     /* must be 0 */
 } coli_moe_cfg;
 

@@ -219,45 +219,55 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
 }
 
 // Template selection for the fused few-token path.
-// Few-token path: three fused kernels (k_decode.h). Shapes it covers:
-// hidden <= 6144, intermediate <= 2048, <= 256 routed experts.
+// Few-token path: three fused kernels (k_decode.h), every weight width.
+// Shapes it covers: hidden <= 6144, intermediate <= 2048, <= 256 routed
+// experts; up to four tokens (int2: two, where the grouped MFMA kernels
+// overtake it, their code expansion being paid once per token there).
 bool small_path_fits(const coli_moe_cfg& c, int64_t T) {
-    return weight_bits(c) == 4 && T <= 4 && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
+    const int max_tok = weight_bits(c) == 2 ? 2 : 4;
+    return T <= max_tok && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
            c.inter <= 2048 && c.inter % 64 == 0 && c.n_experts <= 256;
 }
 
-template <int NT, int NBJH, bool TAP>
+template <int NT, int NBJH, bool TAP, int BITS>
 void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     const int nrb = a.I / 32;
     mk.mark("dec_router");
     const int qb = (a.T * (a.H / 32) + 7) / 8;  // workgroups needed for Q8_0(x)
-    dec::k_dec_router<NT><<<(a.E > qb) ? a.E : qb, 256, 0, s>>>(a);
+    dec::k_dec_router<NT, BITS><<<(a.E > qb) ? a.E : qb, 256, 0, s>>>(a);
     mk.mark("dec_gateup");
     const int um = (a.T * a.K < a.E) ? a.T * a.K : a.E;
     const int hbw = (NT > 1) ? 2 : 1;  // h-blocks per workgroup (k_dec_gateup)
-    dec::k_dec_gateup<NT, NBJH, TAP><<<(a.S + um) * (nrb / hbw), 256, 0, s>>>(a);
+    dec::k_dec_gateup<NT, NBJH, TAP, BITS><<<(a.S + um) * (nrb / hbw), 256, 0, s>>>(a);
     mk.mark("dec_down");
     if (NT == 4)
-        dec::k_dec_down_x<NT, 1><<<a.H / 8, 256, 0, s>>>(a);
+        dec::k_dec_down_x<NT, 1, BITS><<<a.H / 8, 256, 0, s>>>(a);
     else
-        dec::k_dec_down<NT, 1, 2, 2><<<a.H / 8, 256, 0, s>>>(a);
+        dec::k_dec_down<NT, 1, 2, 2, BITS><<<a.H / 8, 256, 0, s>>>(a);
 }
 
-template <int NT>
+template <int NT, int BITS>
 void launch_small_nt(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     if (a.H <= 2048) {
-        if (a.tap) launch_small_tap<NT, 1, true>(a, s, mk);
-        else launch_small_tap<NT, 1, false>(a, s, mk);
+        if (a.tap) launch_small_tap<NT, 1, true, BITS>(a, s, mk);
+        else launch_small_tap<NT, 1, false, BITS>(a, s, mk);
     } else {
-        if (a.tap) launch_small_tap<NT, 3, true>(a, s, mk);
-        else launch_small_tap<NT, 3, false>(a, s, mk);
+        if (a.tap) launch_small_tap<NT, 3, true, BITS>(a, s, mk);
+        else launch_small_tap<NT, 3, false, BITS>(a, s, mk);
     }
 }
 
-void launch_small(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
-    if (a.T <= 1) launch_small_nt<1>(a, s, mk);
-    else if (a.T <= 2) launch_small_nt<2>(a, s, mk);
-    else launch_small_nt<4>(a, s, mk);
+template <int BITS>
+void launch_small_bits(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
+    if (a.T <= 1) launch_small_nt<1, BITS>(a, s, mk);
+    else if (a.T <= 2) launch_small_nt<2, BITS>(a, s, mk);
+    else launch_small_nt<4, BITS>(a, s, mk);
+}
+
+void launch_small(const dec::DecArgs& a, int bits, hipStream_t s, Marks& mk) {
+    if (bits == 8) launch_small_bits<8>(a, s, mk);
+    else if (bits == 2) launch_small_bits<2>(a, s, mk);
+    else launch_small_bits<4>(a, s, mk);
 }
 
 int hip_status() {
@@ -287,10 +297,11 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
     const int H = c.hidden, I = c.inter, E = c.n_experts, K = c.top_k, S = c.n_shared;
     const int bits = weight_bits(c);
     const int64_t blob_q = 3ll * I * H * bits / 8, blob_s = 2ll * I + H;
-    // grouped MFMA path when the row tiles divide the shapes, else the GEMV
-    // path; int8 and int2 weights run on the MFMA kernels only
+    // few tokens: the fused kernels (every width); else the grouped MFMA
+    // path when the row tiles divide the shapes, else the GEMV path, which
+    // has int4 weights only
     const bool mfma = (H % pf::kRows) == 0 && (I % pf::kRows) == 0;
-    if (bits != 4 && !mfma) return COLI_E_UNSUPPORTED;
+    if (bits != 4 && !mfma && !small_path_fits(c, T)) return COLI_E_UNSUPPORTED;
     char* base = static_cast<char*>(ws);
     int8_t* qx = reinterpret_cast<int8_t*>(base + L.pub.qx);
     float* dx = reinterpret_cast<float*>(base + L.pub.dx);
@@ -327,7 +338,7 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         a.tap_rows = (int)L.pub.tap_rows;
         a.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
         a.y = y; a.accum = (flags & COLI_FWD_ACCUM) ? 1 : 0;
-        launch_small(a, s, mk);
+        launch_small(a, bits, s, mk);
         mk.mark("end");
         return hip_status();
     }

@@ -30,12 +30,91 @@ __device__ __forceinline__ uint4 ldnt(const uint8_t* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// Expert weight widths of the few-token kernels. A row holds 4 BITS bytes
+// per 32-wide block (codes packed little end first). blk is one block in
+// registers, dot its exact int32 product with 32 Q8_0 codes stored in the
+// order kL (0 natural, 1 the 8-group order e0 e2 e4 e6 e1 e3 e5 e7, 2 the
+// 16-group order e0 e4 e8 e12 e1 ...), times kDiv = 1 / kInv (the int4
+// codes enter the dot as 16 q, int2 codes as 64 q, each shifted into the top
+// of its byte).
+// HR h-rows per gate/up step keep a step's loads at 3 KB per row pair of
+// int4 (one int8 row pair, four int2 row pairs).
+template <int BITS> struct DW;
+template <> struct DW<4> {
+    typedef uint4 blk;
+    static constexpr int kL = 1, kDiv = 16, HR = 2;
+    static constexpr double kInv = 0.0625;
+    static __device__ __forceinline__ blk load(const uint8_t* p) { return ldnt(p); }
+    static __device__ __forceinline__ int dot(const blk& w, uint4 a0, uint4 a1) {
+        return dot_block16(w, a0, a1);
+    }
+};
+template <> struct DW<8> {
+    struct blk {
+        v4u lo, hi;
+    };
+    static constexpr int kL = 0, kDiv = 1, HR = 1;
+    static constexpr double kInv = 1.0;
+    static __device__ __forceinline__ blk load(const uint8_t* p) {
+        blk b;
+        b.lo = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+        b.hi = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p + 16));
+        return b;
+    }
+    static __device__ __forceinline__ int dot(const blk& w, uint4 a0, uint4 a1) {
+        int acc = 0;
+        acc = __builtin_amdgcn_sdot4((int)w.lo.x, (int)a0.x, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.lo.y, (int)a0.y, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.lo.z, (int)a0.z, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.lo.w, (int)a0.w, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.hi.x, (int)a1.x, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.hi.y, (int)a1.y, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.hi.z, (int)a1.z, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.hi.w, (int)a1.w, acc, false);
+        return acc;
+    }
+};
+template <> struct DW<2> {
+    typedef v2u blk;
+    static constexpr int kL = 2, kDiv = 64, HR = 4;
+    static constexpr double kInv = 0.015625;
+    static __device__ __forceinline__ blk load(const uint8_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    }
+    // (x << s) & 0xC0C0C0C0 puts code 4j + (6 - s) / 2 of dword x, times 64,
+    // in byte j: s = 6, 4, 2, 0 give elements {0,4,8,12}, {1,5,9,13}, ...
+    static __device__ __forceinline__ int dot(const blk& w, uint4 a0, uint4 a1) {
+        constexpr unsigned M = 0xC0C0C0C0u;
+        int acc = 0;
+        acc = __builtin_amdgcn_sdot4((int)((w.x << 6) & M), (int)a0.x, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)((w.x << 4) & M), (int)a0.y, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)((w.x << 2) & M), (int)a0.z, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)(w.x & M), (int)a0.w, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)((w.y << 6) & M), (int)a1.x, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)((w.y << 4) & M), (int)a1.y, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)((w.y << 2) & M), (int)a1.z, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)(w.y & M), (int)a1.w, acc, false);
+        return acc;
+    }
+};
+
+// Position of element k (0..31) of a block in activation order L.
+template <int L>
+__device__ __forceinline__ int act_pos(int k) {
+    if (L == 0) return k;
+    if (L == 1) return q8_perm_pos(k);
+    return (k & ~15) + 4 * (k & 3) + ((k >> 2) & 3);
+}
+
 // Transposed wave reduction of V values per lane: after log2(V) halving
 // butterflies every lane holds one partial of value index (lane >> (6 -
 // log2 V)); the remaining butterflies finish that sum. Returns the full sum
 // of that value index.
 template <int V>
 __device__ __forceinline__ double wave_reduce_tr(double* v, int lane) {
+    static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V: a power of two up to 64");
     int step = 0;
 #pragma unroll
     for (int h = V; h > 1; h >>= 1) {
@@ -673,38 +752,43 @@ constexpr int kUinfoW = 1 + 3 * kMaxEntries;  // offset of the slot weights in u
 
 // Gate/up GEMV for one expert, NT token slots and 32 intermediate rows
 // (h-block hb), then SwiGLU and Q8_0(h) into qh/dh at slots slot0 + i.
-// Activations: Q8_0 codes of x in 8-group order (qx) and block scales (dx),
-// rows of token tok[i]. Four waves; wave w owns h-rows w, w+4, ..., w+28,
-// taken two per step (two gate + two up rows), so the four waves read 8
-// consecutive rows of each matrix at a time; the loop is fully unrolled and
-// every load unconditional (lanes past the last block read a clamped address
-// and see zero activations), with two steps' loads in flight.
-template <int NT, int NBJ, bool TAP>
+// Activations: Q8_0 codes of x in the width's order (qx) and block scales
+// (dx), rows of token tok[i]. Four waves; wave w owns h-rows w, w+4, ...,
+// w+28, taken HR per step (HR gate + HR up rows), so the four waves read
+// 4 HR consecutive rows of each matrix at a time; the loop is fully unrolled
+// and every load unconditional (lanes past the last block read a clamped
+// address and see zero activations), with two steps' loads in flight.
+template <int NT, int NBJ, bool TAP, int BITS>
 __device__ __forceinline__ void gateup_block(const DecArgs& a, int e, int hb, int n,
                                              const int* tok, int slot0, float (*hbuf)[32]) {
+    typedef DW<BITS> F;
+    typedef typename F::blk Blk;
+    constexpr int HR = F::HR, RQ = 2 * HR, NS = 8 / HR;  // rows per step, steps
     const int H = a.H, I = a.I, BH = H >> 5;
+    const int64_t rowb = (int64_t)H * BITS / 8;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
-    const uint8_t* up = gate + (int64_t)I * (H >> 1);
+    const uint8_t* up = gate + (int64_t)I * rowb;
     const float* gs = a.es + (int64_t)e * a.blob_s;
     const float* us = gs + I;
     const int r0 = hb * 32 + wave;  // rows r0 + 4k, k = 0..7
     int boff[NBJ];
 #pragma unroll
-    for (int j = 0; j < NBJ; ++j) boff[j] = min(lane + 64 * j, BH - 1) * 16;
-    uint4 wb[2][4][NBJ];
-    auto load_pair = [&](int p, uint4 (&dst)[4][NBJ]) {
+    for (int j = 0; j < NBJ; ++j) boff[j] = min(lane + 64 * j, BH - 1) * (4 * BITS);
+    Blk wb[2][RQ][NBJ];
+    // step p: gate rows r0 + 4 (HR p + q), q < HR, then the same up rows
+    auto load_pair = [&](int p, Blk (&dst)[RQ][NBJ]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = r0 + 4 * (2 * p + (q & 1));
-            const uint8_t* row = ((q < 2) ? gate : up) + (int64_t)r * (H >> 1);
+        for (int q = 0; q < RQ; ++q) {
+            const int r = r0 + 4 * (HR * p + (q % HR));
+            const uint8_t* row = ((q < HR) ? gate : up) + (int64_t)r * rowb;
 #pragma unroll
-            for (int j = 0; j < NBJ; ++j) dst[q][j] = ldnt(row + boff[j]);
+            for (int j = 0; j < NBJ; ++j) dst[q][j] = F::load(row + boff[j]);
         }
     };
     load_pair(0, wb[0]);
-    load_pair(1, wb[1]);
+    if (NS > 1) load_pair(1, wb[1]);
     // row scales, one per lane (lane k & 7 holds row r0 + 4 (k & 7))
     const float gsl = gs[r0 + 4 * (lane & 7)];
     const float usl = us[r0 + 4 * (lane & 7)];
@@ -723,47 +807,49 @@ __device__ __forceinline__ void gateup_block(const DecArgs& a, int e, int hb, in
             const float d = a.dx[(int64_t)t * BH + bb];
             xa[i][j][0] = ok ? a0 : make_uint4(0, 0, 0, 0);
             xa[i][j][1] = ok ? a1 : make_uint4(0, 0, 0, 0);
-            xd[i][j] = ok ? (double)d * 0.0625 : 0.0;  // undo the x16 of the codes
+            xd[i][j] = ok ? (double)d * F::kInv : 0.0;  // undo the factor of the codes
         }
     }
+    constexpr int V = RQ * NT;  // values per step, a power of two
+    constexpr int kShift = 6 - ((V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : 1);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        if (p >= 1 && p < 3) load_pair(p + 1, wb[(p + 1) & 1]);
+    for (int p = 0; p < NS; ++p) {
+        if (p >= 1 && p < NS - 1) load_pair(p + 1, wb[(p + 1) & 1]);
         // keep the next step's loads issued ahead of this step's arithmetic
         __builtin_amdgcn_sched_barrier(0);
-        const uint4 (&wc)[4][NBJ] = wb[p & 1];
-        // values ordered (quad, token): quad 0/1 = gate rows of step p, 2/3 = up rows
-        double v[4 * NT];
+        const Blk (&wc)[RQ][NBJ] = wb[p & 1];
+        // values ordered (row, token): rows q < HR are the gate rows of step p,
+        // the others the up rows
+        double v[V];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < RQ; ++q)
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 double acc = 0.0;
 #pragma unroll
                 for (int j = 0; j < NBJ; ++j) {
-                    const int d16 = dot_block16(wc[q][j], xa[i][j][0], xa[i][j][1]);
-                    acc += xd[i][j] * (double)d16;
-                    if (TAP && q < 2) {
-                        const int r = r0 + 4 * (2 * p + q), b = lane + 64 * j;
+                    const int dq = F::dot(wc[q][j], xa[i][j][0], xa[i][j][1]);
+                    acc += xd[i][j] * (double)dq;
+                    if (TAP && q < HR) {
+                        const int r = r0 + 4 * (HR * p + q), b = lane + 64 * j;
                         if (i < n && b < BH && (r % a.tap_stride) == 0)
                             a.tap[((int64_t)(slot0 + i) * a.tap_rows + r / a.tap_stride) * BH + b] =
-                                d16 / 16;
+                                dq / F::kDiv;
                     }
                 }
                 v[q * NT + i] = acc;
             }
-        const double sum = wave_reduce_tr<4 * NT>(v, lane);
+        const double sum = wave_reduce_tr<V>(v, lane);
         const double other = __shfl_xor(sum, 32, 64);  // up value for gate lanes
-        constexpr int kShift = (NT == 1) ? 4 : (NT == 2) ? 3 : 2;  // 6 - log2(4 NT)
         const int vi = lane >> kShift;   // value index held by this lane
-        const int kq = 2 * p + ((vi < 2 * NT) ? vi / NT : 0);
+        const int kq = HR * p + ((vi < HR * NT) ? vi / NT : 0);
         const float gsk = __shfl(gsl, kq, 64), usk = __shfl(usl, kq, 64);
-        if (vi < 2 * NT && lane == (vi << kShift)) {
-            const int q = vi / NT, i = vi - q * NT;   // q in {0, 1}: row r0 + 4(2p+q)
+        if (vi < HR * NT && lane == (vi << kShift)) {
+            const int q = vi / NT, i = vi - q * NT;   // q < HR: row r0 + 4(HR p + q)
             if (i < n) {
                 const float g = (float)((double)gsk * sum);
                 const float u = (float)((double)usk * other);
-                hbuf[i][wave + 4 * (2 * p + q)] = swiglu_f32(g, u);
+                hbuf[i][wave + 4 * (HR * p + q)] = swiglu_f32(g, u);
             }
         }
     }
@@ -777,7 +863,7 @@ __device__ __forceinline__ void gateup_block(const DecArgs& a, int e, int hb, in
         const float dd = amax / 127.0f;
         const int c = q8_code(val, dd);
         if (i < n) {
-            a.qh[(int64_t)(slot0 + i) * I + hb * 32 + q8_perm_pos(k)] = (int8_t)c;
+            a.qh[(int64_t)(slot0 + i) * I + hb * 32 + act_pos<F::kL>(k)] = (int8_t)c;
             if (k == 0) a.dh[(int64_t)(slot0 + i) * (I >> 5) + hb] = dd;
         }
     }
@@ -787,79 +873,86 @@ __device__ __forceinline__ void gateup_block(const DecArgs& a, int e, int hb, in
 // scales of the n tokens are staged in LDS (xs: n rows of H bytes, xds: n
 // rows of H/32 scales) and read per step, one token at a time, so the
 // activations do not occupy registers for the whole kernel.
-template <int NT, int NBJ, bool TAP>
+template <int NT, int NBJ, bool TAP, int BITS>
 __device__ __forceinline__ void gateup_block_lds(const DecArgs& a, int e, int hb, int n,
                                                  int slot0, const uint8_t* xs, const float* xds,
                                                  float (*hbuf)[32]) {
+    typedef DW<BITS> F;
+    typedef typename F::blk Blk;
+    constexpr int HR = F::HR, RQ = 2 * HR, NS = 8 / HR;
     const int H = a.H, I = a.I, BH = H >> 5;
+    const int64_t rowb = (int64_t)H * BITS / 8;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
-    const uint8_t* up = gate + (int64_t)I * (H >> 1);
+    const uint8_t* up = gate + (int64_t)I * rowb;
     const float* gs = a.es + (int64_t)e * a.blob_s;
     const float* us = gs + I;
     const int r0 = hb * 32 + wave;  // rows r0 + 4k, k = 0..7
     int boff[NBJ];
 #pragma unroll
-    for (int j = 0; j < NBJ; ++j) boff[j] = min(lane + 64 * j, BH - 1) * 16;
-    uint4 wb[2][4][NBJ];
-    auto load_pair = [&](int p, uint4 (&dst)[4][NBJ]) {
+    for (int j = 0; j < NBJ; ++j) boff[j] = min(lane + 64 * j, BH - 1) * (4 * BITS);
+    Blk wb[2][RQ][NBJ];
+    auto load_pair = [&](int p, Blk (&dst)[RQ][NBJ]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = r0 + 4 * (2 * p + (q & 1));
-            const uint8_t* row = ((q < 2) ? gate : up) + (int64_t)r * (H >> 1);
+        for (int q = 0; q < RQ; ++q) {
+            const int r = r0 + 4 * (HR * p + (q % HR));
+            const uint8_t* row = ((q < HR) ? gate : up) + (int64_t)r * rowb;
 #pragma unroll
-            for (int j = 0; j < NBJ; ++j) dst[q][j] = ldnt(row + boff[j]);
+            for (int j = 0; j < NBJ; ++j) dst[q][j] = F::load(row + boff[j]);
         }
     };
     load_pair(0, wb[0]);
-    load_pair(1, wb[1]);
+    if (NS > 1) load_pair(1, wb[1]);
     const float gsl = gs[r0 + 4 * (lane & 7)];
     const float usl = us[r0 + 4 * (lane & 7)];
+    constexpr int V = RQ * NT;  // values per step, a power of two
+    constexpr int kShift = 6 - ((V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : 1);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        if (p >= 1 && p < 3) load_pair(p + 1, wb[(p + 1) & 1]);
+    for (int p = 0; p < NS; ++p) {
+        if (p >= 1 && p < NS - 1) load_pair(p + 1, wb[(p + 1) & 1]);
         __builtin_amdgcn_sched_barrier(0);
-        const uint4 (&wc)[4][NBJ] = wb[p & 1];
-        double v[4 * NT];
+        const Blk (&wc)[RQ][NBJ] = wb[p & 1];
+        double v[V];
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-            double acc[4] = {0.0, 0.0, 0.0, 0.0};
+            double acc[RQ];
+#pragma unroll
+            for (int q = 0; q < RQ; ++q) acc[q] = 0.0;
             if (i < n) {
 #pragma unroll
                 for (int j = 0; j < NBJ; ++j) {
                     const int b = lane + 64 * j, bb = min(b, BH - 1);
                     const uint4* px = reinterpret_cast<const uint4*>(xs + i * H + bb * 32);
                     const uint4 x0 = px[0], x1 = px[1];
-                    const double xd = (b < BH) ? (double)xds[i * BH + bb] * 0.0625 : 0.0;
+                    const double xd = (b < BH) ? (double)xds[i * BH + bb] * F::kInv : 0.0;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int d16 = dot_block16(wc[q][j], x0, x1);
-                        acc[q] += xd * (double)d16;
-                        if (TAP && q < 2) {
-                            const int r = r0 + 4 * (2 * p + q);
+                    for (int q = 0; q < RQ; ++q) {
+                        const int dq = F::dot(wc[q][j], x0, x1);
+                        acc[q] += xd * (double)dq;
+                        if (TAP && q < HR) {
+                            const int r = r0 + 4 * (HR * p + q);
                             if (b < BH && (r % a.tap_stride) == 0)
                                 a.tap[((int64_t)(slot0 + i) * a.tap_rows + r / a.tap_stride) * BH +
-                                      b] = d16 / 16;
+                                      b] = dq / F::kDiv;
                         }
                     }
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q * NT + i] = acc[q];
+            for (int q = 0; q < RQ; ++q) v[q * NT + i] = acc[q];
         }
-        const double sum = wave_reduce_tr<4 * NT>(v, lane);
+        const double sum = wave_reduce_tr<V>(v, lane);
         const double other = __shfl_xor(sum, 32, 64);
-        constexpr int kShift = (NT == 1) ? 4 : (NT == 2) ? 3 : 2;
         const int vi = lane >> kShift;
-        const int kq = 2 * p + ((vi < 2 * NT) ? vi / NT : 0);
+        const int kq = HR * p + ((vi < HR * NT) ? vi / NT : 0);
         const float gsk = __shfl(gsl, kq, 64), usk = __shfl(usl, kq, 64);
-        if (vi < 2 * NT && lane == (vi << kShift)) {
+        if (vi < HR * NT && lane == (vi << kShift)) {
             const int q = vi / NT, i = vi - q * NT;
             if (i < n) {
                 const float g = (float)((double)gsk * sum);
                 const float u = (float)((double)usk * other);
-                hbuf[i][wave + 4 * (2 * p + q)] = swiglu_f32(g, u);
+                hbuf[i][wave + 4 * (HR * p + q)] = swiglu_f32(g, u);
             }
         }
     }
@@ -873,7 +966,7 @@ __device__ __forceinline__ void gateup_block_lds(const DecArgs& a, int e, int hb
         const float dd = amax / 127.0f;
         const int c = q8_code(val, dd);
         if (i < n) {
-            a.qh[(int64_t)(slot0 + i) * I + hb * 32 + q8_perm_pos(k)] = (int8_t)c;
+            a.qh[(int64_t)(slot0 + i) * I + hb * 32 + act_pos<F::kL>(k)] = (int8_t)c;
             if (k == 0) a.dh[(int64_t)(slot0 + i) * (I >> 5) + hb] = dd;
         }
     }
@@ -936,7 +1029,7 @@ __device__ void publish_route(const DecArgs& a, const Route& R) {
 // quantises blocks 8e .. 8e+7 of the T x H/32 activation blocks (half a
 // wave per block, lane k holding element k), while its router row loads are
 // in flight.
-template <int NT>
+template <int NT, int BITS>
 __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
     __shared__ double red[NT][4];
     const int e = blockIdx.x;  // grid: max(E, blocks / 8) workgroups
@@ -960,7 +1053,7 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
 #pragma unroll
             for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
             const float d = amax / 127.0f;
-            a.qx[(int64_t)blk * 32 + q8_perm_pos(k)] = (int8_t)q8_code(v, d);
+            a.qx[(int64_t)blk * 32 + act_pos<DW<BITS>::kL>(k)] = (int8_t)q8_code(v, d);
             if (k == 0) a.dx[blk] = d;
         }
     }
@@ -1004,7 +1097,7 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
 
 // B: blocks [0, S*nrb) shared-expert h-blocks, then (u, hb) for the u-th
 // expert in use (u < min(E, T*K)); block (u = 0, hb = 0) publishes routing.
-template <int NT, int NBJ, bool TAP>
+template <int NT, int NBJ, bool TAP, int BITS>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
     // several tokens: activations staged in LDS, sharing space with the
     // top-k scratch (dead by then); H <= 6144 on this path
@@ -1032,9 +1125,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
                 stage_tokens(a, s_tok, a.T, xs, xds);
 #pragma unroll 1
                 for (int h = 0; h < HB; ++h)
-                    gateup_block_lds<NT, NBJ, TAP>(a, a.E, b * HB + h, a.T, a.T * a.K, xs, xds, hbuf);
+                    gateup_block_lds<NT, NBJ, TAP, BITS>(a, a.E, b * HB + h, a.T, a.T * a.K, xs, xds, hbuf);
             } else {
-                gateup_block<NT, NBJ, TAP>(a, a.E, b, a.T, s_tok, a.T * a.K, hbuf);
+                gateup_block<NT, NBJ, TAP, BITS>(a, a.E, b, a.T, s_tok, a.T * a.K, hbuf);
             }
             return;
         }
@@ -1058,9 +1151,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
         stage_tokens(a, &R.ent_t[s0], n, xs, xds);
 #pragma unroll 1
         for (int h = 0; h < HB; ++h)
-            gateup_block_lds<NT, NBJ, TAP>(a, e, hw * HB + h, n, s0, xs, xds, hbuf);
+            gateup_block_lds<NT, NBJ, TAP, BITS>(a, e, hw * HB + h, n, s0, xs, xds, hbuf);
     } else {
-        gateup_block<NT, NBJ, TAP>(a, e, hw, n, &R.ent_t[s0], s0, hbuf);
+        gateup_block<NT, NBJ, TAP, BITS>(a, e, hw, n, &R.ent_t[s0], s0, hbuf);
     }
 }
 
@@ -1070,8 +1163,10 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
 // requested before any is used (unconditional loads, clamped indices), then
 // reduced. Each wave accumulates its rows' combine in LDS (fp64), in
 // ascending expert order with the shared expert last.
-template <int NT, int NBJ, int RPW, int NB>
+template <int NT, int NBJ, int RPW, int NB, int BITS>
 __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
+    typedef DW<BITS> F;
+    typedef typename F::blk Blk;
     __shared__ int s_e[kMaxEntries], s_s0[kMaxEntries], s_n[kMaxEntries];
     __shared__ float s_w[kMaxEntries + kMaxTok];
     __shared__ int s_t[kMaxEntries + kMaxTok];
@@ -1091,18 +1186,19 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
     // one expert's operands for this wave's rows: weights, Q8_0(h) of its
     // tokens, row scales
     struct Operands {
-        uint4 w[RPW][NBJ];
+        Blk w[RPW][NBJ];
         uint4 ha[NT][NBJ][2];
         float hdf[NT][NBJ];
         float dsv[RPW];
     };
+    const int64_t rowb = (int64_t)I * BITS / 8;  // bytes per down row
     auto load_w = [&](int ev, Operands& o) {
-        const uint8_t* down = a.eq + (int64_t)ev * a.blob_q + (int64_t)I * H;
+        const uint8_t* down = a.eq + (int64_t)ev * a.blob_q + 2 * (int64_t)H * rowb;
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll
             for (int j = 0; j < NBJ; ++j)
-                o.w[r][j] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl[j] * 16);
+                o.w[r][j] = F::load(down + (int64_t)(c0 + r) * rowb + bcl[j] * (4 * BITS));
     };
     auto load_h = [&](int ev, int s0, int n, Operands& o) {
         const float* ds = a.es + (int64_t)ev * a.blob_s + 2 * I;
@@ -1133,8 +1229,8 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
 #pragma unroll
                 for (int j = 0; j < NBJ; ++j) {
                     const bool ok = i < n && lane + 64 * j < BI;
-                    const double hd = ok ? (double)o.hdf[i][j] * 0.0625 : 0.0;
-                    p += hd * (double)dot_block16(o.w[r][j], o.ha[i][j][0], o.ha[i][j][1]);
+                    const double hd = ok ? (double)o.hdf[i][j] * F::kInv : 0.0;
+                    p += hd * (double)F::dot(o.w[r][j], o.ha[i][j][0], o.ha[i][j][1]);
                 }
                 vals[r * NT + i] = p;
             }
@@ -1240,8 +1336,9 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
 // the whole job: one memory round trip per wave). Per-(row, expert, token)
 // results y_e = fp32(s_down * sum) go to LDS; the combine then runs in
 // ascending expert order with the shared expert last.
-template <int NT, int PB>
+template <int NT, int PB, int BITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_dec_down_x(DecArgs a) {
+    typedef DW<BITS> F;
     constexpr int RW = 8;                        // rows per workgroup
     constexpr int kSlots = kMaxEntries + kMaxTok;
     __shared__ int s_e[kMaxEntries + 1], s_s0[kMaxEntries + 1], s_n[kMaxEntries + 1];
@@ -1279,7 +1376,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int bcl = min(lane, BI - 1);           // I <= 2048: one block per lane
 #pragma unroll 1
     for (int v0 = wave; v0 < nu; v0 += 4 * PB) {
-        uint4 w[PB][RW];
+        typename F::blk w[PB][RW];
         uint4 ha[PB][NT][2];
         float hdf[PB][NT];
         int ev[PB];
@@ -1287,9 +1384,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         for (int m = 0; m < PB; ++m) {
             const int v = min(v0 + 4 * m, nu - 1);
             ev[m] = __builtin_amdgcn_readfirstlane(s_e[v]);
-            const uint8_t* down = a.eq + (int64_t)ev[m] * a.blob_q + (int64_t)I * H;
+            const int64_t rowb = (int64_t)I * BITS / 8;
+            const uint8_t* down = a.eq + (int64_t)ev[m] * a.blob_q + 2 * (int64_t)H * rowb;
 #pragma unroll
-            for (int r = 0; r < RW; ++r) w[m][r] = ldnt(down + (int64_t)(c0 + r) * (I >> 1) + bcl * 16);
+            for (int r = 0; r < RW; ++r)
+                w[m][r] = F::load(down + (int64_t)(c0 + r) * rowb + bcl * (4 * BITS));
         }
 #pragma unroll
         for (int m = 0; m < PB; ++m) {
@@ -1319,11 +1418,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 const bool ok = i < n && lane < BI;
-                const double hd = ok ? (double)hdf[m][i] * 0.0625 : 0.0;
+                const double hd = ok ? (double)hdf[m][i] * F::kInv : 0.0;
                 double vals[RW];
 #pragma unroll
                 for (int r = 0; r < RW; ++r)
-                    vals[r] = hd * (double)dot_block16(w[m][r], ha[m][i][0], ha[m][i][1]);
+                    vals[r] = hd * (double)F::dot(w[m][r], ha[m][i][0], ha[m][i][1]);
                 const double sum = wave_reduce_tr<RW>(vals, lane);
                 const int r = lane >> 3;  // 64 / RW lanes per value
                 const float ds = __shfl(dsm[m], r, 64);

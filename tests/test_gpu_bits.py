@@ -1,9 +1,9 @@
 """GPU parity of the int8 and int2 weight formats (coli_pack_weights, and the
-layer on the grouped MFMA kernels, which serve every token count for these
-widths): packing bit-exact; Q8_0(x) codes in each width's element order,
-per-block gate dots bit-exact through the debug tap; Q8_0(h) codes equal;
-outputs within 1e-4 rel-L2 of the oracle (tiny workload on every token; full
-decode and prefill shapes on sampled tokens)."""
+layer: the fused few-token kernels up to four tokens, the grouped MFMA
+kernels above): packing bit-exact; Q8_0(x) codes in each width's element
+order, per-block gate dots bit-exact through the debug tap; Q8_0(h) codes
+equal; outputs within 1e-4 rel-L2 of the oracle (tiny workload on every
+token; full decode, MTP-verify and prefill shapes on sampled tokens)."""
 import dataclasses
 
 import numpy as np
@@ -101,7 +101,7 @@ def _compare(ref, cfg, bits, x, y, taps, tokens):
 
 
 @pytest.mark.parametrize("bits", [2, 8])
-@pytest.mark.parametrize("n_tok", [1, 2, 5, 33])
+@pytest.mark.parametrize("n_tok", [1, 2, 3, 4, 5, 33])
 def test_tiny_layer_every_token(C, ref, bits, n_tok):
     cfg = cs.with_tokens(cs.CONFIGS[0], n_tok)
     _note("tiny", bits, n_tok)
@@ -112,7 +112,7 @@ def test_tiny_layer_every_token(C, ref, bits, n_tok):
 
 
 @pytest.mark.parametrize("bits", [2, 8])
-@pytest.mark.parametrize("cid,n_tok,sample", [(1, 1, None), (3, 512, 4)])
+@pytest.mark.parametrize("cid,n_tok,sample", [(1, 1, None), (2, 3, None), (3, 512, 4)])
 def test_full_size_layers(C, ref, bits, cid, n_tok, sample):
     cfg = cs.with_tokens(cs.CONFIGS[cid], n_tok)
     _note("full", bits, cfg.name, n_tok)
@@ -127,8 +127,22 @@ def test_full_size_layers(C, ref, bits, cid, n_tok, sample):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("n_tok", [1, 3])
+def test_few_token_ragged_hidden(C, ref, bits, n_tok):
+    # hidden 288 = 9 blocks of 32: most lanes of a row hold no block
+    cfg = dataclasses.replace(cs.CONFIGS[0], hidden=288, n_tok=n_tok)
+    _note("ragged hidden", bits, n_tok)
+    W = _layer(C, cfg, bits)
+    x = layer_input(ref, cfg)
+    y, taps = _run(C, W, x)
+    _compare(ref, cfg, bits, x, y, taps, list(range(n_tok)))
+
+
 def test_rejects_unsupported_widths(C):
-    cfg = dataclasses.replace(cs.CONFIGS[0], hidden=288, n_tok=1)  # 288 = 9 x 32, not 64k
+    # five tokens leave the fused kernels; hidden 288 = 9 x 32 is no multiple
+    # of the MFMA row tile (64), and the GEMV kernels take int4 only
+    cfg = dataclasses.replace(cs.CONFIGS[0], hidden=288, n_tok=5)
     for bits, code in [(8, C.COLI_E_UNSUPPORTED), (3, C.COLI_E_INVAL)]:
         lc = lib_cfg(C, cfg, bits=bits)
         n = cfg.n_experts + cfg.n_shared
@@ -143,9 +157,9 @@ def test_rejects_unsupported_widths(C):
             continue
         W = C.LayerWeights(lc, wr, b, q, s)
         ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
-        y = torch.empty((1, cfg.hidden), device="cuda")
+        y = torch.empty((5, cfg.hidden), device="cuda")
         with pytest.raises(C.ColiError) as ei:
-            C.coli_moe_forward(W, torch.zeros((1, cfg.hidden), device="cuda"), y, ws)
+            C.coli_moe_forward(W, torch.zeros((5, cfg.hidden), device="cuda"), y, ws)
         assert ei.value.code == code
     w = torch.zeros((2, 64), device="cuda")
     with pytest.raises(C.ColiError):
