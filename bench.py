@@ -189,6 +189,9 @@ def main():
     weight_gbps = uniq_avg * eb / (ms_per_step * 1e-3) / 1e9
 
     roofline = gateup_roofline(kern, cfg, gate_up_bytes, T, bits)
+    ceiling = read_ceiling_gbps(C)
+    if roofline:
+        roofline["frac_of_read_ceiling"] = round(roofline["achieved"] / ceiling, 4)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -210,6 +213,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "expert_weight_gbps": round(weight_gbps, 1),
         "expert_weight_frac_hbm": round(weight_gbps / HBM_PEAK_GBPS, 4),
+        "read_ceiling_gbps": ceiling,
+        "expert_weight_frac_read_ceiling": round(weight_gbps / ceiling, 4),
         "unique_experts_per_step": round(uniq_avg, 2),
         "algorithmic_bytes_per_step": int(step_bytes),
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
@@ -304,6 +309,27 @@ def run_pack_fp8(args, cfg):
                      "traffic": TRAFFIC.get(("pack_fp8_gateup", workload))},
         "cpu_baseline": None,
     }), flush=True)
+
+
+def read_ceiling_gbps(C, gib=4, reps=10):
+    """Measured HBM streaming-read ceiling: coli_stream_read over a buffer far
+    larger than the 256 MB last-level cache, HIP events on the launch stream."""
+    import torch
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        C.coli_stream_read(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        C.coli_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbps = buf.numel() / (ms * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return round(gbps, 1)
 
 
 def gateup_roofline(kern, cfg, gate_up_bytes, T, bits=4):

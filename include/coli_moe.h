@@ -239,6 +239,19 @@ COLI_API int coli_moe_forward_profiled(const coli_moe_weights* w, const float* x
 COLI_API int coli_rmsnorm(const float* x, int64_t n_tok, int64_t dim, float eps, float* out,
                           void* stream);
 
+/* Measurement helper, not a step of the layer: reads `bytes` of device memory
+ * at src once with streaming (nontemporal) 16-byte loads, the pattern of the
+ * layer's weight streams, so that timing it gives the HBM read ceiling the
+ * expert-weight rates are quoted against beside the published peak. It has
+ * no counterpart in the pages (their engine reads experts from disk).
+ *   src   device pointer, 16-byte aligned; bytes a multiple of 16 (0: no-op)
+ *   sink  device uint32 (4-byte aligned): an XOR checksum of the data is
+ *         folded into it atomically (its old value is kept in the XOR); it
+ *         exists so that no load is dead code
+ * Errors: COLI_E_INVAL (bytes < 0 or not a multiple of 16, null pointers),
+ * COLI_E_ALIGN. Enqueues one kernel on `stream`. */
+COLI_API int coli_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ COLI_FWD_DEBUG_TAPS = 2
 EXPORTS = ("coli_strerror", "coli_pack_weights", "coli_pack_int4", "coli_pack_fp8_int4",
            "coli_quant_q8", "coli_moe_workspace_bytes",
            "coli_moe_workspace_layout", "coli_moe_route", "coli_moe_forward",
-           "coli_moe_forward_profiled", "coli_rmsnorm")
+           "coli_moe_forward_profiled", "coli_rmsnorm", "coli_stream_read")
 
 
 class ColiError(RuntimeError):
@@ -86,6 +86,7 @@ def _load():
                                             ctypes.POINTER(i32),
                                             ctypes.POINTER(ctypes.c_char_p)]
     L.coli_rmsnorm.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp]
+    L.coli_stream_read.argtypes = [vp, i64, vp, vp]
     for name in EXPORTS:
         getattr(L, name)
     return L
@@ -258,3 +259,10 @@ def coli_rmsnorm(x: torch.Tensor, out: torch.Tensor, eps: float = 1e-5, stream=N
     n, dim = x.shape
     _check(_lib.coli_rmsnorm(_dev(x, "x", torch.float32), n, dim, eps,
                              _dev(out, "out", torch.float32), _stream(stream)), "coli_rmsnorm")
+
+
+def coli_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Streaming read of buf (uint8, device) into the XOR checksum sink (int32[1])."""
+    _check(_lib.coli_stream_read(_dev(buf, "buf", torch.uint8), buf.numel(),
+                                 _dev(sink, "sink", torch.int32), _stream(stream)),
+           "coli_stream_read")

@@ -575,4 +575,17 @@ COLI_API int coli_rmsnorm(const float* x, int64_t n_tok, int64_t dim, float eps,
     return hip_status();
 }
 
+COLI_API int coli_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+    if (bytes < 0 || (bytes & 15) != 0) return COLI_E_INVAL;
+    if (bytes == 0) return COLI_OK;
+    if (!src || !sink) return COLI_E_INVAL;
+    if (misaligned(src) || (reinterpret_cast<uintptr_t>(sink) & 3) != 0) return COLI_E_ALIGN;
+    const int64_t n16 = bytes >> 4;
+    const int64_t want = (n16 + 255) / 256;
+    const unsigned grid = (unsigned)(want < 256 ? want : 256);  // one workgroup per CU
+    k_stream_read<<<grid, 256, 0, (hipStream_t)stream>>>(reinterpret_cast<const v4u_s*>(src), n16,
+                                                         sink);
+    return hip_status();
+}
+
 }  // extern "C"

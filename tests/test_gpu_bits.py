@@ -127,10 +127,10 @@ def test_full_size_layers(C, ref, bits, cid, n_tok, sample):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("bits", [2, 8])
-@pytest.mark.parametrize("n_tok", [1, 3])
+@pytest.mark.parametrize("bits,n_tok", [(2, 1), (2, 2), (8, 1), (8, 3), (8, 4)])
 def test_few_token_ragged_hidden(C, ref, bits, n_tok):
-    # hidden 288 = 9 blocks of 32: most lanes of a row hold no block
+    # hidden 288 = 9 blocks of 32: most lanes of a row hold no block (the
+    # fused kernels take up to four tokens, two with int2 weights)
     cfg = dataclasses.replace(cs.CONFIGS[0], hidden=288, n_tok=n_tok)
     _note("ragged hidden", bits, n_tok)
     W = _layer(C, cfg, bits)

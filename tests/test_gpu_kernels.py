@@ -196,3 +196,21 @@ def test_pack_fp8_int4_every_code(C, ref, cols):
     rq, rs = ref.pack_fp8_int4(q8.numpy(), bs.numpy())
     np.testing.assert_array_equal(s.cpu().numpy(), rs)
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 7 * 16, 64 << 20])
+def test_stream_read_checksum(C, nbytes):
+    # the read-ceiling probe touches every 16-byte word once: its XOR checksum
+    # equals the XOR of all 32-bit words of the buffer
+    _note("stream_read", nbytes)
+    rng = np.random.RandomState(nbytes % 1000)
+    host = rng.randint(0, 2**32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(host.view(np.uint8).copy()).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    C.coli_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host)
+    assert np.uint32(sink.cpu().numpy().view(np.uint32)[0]) == want
+    lib = C.lib()
+    assert lib.coli_stream_read(buf.data_ptr(), 24, sink.data_ptr(), None) == C.COLI_E_INVAL
+    assert lib.coli_stream_read(buf.data_ptr() + 4, 16, sink.data_ptr(), None) == C.COLI_E_ALIGN
