@@ -29,10 +29,13 @@ HBM_PEAK_GBPS = 8000.0
 # HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (two runs), scaled by what the counters read for a plain device
 # copy of known size (FETCH_SIZE x 2, WRITE_SIZE x 1). Keyed by (kernel,
-# workload); dropped whenever that kernel changes.
+# workload as the JSON line names it); dropped whenever that kernel changes.
 TRAFFIC = {
     # profiles/dec_kernels_decode_T1.txt
-    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55678.7 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55662.1 * 2 + 38.4) * 1024,
+    # profiles/dec_kernels_decode_T1_int8.txt, profiles/dec_kernels_decode_T1_int2.txt
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int8 weights"): (111699.8 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int2 weights"): (27989.4 * 2 + 38.4) * 1024,
     # profiles/pf_kernels_prefill_T512.txt
     ("pf_gateup", "prefill T512 zipf-bias"): (1749219.2 * 2 + 14454.1) * 1024,
     # profiles/pack_fp8_int4_layer.txt (the gate/up launch)
@@ -334,19 +337,19 @@ def read_ceiling_gbps(C, gib=4, reps=10):
 
 def gateup_roofline(kern, cfg, gate_up_bytes, T, bits=4):
     """Roofline of the gate/up kernel (the dominant launch of every path):
-    algorithmic HBM bytes per launch / its mean event-timed duration. The
-    stored traffic figures are those of the int4 kernels."""
+    algorithmic HBM bytes per launch / its mean event-timed duration, with the
+    stored counter traffic of that kernel and workload where there is one."""
     gk = next((k for k in ("dec_gateup", "pf_gateup", "gateup") if k in kern), None)
     if gk is None:
         return None
     if gk == "dec_gateup":
         gate_up_bytes += 8 * T * cfg.n_experts  # the fp64 logits the kernel reads
     ms = kern[gk]
+    wl = cfg.name + (f" int{bits} weights" if bits != 4 else "")
     ach = gate_up_bytes / (ms * 1e-3) / 1e9
     out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-           "traffic": (int(TRAFFIC[(gk, cfg.name)])
-                       if bits == 4 and (gk, cfg.name) in TRAFFIC else None),
+           "traffic": (int(TRAFFIC[(gk, wl)]) if (gk, wl) in TRAFFIC else None),
            "kernel": gk, "bytes_per_launch": int(gate_up_bytes),
            "avg_launch_us": round(ms * 1e3, 2)}
     if gk == "pf_gateup":
