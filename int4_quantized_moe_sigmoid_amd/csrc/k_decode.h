@@ -188,11 +188,6 @@ struct Route {
 
 // LDS scratch of the top-k, dead once the routing is done.
 struct TopkScratch {
-    unsigned long long gmax[kMaxTok][8];   // max key of each 32-expert group
-    unsigned long long gmax8[kMaxTok][32]; // max key of each 8-expert group (groups only)
-    unsigned long long keep[kMaxTok];      // kept routing groups (group-limited selection)
-    unsigned long long gthr[kMaxTok];      // key threshold from the kept groups (0: none)
-    int ncand[kMaxTok];
     unsigned long long ckey[kMaxTok][256];
     int ce[kMaxTok][256];
     double cs[kMaxTok][256];
@@ -215,257 +210,6 @@ __device__ __forceinline__ void top2_lanes(double& a, double& b, int n) {
     }
 }
 
-// Sigmoid + bias + top-k + gate weights of T <= 4 tokens by the whole
-// workgroup (thread e owns expert e, E <= blockDim.x). Selection order is c
-// descending, expert index ascending among equal c; an expert's position is
-// the number of experts ahead of it in that order. Only experts whose c is at
-// least the smallest of the 32-expert group maxima can be among the K largest
-// (when there are >= K groups those maxima are >= K distinct experts), so
-// positions are counted among those few candidates only.
-__device__ __forceinline__ void topk_wg(const double* sig, const double* cval, int T, int E, int K,
-                                        int norm, double rho, GroupSel gsel, Route& R,
-                                        TopkScratch& Z) {
-    const int e = threadIdx.x;
-    const int G = (E + 31) >> 5, G8 = (E + 7) >> 3;
-    const bool grouped = gsel.ng > 1;
-    const bool filt = G >= K || (grouped && G8 >= K);
-    if (threadIdx.x < kMaxTok * 8) (&Z.gmax[0][0])[threadIdx.x] = 0ull;
-    if (threadIdx.x < kMaxTok * 32) (&Z.gmax8[0][0])[threadIdx.x] = 0ull;
-    if (threadIdx.x < kMaxTok) Z.ncand[threadIdx.x] = 0;
-    // sigmoid s and selection score c = s + bias, from the router kernel
-    double s[kMaxTok], cs[kMaxTok];
-#pragma unroll
-    for (int t = 0; t < kMaxTok; ++t) {
-        const bool in = t < T && e < E;
-        s[t] = in ? sig[(int64_t)t * E + e] : 0.0;
-        cs[t] = in ? cval[(int64_t)t * E + e] : 0.0;
-    }
-    __syncthreads();
-    unsigned long long key[kMaxTok];
-#pragma unroll
-    for (int t = 0; t < kMaxTok; ++t) key[t] = (t < T && e < E) ? order_key(cs[t]) : 0ull;
-    // group-limited selection: the experts of dropped groups get key 0 (below
-    // every real key). With groups of 2..64 experts (a power of two: a group
-    // never straddles a wave) the group maxima come from lane shuffles, and the
-    // smallest second-largest c of the kept groups (2 tg >= K experts at or
-    // above it) bounds the K-th largest from below; otherwise the scores go
-    // through LDS and the expert-group maxima below give the bound.
-    const bool gshfl = grouped && gsel.gs >= 2 && gsel.gs <= 64 && !(gsel.gs & (gsel.gs - 1));
-    if (grouped) {
-        const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-        if (gshfl) {
-#pragma unroll
-            for (int t = 0; t < kMaxTok; ++t) {
-                if (t < T) {  // uniform
-                    double a = e < E ? cs[t] : -__builtin_inf(), b2 = -__builtin_inf();
-                    top2_lanes(a, b2, gsel.gs);
-                    if (e < E && (e & (gsel.gs - 1)) == 0) {
-                        Z.cs[t][e / gsel.gs] = a + b2;  // group score (cs is free until later)
-                        Z.cs[t][64 + e / gsel.gs] = b2;
-                    }
-                }
-            }
-            __syncthreads();
-            if (wv < T) {
-                const bool in = lane < gsel.ng;
-                const double sc = in ? Z.cs[wv][lane] : -__builtin_inf();
-                const double bq = in ? Z.cs[wv][64 + lane] : 0.0;
-                int rank = 0;
-                for (int j = 0; j < gsel.ng; ++j) {
-                    const double o = __shfl(sc, j, 64);
-                    rank += (o > sc || (o == sc && j < lane)) ? 1 : 0;
-                }
-                const bool kept = in && rank < gsel.tg;
-                const unsigned long long keep = __ballot(kept);
-                double tb = kept ? bq : __builtin_inf();
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) tb = fmin(tb, __shfl_xor(tb, o, 64));
-                if (lane == 0) {
-                    Z.keep[wv] = keep;
-                    Z.gthr[wv] = 2 * gsel.tg >= K ? order_key(tb) : 0ull;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < kMaxTok; ++t)
-                if (t < T && e < E) Z.cs[t][e] = cs[t];
-            __syncthreads();
-            if (wv < T) {
-                const unsigned long long keep = group_keep_mask(Z.cs[wv], gsel);
-                if (lane == 0) {
-                    Z.keep[wv] = keep;
-                    Z.gthr[wv] = 0ull;
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int t = 0; t < kMaxTok; ++t)
-            if (t < T && e < E && !((Z.keep[t] >> (e / gsel.gs)) & 1ull)) key[t] = 0ull;
-    }
-#pragma unroll
-    for (int t = 0; t < kMaxTok; ++t) {
-        if (t < T && filt && !gshfl && key[t]) {
-            atomicMax(&Z.gmax[t][e >> 5], key[t]);
-            if (grouped) atomicMax(&Z.gmax8[t][e >> 3], key[t]);
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < kMaxTok; ++t) {
-        if (t < T && e < E) {
-            // the smallest maximum of >= K non-empty expert groups bounds the
-            // K-th largest key from below (32-expert groups, else 8-expert)
-            unsigned long long thr = 0ull;
-            if (gshfl) {
-                thr = Z.gthr[t];
-            } else if (filt) {
-                unsigned long long mn = ~0ull;
-                int cnt = 0;
-                for (int g = 0; g < G; ++g) {
-                    const unsigned long long v = Z.gmax[t][g];
-                    if (v) {
-                        mn = min(mn, v);
-                        ++cnt;
-                    }
-                }
-                if (cnt >= K) {
-                    thr = mn;
-                } else if (grouped) {
-                    mn = ~0ull;
-                    cnt = 0;
-                    for (int g = 0; g < G8; ++g) {
-                        const unsigned long long v = Z.gmax8[t][g];
-                        if (v) {
-                            mn = min(mn, v);
-                            ++cnt;
-                        }
-                    }
-                    if (cnt >= K) thr = mn;
-                }
-            }
-            if (key[t] && key[t] >= thr) {
-                const int p = atomicAdd(&Z.ncand[t], 1);
-                Z.ckey[t][p] = key[t];
-                Z.ce[t][p] = e;
-                Z.cs[t][p] = s[t];
-            }
-        }
-    }
-    __syncthreads();
-    for (int t = 0; t < T; ++t) {
-        const int m = Z.ncand[t];
-        for (int i = threadIdx.x; i < m; i += blockDim.x) {
-            const unsigned long long ki = Z.ckey[t][i];
-            const int ei = Z.ce[t][i];
-            int rank = 0;
-            // eight candidates per round, loads issued together
-            for (int j0 = 0; j0 < m; j0 += 8) {
-                unsigned long long kj[8];
-                int ej[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = min(j0 + u, m - 1);
-                    kj[u] = Z.ckey[t][j];
-                    ej[u] = Z.ce[t][j];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    rank += (j0 + u < m && (kj[u] > ki || (kj[u] == ki && ej[u] < ei))) ? 1 : 0;
-            }
-            if (rank < K) {
-                R.idx[t][rank] = ei;
-                R.flat[t * K + rank] = ei;
-                Z.ssel[t][rank] = Z.cs[t][i];
-            }
-        }
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < T * K) {
-        const int t = threadIdx.x / K, k = threadIdx.x - t * K;
-        double sv[16];
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) sv[kk] = Z.ssel[t][min(kk, K - 1)];
-        double sum = 0.0;
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk)
-            if (kk < K) sum += sv[kk];  // k ascending
-        double v = Z.ssel[t][k];
-        if (norm) v = v / sum;
-        v = v * rho;
-        R.w[t][k] = (float)v;
-    }
-}
-
-// Fills R (in LDS) for T tokens; must be called by the whole workgroup
-// (blockDim.x >= E).
-__device__ __forceinline__ void route_small(const double* sig, const double* cval, int T, int E, int K, int S,
-                            int norm, double rho, GroupSel gsel, Route& R, TopkScratch& Z) {
-    topk_wg(sig, cval, T, E, K, norm, rho, gsel, R, Z);
-    __syncthreads();
-    // entries j = t K + k in (token, k) order; entry j belongs to an earlier
-    // token than entry i exactly when j < t_i K
-    const int n = T * K;
-    const int i = threadIdx.x;
-    int e = 0, t = 0, k = 0, rank = 0, first = 1, cnt = 0;
-    if (i < n) {
-        t = i / K;
-        k = i - t * K;
-        e = R.flat[i];
-        const int tk = t * K;
-        for (int j0 = 0; j0 < n; j0 += 8) {
-            int ej[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) ej[u] = R.flat[min(j0 + u, n - 1)];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u;
-                if (j < n) {
-                    if (ej[u] < e || (ej[u] == e && j < tk)) ++rank;
-                    if (ej[u] == e) {
-                        ++cnt;
-                        if (j < tk) first = 0;
-                    }
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (i < n) {
-        R.ent_e[rank] = e;
-        R.ent_t[rank] = t;
-        R.ent_w[rank] = R.w[t][k];
-        R.slot_of[t][k] = rank;
-    }
-    if (i < T && S) R.slot_of[i][K] = n + i;
-    __syncthreads();
-    // u = number of distinct experts below e = number of sorted entries j
-    // that start a new expert run and hold an expert < e
-    if (i < n && first) {
-        int u = 0;
-        for (int j0 = 0; j0 < n; j0 += 8) {
-            int ej[8], ep[8];
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const int j = min(j0 + v, n - 1);
-                ej[v] = R.ent_e[j];
-                ep[v] = R.ent_e[max(j - 1, 0)];
-            }
-#pragma unroll
-            for (int v = 0; v < 8; ++v) {
-                const int j = j0 + v;
-                if (j < n && (j == 0 || ep[v] != ej[v]) && ej[v] < e) ++u;
-            }
-        }
-        R.u_e[u] = e;
-        R.u_s0[u] = rank;
-        R.u_n[u] = cnt;
-        // the largest expert's run ends the sorted entries: u + 1 experts
-        if (rank + cnt == n) R.n_uniq = u + 1;
-    }
-    __syncthreads();
-}
-
 // Cross-lane moves of 64-bit values without LDS: a DPP move (CTRL: quad
 // permute, half-row or row mirror) or a read of one lane into all lanes.
 template <int CTRL>
@@ -482,18 +226,20 @@ __device__ __forceinline__ unsigned long long readlane64(unsigned long long v, i
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E;  // quad permutes [1,0,3,2], [2,3,0,1]
 constexpr int kDppRowMirror = 0x140, kDppHalfMirror = 0x141;
 
-// Routing of a single token by one wave (wave 0), the other waves waiting
-// at one barrier; same selection rule and results as route_small. Lane L
-// holds experts 4L .. 4L+3 (E <= 256). The smallest of the 32-expert group
-// maxima (8 lanes per group) is found with lane shuffles; the experts at or
-// above it are compacted into LDS with ballots and ranked by who is ahead
-// (c descending, index ascending). All LDS traffic stays within the wave,
-// whose LDS operations complete in program order.
-__device__ __forceinline__ void route_one(const double* sig, const double* cval, int E, int K,
+// Top-k of token t by one wave, which uses only row t of the scratch: idx,
+// flat entries t K + k and gates w of token t. Lane L holds experts 4L ..
+// 4L+3 (E <= 256). The smallest of the 32-expert group maxima (8 lanes per
+// group) is found with lane shuffles; the experts at or above it are
+// compacted into LDS with ballots and ranked by who is ahead (c descending,
+// index ascending); the gates are summed in k order. All LDS traffic stays
+// within the wave, whose LDS operations complete in program order. With ONE
+// (a single token) the wave also fills the sorted entries and the expert list.
+template <bool ONE>
+__device__ __forceinline__ void topk_wave(const double* sig, const double* cval, int E, int K,
                                           int S, int norm, double rho, GroupSel gsel, Route& R,
-                                          TopkScratch& Z) {
+                                          TopkScratch& Z, int t) {
     const int lane = threadIdx.x & 63;
-    if (threadIdx.x < 64) {
+    {
         unsigned long long key[4];
         double sv[4], cv[4];
         bool ok[4];
@@ -546,11 +292,11 @@ __device__ __forceinline__ void route_one(const double* sig, const double* cval,
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (ok[j]) Z.cs[1][4 * lane + j] = cv[j];  // row 1 is free here
+                    if (ok[j]) Z.cs[t][4 * lane + j] = cv[j];  // free until the compaction
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const unsigned long long keep = group_keep_mask(Z.cs[1], gsel);
+                const unsigned long long keep = group_keep_mask(Z.cs[t], gsel);
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (ok[j] && !((keep >> ((4 * lane + j) / gsel.gs)) & 1ull)) {
@@ -602,9 +348,9 @@ __device__ __forceinline__ void route_one(const double* sig, const double* cval,
             const unsigned long long bal = __ballot(c);
             if (c) {
                 const int p = base + __popcll(bal & ((1ull << lane) - 1ull));
-                Z.ckey[0][p] = key[j];
-                Z.ce[0][p] = 4 * lane + j;
-                Z.cs[0][p] = sv[j];
+                Z.ckey[t][p] = key[j];
+                Z.ce[t][p] = 4 * lane + j;
+                Z.cs[t][p] = sv[j];
             }
             base += __popcll(bal);
         }
@@ -612,9 +358,9 @@ __device__ __forceinline__ void route_one(const double* sig, const double* cval,
         if (m <= 64) {
             // one candidate per lane; the others broadcast from their lanes
             const bool has = lane < m;
-            const unsigned long long ki = has ? Z.ckey[0][lane] : 0ull;
-            const int ei = has ? Z.ce[0][lane] : 0x7fffffff;
-            const double si = has ? Z.cs[0][lane] : 0.0;
+            const unsigned long long ki = has ? Z.ckey[t][lane] : 0ull;
+            const int ei = has ? Z.ce[t][lane] : 0x7fffffff;
+            const double si = has ? Z.cs[t][lane] : 0.0;
             int rank = 0;
             for (int j = 0; j < m; ++j) {  // uniform
                 const unsigned long long kj = readlane64(ki, j);
@@ -641,21 +387,23 @@ __device__ __forceinline__ void route_one(const double* sig, const double* cval,
                 if (norm) v = v / sum;
                 v = v * rho;
                 const float w = (float)v;
-                R.idx[0][rank] = ei;
-                R.flat[rank] = ei;
-                R.w[0][rank] = w;
-                R.ent_e[slot] = ei;
-                R.ent_t[slot] = 0;
-                R.ent_w[slot] = w;
-                R.slot_of[0][rank] = slot;
-                R.u_e[slot] = ei;
-                R.u_s0[slot] = slot;
-                R.u_n[slot] = 1;
+                R.idx[t][rank] = ei;
+                R.flat[t * K + rank] = ei;
+                R.w[t][rank] = w;
+                if (ONE) {  // one token: sorted entries = experts ascending
+                    R.ent_e[slot] = ei;
+                    R.ent_t[slot] = 0;
+                    R.ent_w[slot] = w;
+                    R.slot_of[0][rank] = slot;
+                    R.u_e[slot] = ei;
+                    R.u_s0[slot] = slot;
+                    R.u_n[slot] = 1;
+                }
             }
         } else {
             for (int i = lane; i < m; i += 64) {
-                const unsigned long long ki = Z.ckey[0][i];
-                const int ei = Z.ce[0][i];
+                const unsigned long long ki = Z.ckey[t][i];
+                const int ei = Z.ce[t][i];
                 int rank = 0;
                 for (int j0 = 0; j0 < m; j0 += 8) {
                     unsigned long long kj[8];
@@ -663,17 +411,17 @@ __device__ __forceinline__ void route_one(const double* sig, const double* cval,
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
                         const int j = min(j0 + u, m - 1);
-                        kj[u] = Z.ckey[0][j];
-                        ej[u] = Z.ce[0][j];
+                        kj[u] = Z.ckey[t][j];
+                        ej[u] = Z.ce[t][j];
                     }
 #pragma unroll
                     for (int u = 0; u < 8; ++u)
                         rank += (j0 + u < m && (kj[u] > ki || (kj[u] == ki && ej[u] < ei))) ? 1 : 0;
                 }
                 if (rank < K) {
-                    R.idx[0][rank] = ei;
-                    R.flat[rank] = ei;
-                    Z.ssel[0][rank] = Z.cs[0][i];
+                    R.idx[t][rank] = ei;
+                    R.flat[t * K + rank] = ei;
+                    Z.ssel[t][rank] = Z.cs[t][i];
                 }
             }
             if (lane < K) {
@@ -681,37 +429,102 @@ __device__ __forceinline__ void route_one(const double* sig, const double* cval,
                 int ix[16];
 #pragma unroll
                 for (int kk = 0; kk < 16; ++kk) {
-                    ss[kk] = Z.ssel[0][min(kk, K - 1)];
-                    ix[kk] = R.idx[0][min(kk, K - 1)];
+                    ss[kk] = Z.ssel[t][min(kk, K - 1)];
+                    ix[kk] = R.idx[t][min(kk, K - 1)];
                 }
                 double sum = 0.0;
 #pragma unroll
                 for (int kk = 0; kk < 16; ++kk)
                     if (kk < K) sum += ss[kk];  // k ascending
-                double v = Z.ssel[0][lane];
+                double v = Z.ssel[t][lane];
                 if (norm) v = v / sum;
                 v = v * rho;
                 const float w = (float)v;
-                R.w[0][lane] = w;
-                // the K experts are distinct: slot = number of chosen experts below
-                const int e = R.idx[0][lane];
-                int slot = 0;
+                R.w[t][lane] = w;
+                if (ONE) {
+                    // the K experts are distinct: slot = number of chosen experts below
+                    const int e = R.idx[t][lane];
+                    int slot = 0;
 #pragma unroll
-                for (int kk = 0; kk < 16; ++kk)
-                    if (kk < K && ix[kk] < e) ++slot;
-                R.ent_e[slot] = e;
-                R.ent_t[slot] = 0;
-                R.ent_w[slot] = w;
-                R.slot_of[0][lane] = slot;
-                R.u_e[slot] = e;
-                R.u_s0[slot] = slot;
-                R.u_n[slot] = 1;
+                    for (int kk = 0; kk < 16; ++kk)
+                        if (kk < K && ix[kk] < e) ++slot;
+                    R.ent_e[slot] = e;
+                    R.ent_t[slot] = 0;
+                    R.ent_w[slot] = w;
+                    R.slot_of[0][lane] = slot;
+                    R.u_e[slot] = e;
+                    R.u_s0[slot] = slot;
+                    R.u_n[slot] = 1;
+                }
             }
         }
-        if (lane == 0) {
+        if (ONE && lane == 0) {
             R.n_uniq = K;
             if (S) R.slot_of[0][K] = K;
         }
+    }
+}
+
+// Routing of one token by wave 0 (the others wait at one barrier).
+__device__ __forceinline__ void route_one(const double* sig, const double* cval, int E, int K,
+                                          int S, int norm, double rho, GroupSel gsel, Route& R,
+                                          TopkScratch& Z) {
+    if (threadIdx.x < 64) topk_wave<true>(sig, cval, E, K, S, norm, rho, gsel, R, Z, 0);
+    __syncthreads();
+}
+
+// Fills R (in LDS) for T <= 4 tokens; called by the whole workgroup.
+__device__ __forceinline__ void route_small(const double* sig, const double* cval, int T, int E, int K, int S,
+                            int norm, double rho, GroupSel gsel, Route& R, TopkScratch& Z) {
+    // wave t routes token t (T <= 4 waves)
+    const int wv = threadIdx.x >> 6;
+    if (wv < T)
+        topk_wave<false>(sig + (int64_t)wv * E, cval + (int64_t)wv * E, E, K, S, norm, rho, gsel,
+                         R, Z, wv);
+    __syncthreads();
+    // Bucketing by wave 0, lane i holding entry i = t K + k ((token, k)
+    // order, T K <= 64): its sorted position is the number of entries with a
+    // smaller expert plus those of the same expert from earlier tokens; the
+    // expert's list index is the number of distinct smaller experts (entries
+    // that open an expert's run). Uniform loops over the entries, broadcast by
+    // lane reads.
+    if (threadIdx.x < 64) {
+        const int n = T * K;
+        const int lane = threadIdx.x;
+        const bool has = lane < n;
+        const int t = has ? lane / K : 0, k = has ? lane - t * K : 0;
+        const int e = has ? R.flat[lane] : 0x7fffffff;
+        int rank = 0, cnt = 0, first = 1;
+        for (int j = 0, tj = 0, kj = 0; j < n; ++j) {  // uniform
+            const int ej = __builtin_amdgcn_readlane(e, j);
+            rank += (ej < e || (ej == e && tj < t)) ? 1 : 0;
+            cnt += (ej == e) ? 1 : 0;
+            if (ej == e && tj < t) first = 0;
+            if (++kj == K) {
+                kj = 0;
+                ++tj;
+            }
+        }
+        int u = 0;
+        for (int j = 0; j < n; ++j) {  // uniform
+            const int ej = __builtin_amdgcn_readlane(e, j);
+            const int fj = __builtin_amdgcn_readlane(first, j);
+            u += (fj && ej < e) ? 1 : 0;
+        }
+        if (has) {
+            R.ent_e[rank] = e;
+            R.ent_t[rank] = t;
+            R.ent_w[rank] = R.w[t][k];
+            R.slot_of[t][k] = rank;
+            if (first) {
+                R.u_e[u] = e;
+                R.u_s0[u] = rank;
+                R.u_n[u] = cnt;
+                // the largest expert's run ends the sorted entries: u + 1 experts
+                if (rank + cnt == n) R.n_uniq = u + 1;
+            }
+        }
+        if (lane < T && S) R.slot_of[lane][K] = n + lane;
     }
     __syncthreads();
 }
@@ -870,13 +683,14 @@ __device__ __forceinline__ void gateup_block(const DecArgs& a, int e, int hb, in
 }
 
 // As gateup_block for experts with several tokens: the Q8_0 codes and
-// scales of the n tokens are staged in LDS (xs: n rows of H bytes, xds: n
-// rows of H/32 scales) and read per step, one token at a time, so the
-// activations do not occupy registers for the whole kernel.
+// scales of all T tokens are staged in LDS (xs: T rows of H bytes, xds: T
+// rows of H/32 scales); the expert's n tokens are rows tok[0..n) and are read
+// per step, one token at a time, so the activations do not occupy registers
+// for the whole kernel.
 template <int NT, int NBJ, bool TAP, int BITS>
 __device__ __forceinline__ void gateup_block_lds(const DecArgs& a, int e, int hb, int n,
-                                                 int slot0, const uint8_t* xs, const float* xds,
-                                                 float (*hbuf)[32]) {
+                                                 const int* tok, int slot0, const uint8_t* xs,
+                                                 const float* xds, float (*hbuf)[32]) {
     typedef DW<BITS> F;
     typedef typename F::blk Blk;
     constexpr int HR = F::HR, RQ = 2 * HR, NS = 8 / HR;
@@ -906,6 +720,9 @@ __device__ __forceinline__ void gateup_block_lds(const DecArgs& a, int e, int hb
     if (NS > 1) load_pair(1, wb[1]);
     const float gsl = gs[r0 + 4 * (lane & 7)];
     const float usl = us[r0 + 4 * (lane & 7)];
+    int tk[NT];  // staged row of the i-th token
+#pragma unroll
+    for (int i = 0; i < NT; ++i) tk[i] = __builtin_amdgcn_readfirstlane(tok[min(i, n - 1)]);
     constexpr int V = RQ * NT;  // values per step, a power of two
     constexpr int kShift = 6 - ((V >= 32) ? 5 : (V >= 16) ? 4 : (V >= 8) ? 3 : (V >= 4) ? 2 : 1);
 #pragma unroll
@@ -923,9 +740,9 @@ __device__ __forceinline__ void gateup_block_lds(const DecArgs& a, int e, int hb
 #pragma unroll
                 for (int j = 0; j < NBJ; ++j) {
                     const int b = lane + 64 * j, bb = min(b, BH - 1);
-                    const uint4* px = reinterpret_cast<const uint4*>(xs + i * H + bb * 32);
+                    const uint4* px = reinterpret_cast<const uint4*>(xs + tk[i] * H + bb * 32);
                     const uint4 x0 = px[0], x1 = px[1];
-                    const double xd = (b < BH) ? (double)xds[i * BH + bb] * F::kInv : 0.0;
+                    const double xd = (b < BH) ? (double)xds[tk[i] * BH + bb] * F::kInv : 0.0;
 #pragma unroll
                     for (int q = 0; q < RQ; ++q) {
                         const int dq = F::dot(wc[q][j], x0, x1);
@@ -973,20 +790,16 @@ __device__ __forceinline__ void gateup_block_lds(const DecArgs& a, int e, int hb
     __syncthreads();  // hbuf is reused by the workgroup's next h-block
 }
 
-// Copies the Q8_0 codes and scales of tokens tok[0..n) into LDS (xs, xds).
-__device__ __forceinline__ void stage_tokens(const DecArgs& a, const int* tok, int n, uint8_t* xs,
-                                             float* xds) {
-    const int H = a.H, BH = H >> 5, V = H >> 4;  // uint4 per row
-    for (int x = threadIdx.x; x < n * V; x += blockDim.x) {
-        const int i = x / V, c = x - i * V;
-        reinterpret_cast<uint4*>(xs + i * H)[c] =
-            reinterpret_cast<const uint4*>(a.qx + (int64_t)tok[i] * H)[c];
-    }
-    for (int x = threadIdx.x; x < n * BH; x += blockDim.x) {
-        const int i = x / BH, c = x - i * BH;
-        xds[i * BH + c] = a.dx[(int64_t)tok[i] * BH + c];
-    }
-    __syncthreads();
+// Copies the Q8_0 codes and scales of all T tokens into LDS rows xs[t]
+// (H bytes) and xds[t] (H/32 scales), by threads tid0 .. tid0 + nt - 1.
+__device__ __forceinline__ void stage_all_tokens(const DecArgs& a, uint8_t* xs, float* xds,
+                                                 int tid0, int nt) {
+    const int V = a.H >> 4, BH = a.H >> 5;  // 16-byte pieces and scales per row
+    const int nq = a.T * V, nd = a.T * BH;   // rows are contiguous on both sides
+    const int i0 = (int)threadIdx.x - tid0;
+    for (int x = i0; x < nq; x += nt)
+        reinterpret_cast<v4u*>(xs)[x] = reinterpret_cast<const v4u*>(a.qx)[x];
+    for (int x = i0; x < nd; x += nt) xds[x] = a.dx[x];
 }
 
 // Publishes the routing computed in R (one workgroup of B) for C, the taps
@@ -1099,19 +912,17 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
 // expert in use (u < min(E, T*K)); block (u = 0, hb = 0) publishes routing.
 template <int NT, int NBJ, bool TAP, int BITS>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
-    // several tokens: activations staged in LDS, sharing space with the
-    // top-k scratch (dead by then); H <= 6144 on this path
+    // several tokens: every token's Q8_0(x) staged in LDS beside the top-k
+    // scratch, so that a wave with no token to route can stage it meanwhile;
+    // H <= 6144 on this path
     constexpr int kAct = (NT > 1) ? NT * 6144 + NT * 192 * 4 : 16;
-    union Shared {
-        TopkScratch z;
-        uint8_t act[kAct];
-    };
-    __shared__ __align__(16) Shared U;
+    __shared__ TopkScratch Z;
+    __shared__ __align__(16) uint8_t act[kAct];
     __shared__ Route R;
     __shared__ float hbuf[NT][32];
     __shared__ int s_tok[NT];
-    uint8_t* xs = U.act;
-    float* xds = reinterpret_cast<float*>(U.act + NT * a.H);
+    uint8_t* xs = act;
+    float* xds = reinterpret_cast<float*>(act + NT * a.H);
     // a workgroup covers HB consecutive h-blocks of 32 rows (one at a single
     // token; two with several, so fewer workgroups redo the routing)
     constexpr int HB = (NT > 1) ? 2 : 1;
@@ -1120,13 +931,15 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
     if (a.S) {
         if (b < nw) {
             if ((int)threadIdx.x < NT) s_tok[threadIdx.x] = min((int)threadIdx.x, a.T - 1);
-            __syncthreads();
             if (NT > 1) {
-                stage_tokens(a, s_tok, a.T, xs, xds);
+                stage_all_tokens(a, xs, xds, 0, 256);
+                __syncthreads();
 #pragma unroll 1
                 for (int h = 0; h < HB; ++h)
-                    gateup_block_lds<NT, NBJ, TAP, BITS>(a, a.E, b * HB + h, a.T, a.T * a.K, xs, xds, hbuf);
+                    gateup_block_lds<NT, NBJ, TAP, BITS>(a, a.E, b * HB + h, a.T, s_tok, a.T * a.K,
+                                                         xs, xds, hbuf);
             } else {
+                __syncthreads();
                 gateup_block<NT, NBJ, TAP, BITS>(a, a.E, b, a.T, s_tok, a.T * a.K, hbuf);
             }
             return;
@@ -1135,11 +948,15 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
     }
     // the routing waves win issue slots over co-resident streaming waves:
     // routing latency sits on the path to this workgroup's first weight load
+    // with fewer than four tokens the last wave, which routes none, stages
+    // the activations while the others route
+    const bool stage_early = NT > 1 && a.T < 4;
+    if (stage_early && threadIdx.x >= 192) stage_all_tokens(a, xs, xds, 192, 64);
     __builtin_amdgcn_s_setprio(3);
     if (NT == 1)
-        route_one(a.sig, a.cval, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
+        route_one(a.sig, a.cval, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, Z);
     else
-        route_small(a.sig, a.cval, a.T, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, U.z);
+        route_small(a.sig, a.cval, a.T, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, Z);
     __builtin_amdgcn_s_setprio(0);
     if (b == 0) publish_route(a, R);
     const int u = b / nw, hw = b - u * nw;
@@ -1148,10 +965,14 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
     const int s0 = __builtin_amdgcn_readfirstlane(R.u_s0[u]);
     const int n = __builtin_amdgcn_readfirstlane(R.u_n[u]);
     if (NT > 1) {
-        stage_tokens(a, &R.ent_t[s0], n, xs, xds);
+        if (!stage_early) {
+            stage_all_tokens(a, xs, xds, 0, 256);
+            __syncthreads();
+        }
 #pragma unroll 1
         for (int h = 0; h < HB; ++h)
-            gateup_block_lds<NT, NBJ, TAP, BITS>(a, e, hw * HB + h, n, s0, xs, xds, hbuf);
+            gateup_block_lds<NT, NBJ, TAP, BITS>(a, e, hw * HB + h, n, &R.ent_t[s0], s0, xs, xds,
+                                                 hbuf);
     } else {
         gateup_block<NT, NBJ, TAP, BITS>(a, e, hw, n, &R.ent_t[s0], s0, hbuf);
     }
