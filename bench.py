@@ -165,7 +165,7 @@ def main():
     unique_counts = []
     if not args.no_profile:
         names = None
-        nev = 16
+        nev = 32  # start and stop of each launch
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
         for e in evs:
             e.record()
@@ -177,8 +177,9 @@ def main():
         for i in range(n_prof):
             names = C.coli_moe_forward_profiled(layers[i % R], xs[i], ys[i & 1], ws, handles)
             torch.cuda.synchronize()
-            for j in range(len(names) - 1):
-                sums[names[j]] = sums.get(names[j], 0.0) + evs[j].elapsed_time(evs[j + 1])
+            for j in range(len(names)):
+                sums[names[j]] = sums.get(names[j], 0.0) + \
+                    evs[2 * j].elapsed_time(evs[2 * j + 1])
             unique_counts.append(int((counts_view[:E] > 0).sum().item()) + S)
         kern = {k: v / n_prof for k, v in sums.items()}
     uniq_avg = float(np.mean(unique_counts)) if unique_counts else float(min(E, T * K) + S)
@@ -460,7 +461,7 @@ def run_stack(args, cfg):
     kern = {}
     uniq = []
     if not args.no_profile:
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(16)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(32)]  # 2 per launch
         for e in evs:
             e.record()
         torch.cuda.synchronize()
@@ -472,8 +473,9 @@ def run_stack(args, cfg):
             C.coli_rmsnorm(x, xn, 1e-5)
             names = C.coli_moe_forward_profiled(layers[l], xn, x, ws, hs, C.COLI_FWD_ACCUM)
             torch.cuda.synchronize()
-            for j in range(len(names) - 1):
-                kern[names[j]] = kern.get(names[j], 0.0) + evs[j].elapsed_time(evs[j + 1]) / NL
+            for j in range(len(names)):
+                kern[names[j]] = kern.get(names[j], 0.0) + \
+                    evs[2 * j].elapsed_time(evs[2 * j + 1]) / NL
             uniq.append(int((counts_view[:E] > 0).sum().item()) + S)
     uniq_avg = float(np.mean(uniq)) if uniq else float(E + S)
     gate_up_bytes = uniq_avg * (2 * I * H * bits // 8 + 4 * 2 * I) + T * (H + H // 8) + \

@@ -223,11 +223,15 @@ COLI_API int coli_moe_forward(const coli_moe_weights* w, const float* x, int64_t
                               float* y, void* ws, size_t ws_bytes, uint32_t flags,
                               void* stream);
 
-/* As coli_moe_forward, and additionally records the HIP events events[0..n-1]
- * (hipEvent_t passed as void*) on the stream before each kernel launch of the
- * forward and after the last one. Returns the number of launch boundaries in
- * *n_used (kernels + 1); events beyond n_events are not recorded. For timing
- * single kernels; results are identical to coli_moe_forward. */
+/* As coli_moe_forward, and additionally times each kernel launch of the
+ * forward: launch j is enqueued with hipExtLaunchKernel and its own start and
+ * stop events, events[2j] and events[2j + 1] (hipEvent_t passed as void*,
+ * created with timing), which the packet processor stamps at the kernel's
+ * begin and end, so that hipEventElapsedTime gives the kernel's duration
+ * without the gaps between launches. names[j] (the caller's array of at least
+ * n_events / 2 entries, or null) receives a static name of launch j. Returns
+ * the number of launches in *n_used; launches past n_events / 2 run untimed.
+ * Results are identical to coli_moe_forward. */
 COLI_API int coli_moe_forward_profiled(const coli_moe_weights* w, const float* x,
                                        int64_t n_tok, float* y, void* ws, size_t ws_bytes,
                                        uint32_t flags, void* stream, void* const* events,

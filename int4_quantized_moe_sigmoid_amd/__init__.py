@@ -241,10 +241,11 @@ def coli_moe_forward(weights: LayerWeights, x: torch.Tensor, y: torch.Tensor, ws
 def coli_moe_forward_profiled(weights: LayerWeights, x: torch.Tensor, y: torch.Tensor,
                               ws: torch.Tensor, events: Sequence[int], flags: int = 0,
                               stream=None):
-    """events: raw hipEvent_t handles. Returns the launch-boundary names used."""
+    """events: raw hipEvent_t handles, two per launch (start, stop of launch j at
+    2j, 2j + 1). Returns the names of the launches timed."""
     n = len(events)
     arr = (ctypes.c_void_p * max(n, 1))(*events)
-    names = (ctypes.c_char_p * max(n, 1))()
+    names = (ctypes.c_char_p * max(n // 2, 1))()
     used = ctypes.c_int(0)
     _check(_lib.coli_moe_forward_profiled(ctypes.byref(weights.struct),
                                           _dev(x, "x", torch.float32), x.shape[0],
@@ -252,7 +253,7 @@ def coli_moe_forward_profiled(weights: LayerWeights, x: torch.Tensor, y: torch.T
                                           _dev(ws, "ws", torch.uint8), ws.numel(), flags,
                                           _stream(stream), arr, n, ctypes.byref(used), names),
            "coli_moe_forward_profiled")
-    return [names[i].decode() for i in range(min(used.value, n))]
+    return [names[i].decode() for i in range(min(used.value, n // 2))]
 
 
 def coli_rmsnorm(x: torch.Tensor, out: torch.Tensor, eps: float = 1e-5, stream=None):

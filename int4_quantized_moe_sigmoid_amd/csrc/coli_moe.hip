@@ -1,6 +1,7 @@
 // Host side of the C ABI (include/coli_moe.h): argument checks, workspace
 // layout, kernel selection and launches. No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cmath>
@@ -119,27 +120,49 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
     P.total = off;
 }
 
-// Optional event marks between launches (coli_moe_forward_profiled).
+// Optional per-launch timing (coli_moe_forward_profiled): mark() names the
+// next launch; launch j then carries events 2j (start) and 2j + 1 (stop),
+// which the packet processor stamps at the kernel's own begin and end.
 struct Marks {
     hipStream_t s;
     void* const* ev = nullptr;
     const char** names = nullptr;
-    int n = 0, used = 0;
-    void mark(const char* name) {
-        if (ev && used < n) (void)hipEventRecord((hipEvent_t)ev[used], s);
-        if (names && used < n) names[used] = name;
+    int n = 0, used = 0;  // n events, used launches so far
+    const char* pending = "";
+    void mark(const char* name) { pending = name; }
+    void take(hipEvent_t* e0, hipEvent_t* e1) {
+        *e0 = *e1 = nullptr;
+        if (ev && 2 * used + 1 < n) {
+            *e0 = (hipEvent_t)ev[2 * used];
+            *e1 = (hipEvent_t)ev[2 * used + 1];
+            if (names) names[used] = pending;
+        }
         ++used;
     }
 };
+
+// kernel<<<grid, block, shmem, s>>>(args...), with the launch's own start and
+// stop events when profiling.
+template <typename... P, typename... A>
+void launch(Marks& mk, void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+            A&&... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    hipEvent_t e0, e1;
+    mk.take(&e0, &e1);
+    if (e0)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, static_cast<P>(args)...);
+    else
+        kernel<<<grid, block, shmem, s>>>(static_cast<P>(args)...);
+}
 
 template <int NT>
 void launch_gateup_nt(int nbj, dim3 grid, hipStream_t s, const coli_moe_weights* w,
                       int64_t blob_q, int64_t blob_s, const int8_t* qx, const float* dx,
                       ItemArgs it, const int32_t* slot_tok, int8_t* qh, float* dh, int32_t* tap,
-                      int tap_rows, int tap_stride) {
+                      int tap_rows, int tap_stride, Marks& mk) {
     const int H = w->cfg.hidden, I = w->cfg.inter;
 #define COLI_GU(NBJ)                                                                          \
-    k_gateup_gemv<NT, NBJ><<<grid, 256, 0, s>>>(w->experts_q, w->experts_scale, blob_q, blob_s, \
+    launch(mk, k_gateup_gemv<NT, NBJ>, grid, 256, 0, s, w->experts_q, w->experts_scale, blob_q, blob_s, \
                                                 qx, dx, it, slot_tok, H, I, qh, dh, tap,        \
                                                 tap_rows, tap_stride)
     switch (nbj) {
@@ -154,10 +177,10 @@ void launch_gateup_nt(int nbj, dim3 grid, hipStream_t s, const coli_moe_weights*
 template <int NT>
 void launch_down_nt(int nbj, dim3 grid, hipStream_t s, const coli_moe_weights* w,
                     int64_t blob_q, int64_t blob_s, const int8_t* qh, const float* dh,
-                    ItemArgs it, float* ye) {
+                    ItemArgs it, float* ye, Marks& mk) {
     const int H = w->cfg.hidden, I = w->cfg.inter;
 #define COLI_DN(NBJ)                                                                          \
-    k_down_gemv<NT, NBJ><<<grid, 256, 0, s>>>(w->experts_q, w->experts_scale, blob_q, blob_s, \
+    launch(mk, k_down_gemv<NT, NBJ>, grid, 256, 0, s, w->experts_q, w->experts_scale, blob_q, blob_s, \
                                               qh, dh, it, H, I, ye)
     switch (nbj) {
         case 1: COLI_DN(1); break;
@@ -185,19 +208,19 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
     mk.mark("router_logits");
     if (T <= 8) {
         if (T <= 1)
-            k_router_gemv<1><<<E, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
+            launch(mk, k_router_gemv<1>, E, 256, 0, s, x, wr, (int)T, H, E, logits);
         else if (T <= 4)
-            k_router_gemv<4><<<E, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
+            launch(mk, k_router_gemv<4>, E, 256, 0, s, x, wr, (int)T, H, E, logits);
         else
-            k_router_gemv<8><<<E, 256, 0, s>>>(x, wr, (int)T, H, E, logits);
+            launch(mk, k_router_gemv<8>, E, 256, 0, s, x, wr, (int)T, H, E, logits);
     } else {
         const int ks = router_ksplit(H, T, E);
         dim3 g((unsigned)((T + kRouterTile - 1) / kRouterTile),
                (unsigned)((E + kRouterTile - 1) / kRouterTile), (unsigned)ks);
-        k_router_gemm<<<g, 256, 0, s>>>(x, wr, (int)T, H, E, ks, rpart);
+        launch(mk, k_router_gemm, g, 256, 0, s, x, wr, (int)T, H, E, ks, rpart);
         const int64_t n = T * E;
         mk.mark("router_reduce");
-        k_router_reduce<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(rpart, ks, n, logits);
+        launch(mk, k_router_reduce, (unsigned)((n + 255) / 256), 256, 0, s, rpart, ks, n, logits);
     }
     mk.mark("topk");
     const unsigned gb = (unsigned)((T + 3) / 4);
@@ -207,15 +230,15 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
     // with groups, each wave stages its token's biased scores in LDS
     const size_t tk_lds = gsel.ng > 1 ? (size_t)4 * E * sizeof(double) : 0;
     if (E <= 64)
-        k_topk<1><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
+        launch(mk, k_topk<1>, gb, 256, tk_lds, s, logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else if (E <= 128)
-        k_topk<2><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
+        launch(mk, k_topk<2>, gb, 256, tk_lds, s, logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else if (E <= 256)
-        k_topk<4><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
+        launch(mk, k_topk<4>, gb, 256, tk_lds, s, logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else if (E <= 512)
-        k_topk<8><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
+        launch(mk, k_topk<8>, gb, 256, tk_lds, s, logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else
-        k_topk<16><<<gb, 256, tk_lds, s>>>(logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
+        launch(mk, k_topk<16>, gb, 256, tk_lds, s, logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
 }
 
 // Template selection for the fused few-token path.
@@ -234,16 +257,16 @@ void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     const int nrb = a.I / 32;
     mk.mark("dec_router");
     const int qb = (a.T * (a.H / 32) + 7) / 8;  // workgroups needed for Q8_0(x)
-    dec::k_dec_router<NT, BITS><<<(a.E > qb) ? a.E : qb, 256, 0, s>>>(a);
+    launch(mk, dec::k_dec_router<NT, BITS>, (a.E > qb) ? a.E : qb, 256, 0, s, a);
     mk.mark("dec_gateup");
     const int um = (a.T * a.K < a.E) ? a.T * a.K : a.E;
     const int hbw = (NT > 1) ? 2 : 1;  // h-blocks per workgroup (k_dec_gateup)
-    dec::k_dec_gateup<NT, NBJH, TAP, BITS><<<(a.S + um) * (nrb / hbw), 256, 0, s>>>(a);
+    launch(mk, dec::k_dec_gateup<NT, NBJH, TAP, BITS>, (a.S + um) * (nrb / hbw), 256, 0, s, a);
     mk.mark("dec_down");
     if (NT == 4)
-        dec::k_dec_down_x<NT, 1, BITS><<<a.H / 8, 256, 0, s>>>(a);
+        launch(mk, dec::k_dec_down_x<NT, 1, BITS>, a.H / 8, 256, 0, s, a);
     else
-        dec::k_dec_down<NT, 1, 2, 2, BITS><<<a.H / 8, 256, 0, s>>>(a);
+        launch(mk, dec::k_dec_down<NT, 1, 2, 2, BITS>, a.H / 8, 256, 0, s, a);
 }
 
 template <int NT, int BITS>
@@ -339,7 +362,6 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         a.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
         a.y = y; a.accum = (flags & COLI_FWD_ACCUM) ? 1 : 0;
         launch_small(a, bits, s, mk);
-        mk.mark("end");
         return hip_status();
     }
 
@@ -347,9 +369,9 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
     const int64_t nblk = T * (H / 32);
     // activations in the element order of the weight width's operand
     const unsigned qg = (unsigned)((nblk * 4 + 255) / 256);
-    if (bits == 4) k_quant_q8<1><<<qg, 256, 0, s>>>(x, nblk, qx, dx);
-    else if (bits == 2) k_quant_q8<2><<<qg, 256, 0, s>>>(x, nblk, qx, dx);
-    else k_quant_q8<0><<<qg, 256, 0, s>>>(x, nblk, qx, dx);
+    if (bits == 4) launch(mk, k_quant_q8<1>, qg, 256, 0, s, x, nblk, qx, dx);
+    else if (bits == 2) launch(mk, k_quant_q8<2>, qg, 256, 0, s, x, nblk, qx, dx);
+    else launch(mk, k_quant_q8<0>, qg, 256, 0, s, x, nblk, qx, dx);
 
     launch_route(c, x, w->w_router, w->bias, T, logits,
                  reinterpret_cast<double*>(base + L.rpart), idx, wts, s, mk);
@@ -357,9 +379,9 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
     const int ch = mfma ? pf::kTok : L.ch;
     const int64_t n_it = max_items_for(c, T, ch);
     mk.mark("bucket_lists");
-    k_bucket_lists<<<E + S, 256, 0, s>>>(idx, (int)T, K, E, S, lists, counts);
+    launch(mk, k_bucket_lists, E + S, 256, 0, s, idx, (int)T, K, E, S, lists, counts);
     mk.mark("bucket_scan");
-    k_bucket_scan<<<1, 1024, 0, s>>>(counts, lists, (int)T, K, E, S, ch, offs, slot_of,
+    launch(mk, k_bucket_scan, 1, 1024, 0, s, counts, lists, (int)T, K, E, S, ch, offs, slot_of,
                                      slot_tok, it.item_e, it.item_s0, it.item_n, n_items);
 
     if (mfma) {
@@ -375,20 +397,20 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         const dim3 g1((unsigned)((I / pf::kRows) * n_it));
         const dim3 g2((unsigned)((H / pf::kRows) * n_it));
         if (bits == 4) {
-            if (tap) pf::k_pf_gateup<4, true><<<g1, 256, 0, s>>>(pa);
-            else pf::k_pf_gateup<4, false><<<g1, 256, 0, s>>>(pa);
+            if (tap) launch(mk, pf::k_pf_gateup<4, true>, g1, 256, 0, s, pa);
+            else launch(mk, pf::k_pf_gateup<4, false>, g1, 256, 0, s, pa);
             mk.mark("pf_down");
-            pf::k_pf_down<4><<<g2, 256, 0, s>>>(pa);
+            launch(mk, pf::k_pf_down<4>, g2, 256, 0, s, pa);
         } else if (bits == 8) {
-            if (tap) pf::k_pf_gateup<8, true><<<g1, 256, 0, s>>>(pa);
-            else pf::k_pf_gateup<8, false><<<g1, 256, 0, s>>>(pa);
+            if (tap) launch(mk, pf::k_pf_gateup<8, true>, g1, 256, 0, s, pa);
+            else launch(mk, pf::k_pf_gateup<8, false>, g1, 256, 0, s, pa);
             mk.mark("pf_down");
-            pf::k_pf_down<8><<<g2, 256, 0, s>>>(pa);
+            launch(mk, pf::k_pf_down<8>, g2, 256, 0, s, pa);
         } else {
-            if (tap) pf::k_pf_gateup<2, true><<<g1, 256, 0, s>>>(pa);
-            else pf::k_pf_gateup<2, false><<<g1, 256, 0, s>>>(pa);
+            if (tap) launch(mk, pf::k_pf_gateup<2, true>, g1, 256, 0, s, pa);
+            else launch(mk, pf::k_pf_gateup<2, false>, g1, 256, 0, s, pa);
             mk.mark("pf_down");
-            pf::k_pf_down<2><<<g2, 256, 0, s>>>(pa);
+            launch(mk, pf::k_pf_down<2>, g2, 256, 0, s, pa);
         }
     } else {
     const int nt = (T >= L.ch) ? L.ch : (int)T;  // tokens per item at most
@@ -400,32 +422,31 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         const int tr = (int)L.pub.tap_rows, ts = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
         if (nt <= 1)
             launch_gateup_nt<1>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
-                                tap, tr, ts);
+                                tap, tr, ts, mk);
         else if (nt <= 2)
             launch_gateup_nt<2>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
-                                tap, tr, ts);
+                                tap, tr, ts, mk);
         else
             launch_gateup_nt<4>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
-                                tap, tr, ts);
+                                tap, tr, ts, mk);
     }
     mk.mark("down");
     {
         dim3 grid((unsigned)((H / 32) * L.max_items));
         if (nt <= 1)
-            launch_down_nt<1>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye);
+            launch_down_nt<1>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye, mk);
         else if (nt <= 2)
-            launch_down_nt<2>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye);
+            launch_down_nt<2>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye, mk);
         else
-            launch_down_nt<4>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye);
+            launch_down_nt<4>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye, mk);
     }
     }
     mk.mark("combine");
     {
         dim3 grid((unsigned)(((H + 255) / 256) * T));
-        k_combine<<<grid, 256, 0, s>>>(ye, slot_of, wts, K, S, H, y,
+        launch(mk, k_combine, grid, 256, 0, s, ye, slot_of, wts, K, S, H, y,
                                        (flags & COLI_FWD_ACCUM) ? 1 : 0);
     }
-    mk.mark("end");
     return hip_status();
 }
 
