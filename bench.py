@@ -532,8 +532,15 @@ def cpu_baseline(cfg, budget_s):
         OL.forward(x)
         timed += time.perf_counter() - t0
         n_tok += cfg.n_tok
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                             None)
+    except OSError:
+        pass
     return {"value": round(n_tok / timed, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"{n_tok} tokens of {cfg.name}, replica 0, one oracle forward per "
                       f"{cfg.n_tok} token(s), {timed:.1f} s timed"}
 
