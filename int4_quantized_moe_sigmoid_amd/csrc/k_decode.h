@@ -139,37 +139,6 @@ __device__ __forceinline__ double wave_reduce_tr(double* v, int lane) {
     return s;
 }
 
-// Q8_0 of block b of fp32 row x (32 values) into the 8-group order, in
-// registers: a0/a1 hold the 32 codes, returns the block scale.
-__device__ __forceinline__ float q8_block_regs(const float* x, uint4& a0, uint4& a1) {
-    const float4* p = reinterpret_cast<const float4*>(x);
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float4 f = p[i];
-        v[4 * i] = f.x;
-        v[4 * i + 1] = f.y;
-        v[4 * i + 2] = f.z;
-        v[4 * i + 3] = f.w;
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    const float d = amax / 127.0f;
-    int c[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) c[i] = q8_code(v[i], d);
-    uint32_t w[8];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        w[2 * g] = pack4_i8(c[8 * g], c[8 * g + 2], c[8 * g + 4], c[8 * g + 6]);
-        w[2 * g + 1] = pack4_i8(c[8 * g + 1], c[8 * g + 3], c[8 * g + 5], c[8 * g + 7]);
-    }
-    a0 = make_uint4(w[0], w[1], w[2], w[3]);
-    a1 = make_uint4(w[4], w[5], w[6], w[7]);
-    return d;
-}
-
 // Routing of T <= 4 tokens, computed redundantly by every workgroup of B.
 struct Route {
     int idx[kMaxTok][16];
