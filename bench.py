@@ -32,10 +32,12 @@ HBM_PEAK_GBPS = 8000.0
 # workload as the JSON line names it); dropped whenever that kernel changes.
 TRAFFIC = {
     # profiles/dec_kernels_decode_T1.txt
-    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55662.1 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55670.6 * 2 + 38.4) * 1024,
     # profiles/dec_kernels_decode_T1_int8.txt, profiles/dec_kernels_decode_T1_int2.txt
-    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int8 weights"): (111699.8 * 2 + 38.4) * 1024,
-    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int2 weights"): (27989.4 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int8 weights"): (111687.3 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int2 weights"): (28007.7 * 2 + 38.4) * 1024,
+    # profiles/dec_kernels_mtp_verify_T3.txt (mean over the counter run's steps)
+    ("dec_gateup", "mtp-verify T3 correlated"): (95923.0 * 2 + 84.8) * 1024,
     # profiles/pf_kernels_prefill_T512.txt
     ("pf_gateup", "prefill T512 zipf-bias"): (1749219.2 * 2 + 14454.1) * 1024,
     # profiles/pack_fp8_int4_layer.txt (the gate/up launch)
