@@ -111,7 +111,9 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
     if (flags & COLI_FWD_DEBUG_TAPS) {
         const int64_t per_row = NS * (H / 32);
         int64_t stride = 1;
-        while (per_row * ((I + stride - 1) / stride) > kTapBudget) stride *= 2;
+        // sampled gate rows (every stride-th) keep the tap near the budget; one
+        // row per slot at the least
+        while (stride < I && per_row * ((I + stride - 1) / stride) > kTapBudget) stride *= 2;
         P.tap_stride = stride;
         P.tap_rows = (I + stride - 1) / stride;
         P.tap = take(NS * P.tap_rows * (H / 32) * 4);

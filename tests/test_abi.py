@@ -46,3 +46,16 @@ def test_host_side_queries_without_gpu():
     big = C.make_cfg(6144, 2048, 2048, 8)
     rc = C.lib().coli_moe_workspace_layout(big, 1, 0, C.coli_moe_ws_layout())
     assert rc == C.COLI_E_UNSUPPORTED
+
+
+def test_debug_tap_layout_for_the_largest_token_count():
+    # the tap samples gate rows so that it stays near its budget; with so many
+    # slots that even one row per slot exceeds it, one row is kept
+    import int4_quantized_moe_sigmoid_amd as C
+    cfg = C.make_cfg(6144, 2048, 256, 8)
+    for T in (1, 4096, 1 << 20):
+        L = C.coli_moe_workspace_layout(cfg, T, C.COLI_FWD_DEBUG_TAPS)
+        assert 1 <= L.tap_rows <= 2048 and L.tap_stride >= 1
+        assert L.tap_rows == (2048 + L.tap_stride - 1) // L.tap_stride
+        assert C.coli_moe_workspace_bytes(cfg, T, C.COLI_FWD_DEBUG_TAPS) >= L.total
+    assert C.coli_moe_workspace_layout(cfg, 1 << 20, C.COLI_FWD_DEBUG_TAPS).tap_rows == 1
