@@ -165,3 +165,28 @@ def test_rejects_unsupported_widths(C):
     with pytest.raises(C.ColiError):
         C.coli_pack_weights(w, 3, torch.empty((2, 32), dtype=torch.uint8, device="cuda"),
                             torch.empty(2, device="cuda"))
+
+
+@pytest.mark.parametrize("bits,n_tok,shared,norm", [(8, 1, 0, False), (8, 3, 1, False),
+                                                     (2, 2, 0, True), (2, 7, 1, False),
+                                                     (8, 9, 0, True)])
+def test_widths_with_groups_and_degenerate_settings(C, ref, bits, n_tok, shared, norm):
+    # int8 / int2 weights together with group-limited selection (8 groups of
+    # 8 experts, 4 kept), no shared expert, gates not normalised; the fused
+    # kernels (up to four tokens, int2 two) and the MFMA kernels
+    cfg = dataclasses.replace(cs.CONFIGS[0], name=f"E64 K4 groups int{bits}", n_experts=64,
+                              top_k=4, n_shared=shared, norm_topk=norm, n_tok=n_tok)
+    _note("widths+groups", bits, n_tok, shared, norm)
+    wr, b, q, s = cs.build_layer(cfg, 0, "cuda",
+                                 lambda w, qv, sv: C.coli_pack_weights(w, bits, qv, sv), bits=bits)
+    W = C.LayerWeights(lib_cfg(C, cfg, n_group=8, topk_group=4, bits=bits), wr, b, q, s)
+    x = layer_input(ref, cfg)
+    y, taps = _run(C, W, x)
+    OL = oracle_layer_for(ref, cfg, 0, x, n_group=8, topk_group=4, bits=bits)
+    yo, to = OL.forward(x, taps=True)
+    np.testing.assert_array_equal(taps["qx"], to["qx"])
+    np.testing.assert_array_equal(taps["idx"], to["idx"])
+    np.testing.assert_allclose(taps["w"], to["w"], rtol=1e-6)
+    err = rel_l2(y, yo)
+    _note("rel_l2", err)
+    assert err <= TOL_REL_L2
