@@ -397,7 +397,7 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         pa.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
         mk.mark("pf_gateup");
         const dim3 g1((unsigned)((I / pf::kRows) * n_it));
-        const dim3 g2((unsigned)((H / pf::kRows) * n_it));
+        const dim3 g2((unsigned)(((H + pf::kDnRows - 1) / pf::kDnRows) * n_it));
         if (bits == 4) {
             if (tap) launch(mk, pf::k_pf_gateup<4, true>, g1, 256, 0, s, pa);
             else launch(mk, pf::k_pf_gateup<4, false>, g1, 256, 0, s, pa);

@@ -1,9 +1,9 @@
 // Grouped int8 MFMA kernels for many tokens (prefill, stacked layers).
 //
 // Work item = (expert, first slot, n <= 32 of its tokens). A workgroup takes
-// one item and a tile of 64 output rows; wave w owns rows 16w .. 16w+15 of
-// the tile (for gate/up: those gate rows and the matching up rows, so SwiGLU
-// needs no exchange). Per 32-wide block b every wave issues
+// one item and a tile of output rows; each wave owns two 16-row tiles (gate/up:
+// 16 gate rows and the matching 16 up rows, so SwiGLU needs no exchange; down:
+// 32 consecutive output rows). Per 32-wide block b every wave issues
 //   D = v_mfma_i32_16x16x32_i8(A = 16 weight rows, B = 16 tokens)
 // whose K extent is exactly one Q8_0 block, so D holds 16 x 16 exact block
 // dots (x16, see below); the fp64 epilogue adds d_b * D into per-lane fp64
@@ -26,50 +26,68 @@
 // e8 e12 e1 e5 e9 e13 e2 e6 e10 e14 e3 e7 e11 e15) of the activations. The
 // x16 / x64 leave the fp64 epilogue as an exact power-of-two scale.
 //
-// Both operands go through LDS in chunks of 16 blocks (8 for int8), loaded one chunk
-// ahead into registers with coalesced 16-byte loads: weight rows per wave
-// (each wave reads only its own rows), the item's activation rows and block
-// scales once per workgroup (all four waves use the same tokens). Pitches
-// are padded so the operand reads hit distinct banks.
+// Staging: the K range is cut into stages of CH blocks. Weight rows, the
+// item's activation rows and their block scales reach LDS with direct-to-LDS
+// loads (global_load_lds_dwordx4 / _dword: lane l of a wave writes 16 / 4
+// bytes at a wave-uniform LDS base + 16 l / 4 l), so no registers hold data
+// in flight. A ring of three LDS slots keeps two stages loading while the
+// third is computed, with one workgroup barrier per stage; each wave waits
+// only for its own loads of the stage it is about to use (vmcnt), and the
+// barrier makes every wave's loads visible. Inside a slot the 16-byte pieces
+// of a row are stored at position piece ^ key(row) (an XOR swizzle chosen per
+// row so that the MFMA operand reads of 16 rows / 16 tokens hit distinct LDS
+// banks); the loads scatter global pieces accordingly.
 #pragma once
-
-#include <type_traits>
 
 #include "coli_common.h"
 
 namespace pf {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-// plain vector type for 16-byte moves (HIP's uint4 struct copies become
-// memcpy calls that keep staging arrays out of registers)
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kTok = 32;              // tokens per work item
-constexpr int kRows = 64;             // output rows per workgroup
+constexpr int kTok = 32;      // tokens per work item
+constexpr int kRows = 64;     // gate/up: h rows per workgroup (16 per wave)
+constexpr int kDnRows = 128;  // down: output rows per workgroup (32 per wave)
+constexpr int kSlots = 3;     // LDS ring: one stage computed, two loading
 
-// Staging geometry and operand form of one weight width (2, 4 or 8 bits).
+// Stage geometry of one weight width (2, 4 or 8 bits).
 template <int BITS>
-struct WFmt {
-    static constexpr int CH = BITS == 8 ? 8 : 16;  // blocks staged per step
-    static constexpr int WB = 4 * BITS;            // bytes of a 32-wide block of a row
-    static constexpr int RB = CH * WB;             // bytes of a row per chunk
-    static constexpr int PB = RB / 16;             // bytes per lane (16 lanes per row)
-    static constexpr int Pitch = RB + 8;           // LDS bytes per staged row
-    static constexpr int ActPitch = CH * 32 + 16;  // LDS bytes per staged activation row
-    static constexpr int DPitch = CH + 1;          // floats per staged scale row
-    static constexpr int ActBytes = kTok * ActPitch;
-    static constexpr int DBytes = kTok * DPitch * 4;
+struct Geo {
+    static constexpr int CH = 4;                         // 32-blocks per stage
+    static constexpr int WB = 4 * BITS;                  // bytes of a row's block
+    static constexpr int RB = CH * WB;                   // bytes of a row per stage
+    static constexpr int NPC = RB / 16;                  // 16-byte pieces per row
+    static constexpr int KS = RB >= 256 ? 1 : 256 / RB;  // rows per 256-byte bank period
+    static constexpr int RPI = 1024 / RB;                // rows per load instruction
+    static constexpr int WBYTES = 32 * RB;               // staged weight bytes per wave
+    static constexpr int WINSTR = WBYTES / 1024;         // weight loads per wave and stage
+    static constexpr int ARB = CH * 32;                  // activation bytes per token
+    static constexpr int ANPC = ARB / 16;
+    static constexpr int AKS = ARB >= 256 ? 1 : 256 / ARB;
+    static constexpr int ARPI = 1024 / ARB;              // token rows per load instruction
+    static constexpr int A_OFF = 4 * WBYTES;
+    static constexpr int D_OFF = A_OFF + kTok * ARB;
+    static constexpr int SLOT = (D_OFF + kTok * CH * 4 + 255) & ~255;
     static constexpr int Scale = BITS == 4 ? 16 : BITS == 2 ? 64 : 1;  // code multiplier
     static constexpr double InvScale = 1.0 / Scale;                    // exact
     static constexpr int Layout = BITS == 4 ? 1 : BITS == 2 ? 2 : 0;   // activation order
+    // activation loads per wave and stage for NG 16-token groups (they cover
+    // 4 * AIW * ARPI >= 16 NG token rows)
+    static constexpr int aiw(int NG) { return NG * ARB / 256 > 0 ? NG * ARB / 256 : 1; }
+    static_assert(RB >= 32 && RB <= 256 && ARB <= 256, "stage geometry");
+    // 16 rows / tokens span whole swizzle-key periods
+    static_assert(16 % (NPC * KS) == 0 && 16 % (ANPC * AKS) == 0, "swizzle keys");
 };
+
+__device__ __forceinline__ int wkey(int r, int ks, int npc) { return (r / ks) % npc; }
 
 struct PfArgs {
     const uint8_t* eq;
     const float* es;
     int64_t blob_q, blob_s;
     int H, I;
-    const int8_t* qx;      // [T, H] Q8_0 codes of x (8-group order)
+    const int8_t* qx;      // [T, H] Q8_0 codes of x (in the weight width's element order)
     const float* dx;       // [T, H/32]
     const int32_t* item_e;
     const int32_t* item_s0;
@@ -83,179 +101,225 @@ struct PfArgs {
     int tap_rows, tap_stride;
 };
 
-__device__ __forceinline__ long a_operand(uint32_t w) {
-    return (long)(uint32_t)nib_lo16(w) | ((long)(uint32_t)nib_hi16(w) << 32);
-}
-
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
     return *reinterpret_cast<const uint32_t*>(p);
 }
 
-// A operand (8 int8 values, k = 8q .. 8q+7 of the block's k order) of the
-// staged block starting at blk, for lane group q.
+// s_waitcnt on the vector memory counter only (lgkmcnt(0) with it when LGKM).
+template <int N, bool LGKM>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | ((LGKM ? 0 : 15) << 8));
+}
+
+// Workgroup barrier without a memory fence (LDS visibility is ordered by the
+// explicit waits around it); the empty asm keeps the compiler from moving
+// memory operations across it.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// A operand of a staged block for lane group q; p points at the byte this
+// lane reads (swizzled position already applied).
 template <int BITS>
-__device__ __forceinline__ long a_op(const uint8_t* blk, int q) {
-    if (BITS == 4) return a_operand(lds_u32(blk + 4 * q));
-    if (BITS == 8) return *reinterpret_cast<const long*>(blk + 8 * q);
-    const uint32_t x = lds_u32(blk + 4 * (q >> 1));
+__device__ __forceinline__ long a_op(const uint8_t* p, int q) {
+    if (BITS == 4) {
+        const uint32_t w = lds_u32(p);
+        return (long)(uint32_t)nib_lo16(w) | ((long)(uint32_t)nib_hi16(w) << 32);
+    }
+    if (BITS == 8) return *reinterpret_cast<const long*>(p);
+    const uint32_t x = lds_u32(p);
     const int s1 = (q & 1) ? 2 : 6;
     const uint32_t lo = (x << s1) & 0xC0C0C0C0u, hi = (x << (s1 - 2)) & 0xC0C0C0C0u;
     return (long)lo | ((long)hi << 32);
 }
 
-// Stages NR rows of one chunk: lane l loads PB bytes (16, int2: 8) of staged
-// row (l >> 4) + 4k at piece (l & 15) of the chunk. Staged rows 16m .. 16m+15
-// are rows 0..15 of matrix m, starting at base[m] (this lane's row l >> 4)
-// with `stride` bytes between rows, `rowb` bytes per row.
-template <int NR, int BITS>
-struct Stager {
-    typedef WFmt<BITS> F;
-    typedef unsigned v2u __attribute__((ext_vector_type(2)));
-    typedef typename std::conditional<F::PB == 16, v4u, v2u>::type piece_t;
-    const uint8_t* base[NR / 16];
-    int64_t stride;
-    int rowb;
-    __device__ __forceinline__ void issue(int c, piece_t (&v)[NR / 4]) const {
-        const int off = min(c * F::RB + (int)(threadIdx.x & 15) * F::PB, rowb - F::PB);
-#pragma unroll
-        for (int k = 0; k < NR / 4; ++k)
-            v[k] = *reinterpret_cast<const piece_t*>(base[k / 4] + (int64_t)(4 * (k % 4)) * stride +
-                                                     off);
-    }
-    __device__ __forceinline__ void commit(uint8_t* lds, const piece_t (&v)[NR / 4]) const {
-        const int r0 = (threadIdx.x & 63) >> 4, bi = threadIdx.x & 15;
-#pragma unroll
-        for (int k = 0; k < NR / 4; ++k) {
-            uint8_t* d = lds + (r0 + 4 * k) * F::Pitch + bi * F::PB;
-            if constexpr (F::PB == 16) {
-                *reinterpret_cast<v2u*>(d) = v[k].xy;
-                *reinterpret_cast<v2u*>(d + 8) = v[k].zw;
-            } else {
-                *reinterpret_cast<v2u*>(d) = v[k];
-            }
-        }
-    }
-};
+// 0.0f in global memory: the source of the block scales past a row's end
+__device__ const float kZeroScale = 0.0f;
 
-// Activation rows of the item's 32 tokens (rows of a [*, NB * 32] int8
-// matrix in the width's element order, with NB block scales per row), one
-// chunk of CH blocks: thread tid loads the 16-byte half (tid & 1) of block
-// (tid % 2CH) / 2 of token rows tid / 2CH + (256 / 2CH) k, and threads below
-// 8 CH four block scales each.
+// Direct-to-LDS loads (lane l writes at LDS address lds + size * l). Issued
+// in asm so that the compiler neither waits on them before unrelated LDS
+// reads nor counts them; every wait for them is explicit (wait_vm).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Position key of the block scales of token j in a stage row (CH floats):
+// tokens j and j + 8 differ, so the reads of 16 tokens hit 16 banks.
 template <int CH>
-struct ActStager {
-    static constexpr int TPR = 2 * CH;        // threads per token row
-    static constexpr int RPP = 256 / TPR;     // token rows per pass
-    static constexpr int NP = kTok / RPP;     // passes
-    static constexpr int ActPitch = CH * 32 + 16, DPitch = CH + 1;
-    const int8_t* row[NP];
-    const float* drow;
-    __device__ __forceinline__ void init(const int8_t* base, const float* dbase, int64_t pitch,
-                                         int NB, const int32_t* rows_of, int n) {
-        const int half = threadIdx.x & 1;
+__device__ __forceinline__ int skey(int j) { return CH == 8 ? (j >> 3) & 1 : 0; }
+
+// Per-lane load plan of one wave for a stage: WINSTR weight loads (staged
+// rows 16t + i of tile t), AIW activation loads and one load of block scales.
+template <int BITS, int NG>
+struct Plan {
+    typedef Geo<BITS> G;
+    static constexpr int AIW = G::aiw(NG);
+    static constexpr int TPI = 64 / G::CH;         // tokens per scale load
+    static constexpr int LD = G::WINSTR + AIW + 1;  // loads per wave and stage
+    const uint8_t* wrow[G::WINSTR];  // this lane's weight row
+    int wpo[G::WINSTR];              // byte offset of its piece in the stage
+    int rowb;
+    const int8_t* arow[AIW];         // this lane's activation row
+    int apo[AIW];
+    int arowb;                       // activation row bytes (H or I)
+    const float* srow;               // scale row of this lane's token
+    int sbk;                         // block of the stage this lane's scale is
+    int NB;                          // blocks per row
+    int wave;
+
+    // tile[t]: row 0 of tile t (16 rows, `rowb` bytes apart, rows from
+    // nrow[t] on clamped to its last); rows_of[j]: activation row of token j
+    // (j < n; tokens past n repeat token n - 1).
+    __device__ __forceinline__ void init(const uint8_t* const (&tile)[2], const int (&nrow)[2],
+                                         int64_t rowb_, const int8_t* act, int64_t arowb_,
+                                         const int32_t* rows_of, int n, const float* scales,
+                                         int NB_) {
+        const int lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        rowb = (int)rowb_;
+        arowb = (int)arowb_;
+        NB = NB_;
 #pragma unroll
-        for (int k = 0; k < NP; ++k) {
-            const int j = min((int)(threadIdx.x / TPR) + RPP * k, n - 1);
-            row[k] = base + (int64_t)rows_of[j] * pitch + 16 * half;
+        for (int i = 0; i < G::WINSTR; ++i) {
+            const int r = i * G::RPI + lane / G::NPC;  // staged row 0..31
+            const int t = r >> 4, rr = min(r & 15, nrow[t] - 1);
+            const int piece = (lane % G::NPC) ^ wkey(r, G::KS, G::NPC);
+            wrow[i] = tile[t] + (int64_t)rr * rowb_;
+            wpo[i] = piece * 16;
         }
-        const int jd = min((int)((threadIdx.x % (8 * CH)) / (CH / 4)), n - 1);
-        drow = dbase + (int64_t)rows_of[jd] * NB;
+#pragma unroll
+        for (int i = 0; i < AIW; ++i) {
+            const int j = (wave * AIW + i) * G::ARPI + lane / G::ANPC;  // token row
+            const int piece = (lane % G::ANPC) ^ wkey(j, G::AKS, G::ANPC);
+            arow[i] = act + (int64_t)rows_of[min(j, n - 1)] * arowb_;
+            apo[i] = piece * 16;
+        }
+        // with CH = 4 waves 2 and 3 repeat the loads of waves 0 and 1
+        const int js = (wave * TPI) % kTok + lane / G::CH;
+        sbk = (lane % G::CH) ^ skey<G::CH>(js);
+        srow = scales + (int64_t)rows_of[min(js, n - 1)] * NB_;
     }
-    __device__ __forceinline__ void issue(int c, int NB, v4u (&v)[NP], float (&dv)[4]) const {
-        const int b = min(c * CH + (int)((threadIdx.x % TPR) >> 1), NB - 1);
+    // Issues the stage's loads into the slot at LDS address `slot`. Pieces
+    // past a row's end are clamped to its last piece; their blocks read
+    // scale 0, so they add nothing.
+    __device__ __forceinline__ void issue(int c, uint32_t slot) const {
+        const uint32_t wdst = slot + wave * G::WBYTES;
 #pragma unroll
-        for (int k = 0; k < NP; ++k) v[k] = *reinterpret_cast<const v4u*>(row[k] + b * 32);
-        // every thread loads (threads >= 8 CH repeat rows of the first 8 CH, in
-        // bounds), so the values stay in registers; only threads < 8 CH store
-        const int b0 = c * CH + (threadIdx.x % (CH / 4)) * 4;
+        for (int i = 0; i < G::WINSTR; ++i)
+            dma_b128(wrow[i] + min(c * G::RB + wpo[i], rowb - 16), wdst + i * 1024);
+        const uint32_t adst = slot + G::A_OFF + wave * AIW * 1024;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dv[i] = drow[min(b0 + i, NB - 1)];
-    }
-    // Scales of blocks past NB are stored as 0, so those blocks add nothing.
-    __device__ __forceinline__ void commit(int c, int NB, uint8_t* act, float* dbuf,
-                                           const v4u (&v)[NP], const float (&dv)[4]) const {
-        const int blk = (threadIdx.x % TPR) >> 1, half = threadIdx.x & 1;
-#pragma unroll
-        for (int k = 0; k < NP; ++k) {
-            const int j = threadIdx.x / TPR + RPP * k;
-            *reinterpret_cast<v4u*>(act + j * ActPitch + blk * 32 + 16 * half) = v[k];
-        }
-        if (threadIdx.x < 8 * CH) {
-            const int j = threadIdx.x / (CH / 4), b0 = (threadIdx.x % (CH / 4)) * 4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dbuf[j * DPitch + b0 + i] = (c * CH + b0 + i < NB) ? dv[i] : 0.0f;
-        }
+        for (int i = 0; i < AIW; ++i)
+            dma_b128(arow[i] + min(c * G::ARB + apo[i], arowb - 16), adst + i * 1024);
+        const int b = c * G::CH + sbk;
+        dma_b32(b < NB ? srow + b : &kZeroScale,
+                slot + G::D_OFF + ((wave * TPI) % kTok) * G::CH * 4);
     }
 };
 
-// K loop of the gate/up kernel for NG 16-token groups: MFMA per block and
-// group, fp64 epilogue. Inside a chunk there are no branches, so the
-// compiler can overlap the next block's LDS reads and MFMAs with the current
-// block's epilogue.
+// K loop: acc[t][g][i] = sum over blocks of d[token] * D(tile t, group g)[i].
+// TAP records the exact block dots of tile 0 for sampled rows.
 template <int BITS, int NG, bool TAP>
-__device__ __forceinline__ void gateup_loop(const PfArgs& a, const Stager<32, BITS>& st,
-                                            const ActStager<WFmt<BITS>::CH>& as, uint8_t* lds,
-                                            uint8_t* act, float* dbuf, double (&accg)[2][4],
-                                            double (&accu)[2][4], int BH, int r0, int q, int lr,
-                                            int s0, int n) {
-    typedef WFmt<BITS> F;
-    constexpr int CH = F::CH;
+__device__ __forceinline__ void mm_loop(const Plan<BITS, NG>& pl, uint8_t* smem,
+                                        double (&acc)[2][2][4], int nst, const PfArgs& a,
+                                        int tap_r0, int s0, int n) {
+    typedef Geo<BITS> G;
+    constexpr int LD = Plan<BITS, NG>::LD;
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 15, q = lane >> 4;
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) accg[g][i] = accu[g][i] = 0.0;
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][g][i] = 0.0;
+    // slot-relative lane bases of the operand reads; the block index of the
+    // stage is XORed into the piece bits (no carries: the other terms have
+    // those bits clear)
+    int wq, wbx;  // piece bit from q, byte in the piece from q
+    if (BITS == 4) { wq = 0; wbx = 4 * q; }
+    else if (BITS == 8) { wq = q >> 1; wbx = 8 * (q & 1); }
+    else { wq = 0; wbx = 4 * (q >> 1); }
+    // Loop-invariant operand offsets of block bi inside a slot. Tile 1 sits
+    // 16 RB above tile 0 and token group 1 16 ARB / 16 CH floats above group
+    // 0 with equal swizzle keys (16 rows / tokens are a whole number of key
+    // periods), so they are immediate offsets of the same address.
+    const int r0k = wkey(lr, G::KS, G::NPC), a0k = wkey(lr, G::AKS, G::ANPC);
+    const int wbase = pl.wave * G::WBYTES + lr * G::RB + ((wq ^ r0k) << 4) + wbx;
+    const int abase = G::A_OFF + lr * G::ARB + (((q >> 1) ^ a0k) << 4) + 8 * (q & 1);
+    const int dbase = G::D_OFF + lr * G::CH * 4 + 4 * skey<G::CH>(lr);
+    int wo[G::CH], ao[G::CH], dof[G::CH];
+#pragma unroll
+    for (int bi = 0; bi < G::CH; ++bi) {
+        const int pb = BITS == 4 ? bi : BITS == 8 ? 2 * bi : bi >> 1;  // piece bits of block bi
+        const int ib = BITS == 2 ? 8 * (bi & 1) : 0;                   // byte in the piece
+        wo[bi] = (wbase ^ (pb << 4)) + ib;
+        ao[bi] = abase ^ (bi << 5);
+        dof[bi] = dbase ^ (bi << 2);
+    }
     const v4i zero = {0, 0, 0, 0};
-    const int nch = (BH + CH - 1) / CH;
-    typename Stager<32, BITS>::piece_t wv[8];
-    v4u av[ActStager<CH>::NP];
-    float adv[4];
-    st.issue(0, wv);
-    as.issue(0, BH, av, adv);
-    st.commit(lds, wv);
-    as.commit(0, BH, act, dbuf, av, adv);
-    __syncthreads();
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
+
+    pl.issue(0, lds0);
+    if (nst > 1) pl.issue(1, lds0 + G::SLOT);
+    // unrolled over the ring so that every slot offset is an immediate
 #pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
-        // unconditional (keeps the staging registers out of memory); after
-        // the last chunk this re-reads that chunk, from cache
-        const int cn = min(c + 1, nch - 1);
-        st.issue(cn, wv);
-        as.issue(cn, BH, av, adv);
+    for (int cb = 0; cb < nst; cb += kSlots) {
 #pragma unroll
-        for (int bi = 0; bi < CH; ++bi) {
-            const long ag = a_op<BITS>(lds + lr * F::Pitch + bi * F::WB, q);
-            const long au = a_op<BITS>(lds + (16 + lr) * F::Pitch + bi * F::WB, q);
+        for (int sl = 0; sl < kSlots; ++sl) {
+            const int c = cb + sl;
+            if (c >= nst) break;
+            const uint8_t* cur = smem + sl * G::SLOT;
+            // this wave's loads of stage c are in (those of stage c + 1 may
+            // not be); with TAP the stores of the taps share the counter and
+            // need not complete in order with the loads, so that variant
+            // waits for all
+            if (c + 1 < nst && !TAP) wait_vm<LD, false>();
+            else wait_vm<0, false>();
+            stage_barrier();  // every wave's loads of stage c are in; slot c - 1 is free
+            if (c + 2 < nst) pl.issue(c + 2, lds0 + ((sl + 2) % kSlots) * G::SLOT);
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int j = 16 * g + lr;
-                const long bv =
-                    *reinterpret_cast<const long*>(act + j * F::ActPitch + bi * 32 + 8 * q);
-                const double dd = (double)dbuf[j * F::DPitch + bi];
-                const v4i cg = __builtin_amdgcn_mfma_i32_16x16x32_i8(ag, bv, zero, 0, 0, 0);
-                const v4i cu = __builtin_amdgcn_mfma_i32_16x16x32_i8(au, bv, zero, 0, 0, 0);
+            for (int bi = 0; bi < G::CH; ++bi) {
+                const long a0 = a_op<BITS>(cur + wo[bi], q);
+                const long a1 = a_op<BITS>(cur + wo[bi] + 16 * G::RB, q);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    accg[g][i] += dd * (double)cg[i];
-                    accu[g][i] += dd * (double)cu[i];
-                    asm volatile("" : "+v"(accg[g][i]), "+v"(accu[g][i]));
-                }
-                if (TAP) {
-                    const int b = c * CH + bi;
+                for (int g = 0; g < NG; ++g) {
+                    const long bv =
+                        *reinterpret_cast<const long*>(cur + ao[bi] + g * 16 * G::ARB);
+                    const double dd = (double)*reinterpret_cast<const float*>(
+                        cur + dof[bi] + g * 16 * G::CH * 4);
+                    const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a0, bv, zero, 0, 0, 0);
+                    const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a1, bv, zero, 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int r = r0 + 4 * q + i;
-                        if (j < n && b < BH && (r % a.tap_stride) == 0)
-                            a.tap[((int64_t)(s0 + j) * a.tap_rows + r / a.tap_stride) * BH + b] =
-                                cg[i] / F::Scale;
+                        acc[0][g][i] += dd * (double)c0[i];
+                        acc[1][g][i] += dd * (double)c1[i];
+                        asm volatile("" : "+v"(acc[0][g][i]), "+v"(acc[1][g][i]));
+                    }
+                    if (TAP) {
+                        const int b = c * G::CH + bi, j = 16 * g + lr, BH = pl.NB;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = tap_r0 + 4 * q + i;
+                            if (j < n && b < BH && (r % a.tap_stride) == 0)
+                                a.tap[((int64_t)(s0 + j) * a.tap_rows + r / a.tap_stride) * BH +
+                                      b] = c0[i] / G::Scale;
+                        }
                     }
                 }
             }
         }
-        __syncthreads();
-        st.commit(lds, wv);
-        as.commit(cn, BH, act, dbuf, av, adv);
-        __syncthreads();
     }
 }
 
@@ -271,10 +335,10 @@ __device__ __forceinline__ constexpr int act_elem(int p) {
 // Gate/up + SwiGLU + Q8_0(h) for one item and 64 intermediate rows; Q8_0(h)
 // is stored in the activation order of the down weights' width.
 template <int BITS, bool TAP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_pf_gateup(PfArgs a) {
-    typedef WFmt<BITS> F;
-    constexpr int kW = 32 * F::Pitch;  // per-wave weight staging (16 gate + 16 up rows)
-    __shared__ __align__(16) uint8_t smem[4 * kW + F::ActBytes + F::DBytes];
+__global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
+    typedef Geo<BITS> G;
+    __shared__ __align__(1024) uint8_t smem[kSlots * G::SLOT];
+    static_assert(kSlots * G::SLOT >= kTok * (kRows + 1) * 4, "h reuses the ring");
     const int nrt = a.I / kRows;
     const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
     if (it >= *a.n_items) return;
@@ -283,31 +347,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, q = lane >> 4;
-    const int ng = (n + 15) >> 4;  // 16-token groups in use (1 or 2)
     const int64_t rowb = (int64_t)H * BITS / 8;
     const uint8_t* gate = a.eq + (int64_t)e * a.blob_q;
     const uint8_t* up = gate + (int64_t)I * rowb;
     const int r0 = rt * kRows + wave * 16;
-    uint8_t* lds = smem + wave * kW;
-    uint8_t* act = smem + 4 * kW;
-    float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + F::ActBytes);
-    static_assert(F::ActBytes >= kTok * (kRows + 1) * 4, "h reuses the activation area");
+    const int nst = (BH + G::CH - 1) / G::CH;
 
-    Stager<32, BITS> st;  // staged rows 0..15: gate rows r0.., 16..31: up rows r0..
-    st.stride = rowb;
-    st.rowb = (int)rowb;
-    st.base[0] = gate + (int64_t)(r0 + q) * rowb;
-    st.base[1] = up + (int64_t)(r0 + q) * rowb;
-    ActStager<F::CH> as;
-    as.init(a.qx, a.dx, H, BH, a.slot_tok + s0, n);
-
-    double accg[2][4], accu[2][4];
-    if (ng == 1)
-        gateup_loop<BITS, 1, TAP>(a, st, as, lds, act, dbuf, accg, accu, BH, r0, q, lr, s0, n);
-    else
-        gateup_loop<BITS, 2, TAP>(a, st, as, lds, act, dbuf, accg, accu, BH, r0, q, lr, s0, n);
-    __syncthreads();  // the activation area is reused for h below
-    float (*hbuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(act);
+    const uint8_t* const tiles[2] = {gate + (int64_t)r0 * rowb, up + (int64_t)r0 * rowb};
+    const int nrow[2] = {16, 16};
+    double acc[2][2][4];
+    if (n <= 16) {
+        Plan<BITS, 1> pl;
+        pl.init(tiles, nrow, rowb, a.qx, H, a.slot_tok + s0, n, a.dx, BH);
+        mm_loop<BITS, 1, TAP>(pl, smem, acc, nst, a, r0, s0, n);
+    } else {
+        Plan<BITS, 2> pl;
+        pl.init(tiles, nrow, rowb, a.qx, H, a.slot_tok + s0, n, a.dx, BH);
+        mm_loop<BITS, 2, TAP>(pl, smem, acc, nst, a, r0, s0, n);
+    }
+    __syncthreads();  // the ring is reused for h below
+    float (*hbuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(smem);
 
     // SwiGLU, then Q8_0 over each 32 consecutive h rows of a token
     const float* gs = a.es + (int64_t)e * a.blob_s;
@@ -319,8 +378,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             // the sums carry the multiplier of the weight codes: scale it away (exact)
-            const float gv = (float)((double)gsr * (accg[g][i] * F::InvScale));
-            const float uv = (float)((double)usr * (accu[g][i] * F::InvScale));
+            const float gv = (float)((double)gsr * (acc[0][g][i] * G::InvScale));
+            const float uv = (float)((double)usr * (acc[1][g][i] * G::InvScale));
             hbuf[16 * g + lr][wave * 16 + 4 * q + i] = swiglu_f32(gv, uv);
         }
     }
@@ -335,10 +394,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         uint32_t w[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            w[i] = pack4_i8(q8_code(hv[act_elem<F::Layout>(4 * i)], d),
-                            q8_code(hv[act_elem<F::Layout>(4 * i + 1)], d),
-                            q8_code(hv[act_elem<F::Layout>(4 * i + 2)], d),
-                            q8_code(hv[act_elem<F::Layout>(4 * i + 3)], d));
+            w[i] = pack4_i8(q8_code(hv[act_elem<G::Layout>(4 * i)], d),
+                            q8_code(hv[act_elem<G::Layout>(4 * i + 1)], d),
+                            q8_code(hv[act_elem<G::Layout>(4 * i + 2)], d),
+                            q8_code(hv[act_elem<G::Layout>(4 * i + 3)], d));
+        typedef unsigned v4u __attribute__((ext_vector_type(4)));
         v4u* o = reinterpret_cast<v4u*>(a.qh + (int64_t)(s0 + j) * I + rt * kRows + 32 * kb);
         o[0] = v4u{w[0], w[1], w[2], w[3]};
         o[1] = v4u{w[4], w[5], w[6], w[7]};
@@ -346,67 +406,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
 }
 
-// K loop of the down kernel (as gateup_loop, one weight matrix).
-template <int BITS, int NG>
-__device__ __forceinline__ void down_loop(const Stager<16, BITS>& st,
-                                          const ActStager<WFmt<BITS>::CH>& as, uint8_t* lds,
-                                          uint8_t* act, float* dbuf, double (&acc)[2][4],
-                                          int BI, int q, int lr) {
-    typedef WFmt<BITS> F;
-    constexpr int CH = F::CH;
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[g][i] = 0.0;
-    const v4i zero = {0, 0, 0, 0};
-    const int nch = (BI + CH - 1) / CH;
-    typename Stager<16, BITS>::piece_t wv[4];
-    v4u av[ActStager<CH>::NP];
-    float adv[4];
-    st.issue(0, wv);
-    as.issue(0, BI, av, adv);
-    st.commit(lds, wv);
-    as.commit(0, BI, act, dbuf, av, adv);
-    __syncthreads();
-#pragma unroll 1
-    for (int c = 0; c < nch; ++c) {
-        // unconditional (keeps the staging registers out of memory); after
-        // the last chunk this re-reads that chunk, from cache
-        const int cn = min(c + 1, nch - 1);
-        st.issue(cn, wv);
-        as.issue(cn, BI, av, adv);
-#pragma unroll
-        for (int bi = 0; bi < CH; ++bi) {
-            const long aw = a_op<BITS>(lds + lr * F::Pitch + bi * F::WB, q);
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const int j = 16 * g + lr;
-                const long bv =
-                    *reinterpret_cast<const long*>(act + j * F::ActPitch + bi * 32 + 8 * q);
-                const double dd = (double)dbuf[j * F::DPitch + bi];
-                const v4i cd = __builtin_amdgcn_mfma_i32_16x16x32_i8(aw, bv, zero, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    acc[g][i] += dd * (double)cd[i];
-                    asm volatile("" : "+v"(acc[g][i]));
-                }
-            }
-        }
-        __syncthreads();
-        st.commit(lds, wv);
-        as.commit(cn, BI, act, dbuf, av, adv);
-        __syncthreads();
-    }
-}
-
-// Down projection for one item and 64 output rows: ye[slot, row] =
-// fp32(s_down[row] * sum_b d_h,b * I_b).
+// Down projection for one item and 128 output rows: ye[slot, row] =
+// fp32(s_down[row] * sum_b d_h,b * I_b). The last row tile may pass H (rows
+// clamped for loading, not stored).
 template <int BITS>
 __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
-    typedef WFmt<BITS> F;
-    constexpr int kW = 16 * F::Pitch;
-    __shared__ __align__(16) uint8_t smem[4 * kW + F::ActBytes + F::DBytes];
-    const int nrt = a.H / kRows;
+    typedef Geo<BITS> G;
+    __shared__ __align__(1024) uint8_t smem[kSlots * G::SLOT];
+    static_assert(kSlots * G::SLOT >= kTok * (kDnRows + 1) * 4, "y reuses the ring");
+    __shared__ int s_rows[kTok];
+    const int nrt = (a.H + kDnRows - 1) / kDnRows;
     const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
     if (it >= *a.n_items) return;
     const int e = a.item_e[it], s0 = a.item_s0[it], n = a.item_n[it];
@@ -414,47 +423,47 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, q = lane >> 4;
-    const int ng = (n + 15) >> 4;
     const int64_t rowb = (int64_t)I * BITS / 8;
-    const uint8_t* down = a.eq + (int64_t)e * a.blob_q + 2 * (int64_t)H * I * BITS / 8;
-    const int r0 = rt * kRows + wave * 16;
-    uint8_t* lds = smem + wave * kW;
-    uint8_t* act = smem + 4 * kW;
-    float* dbuf = reinterpret_cast<float*>(smem + 4 * kW + F::ActBytes);
-    static_assert(F::ActBytes >= kTok * (kRows + 1) * 4, "y reuses the activation area");
-
-    Stager<16, BITS> st;
-    st.stride = rowb;
-    st.rowb = (int)rowb;
-    st.base[0] = down + (int64_t)(r0 + q) * rowb;
+    const uint8_t* down = a.eq + (int64_t)e * a.blob_q + 2 * (int64_t)H * rowb;
+    const int R0 = rt * kDnRows + wave * 32;
+    const int nst = (BI + G::CH - 1) / G::CH;
     // the item's slots are consecutive rows of q_h
-    __shared__ int s_rows[kTok];
     if (threadIdx.x < kTok) s_rows[threadIdx.x] = s0 + threadIdx.x;
     __syncthreads();
-    ActStager<F::CH> as;
-    as.init(a.qh, a.dh, I, BI, s_rows, n);
 
-    double acc[2][4];
-    if (ng == 1)
-        down_loop<BITS, 1>(st, as, lds, act, dbuf, acc, BI, q, lr);
-    else
-        down_loop<BITS, 2>(st, as, lds, act, dbuf, acc, BI, q, lr);
-    __syncthreads();  // the activation area is reused for y below
-    float (*ybuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(act);
+    // rows past H are clamped to H - 1 (tile bases stay inside the matrix)
+    const int t0 = min(R0, H - 1), t1 = min(R0 + 16, H - 1);
+    const uint8_t* const tiles[2] = {down + (int64_t)t0 * rowb, down + (int64_t)t1 * rowb};
+    const int nrow[2] = {max(1, min(16, H - t0)), max(1, min(16, H - t1))};
+    double acc[2][2][4];
+    if (n <= 16) {
+        Plan<BITS, 1> pl;
+        pl.init(tiles, nrow, rowb, a.qh, I, s_rows, n, a.dh, BI);
+        mm_loop<BITS, 1, false>(pl, smem, acc, nst, a, 0, s0, n);
+    } else {
+        Plan<BITS, 2> pl;
+        pl.init(tiles, nrow, rowb, a.qh, I, s_rows, n, a.dh, BI);
+        mm_loop<BITS, 2, false>(pl, smem, acc, nst, a, 0, s0, n);
+    }
+    __syncthreads();  // the ring is reused for y below
+    float (*ybuf)[kDnRows + 1] = reinterpret_cast<float (*)[kDnRows + 1]>(smem);
 
     const float* ds = a.es + (int64_t)e * a.blob_s + 2 * I;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rl = wave * 16 + 4 * q + i;
-        const float dsr = ds[rt * kRows + rl];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int g = 0; g < 2; ++g)  // undo the multiplier of the weight codes
-            ybuf[16 * g + lr][rl] = (float)((double)dsr * (acc[g][i] * F::InvScale));
-    }
+        for (int i = 0; i < 4; ++i) {
+            const int rl = wave * 32 + 16 * t + 4 * q + i;
+            const float dsr = ds[min(rt * kDnRows + rl, H - 1)];
+#pragma unroll
+            for (int g = 0; g < 2; ++g)  // undo the multiplier of the weight codes
+                ybuf[16 * g + lr][rl] = (float)((double)dsr * (acc[t][g][i] * G::InvScale));
+        }
     __syncthreads();
-    for (int v = threadIdx.x; v < n * kRows; v += 256) {
-        const int j = v >> 6, r = v & 63;
-        a.ye[(int64_t)(s0 + j) * H + rt * kRows + r] = ybuf[j][r];
+    const int nr = min(kDnRows, H - rt * kDnRows);
+    for (int v = threadIdx.x; v < n * kDnRows; v += 256) {
+        const int j = v >> 7, r = v & 127;
+        if (r < nr) a.ye[(int64_t)(s0 + j) * H + rt * kDnRows + r] = ybuf[j][r];
     }
 }
 
