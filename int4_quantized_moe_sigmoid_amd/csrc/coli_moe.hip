@@ -64,6 +64,7 @@ GroupSel group_sel(const coli_moe_cfg& c) {
 struct Layout {
     coli_moe_ws_layout pub;
     size_t lists, items, n_items, uinfo, rpart, sig;
+    size_t mx, ex, mh, eh;  // integer block scales of x and h (grouped MFMA path)
     int64_t max_items;
     int ch;
 };
@@ -108,6 +109,10 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
     P.qh = take(NS * I);
     P.dh = take(NS * (I / 32) * 4);
     P.ye = take(NS * H * 4);
+    L->mx = take(T * (H / 32) * 4);
+    L->ex = take(T * 4);
+    L->mh = take(NS * (I / 32) * 4);
+    L->eh = take(NS * 4);
     if (flags & COLI_FWD_DEBUG_TAPS) {
         const int64_t per_row = NS * (H / 32);
         int64_t stride = 1;
@@ -395,22 +400,36 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         pa.qh = qh; pa.dh = dh; pa.ye = ye; pa.tap = tap;
         pa.tap_rows = (int)L.pub.tap_rows;
         pa.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
+        int32_t* mxp = reinterpret_cast<int32_t*>(base + L.mx);
+        int32_t* exp_ = reinterpret_cast<int32_t*>(base + L.ex);
+        int32_t* mhp = reinterpret_cast<int32_t*>(base + L.mh);
+        int32_t* ehp = reinterpret_cast<int32_t*>(base + L.eh);
+        pa.mx = mxp; pa.ex = exp_; pa.mh = mhp; pa.eh = ehp;
+        const int64_t NS = L.pub.n_slots;
+        mk.mark("scale_int_x");
+        launch(mk, pf::k_scale_int, (unsigned)((T + 3) / 4), 256, 0, s, dx, T, H / 32, mxp, exp_);
         mk.mark("pf_gateup");
         const dim3 g1((unsigned)((I / pf::kRows) * n_it));
         const dim3 g2((unsigned)(((H + pf::kDnRows - 1) / pf::kDnRows) * n_it));
         if (bits == 4) {
             if (tap) launch(mk, pf::k_pf_gateup<4, true>, g1, 256, 0, s, pa);
             else launch(mk, pf::k_pf_gateup<4, false>, g1, 256, 0, s, pa);
+            mk.mark("scale_int_h");
+            launch(mk, pf::k_scale_int, (unsigned)((NS + 3) / 4), 256, 0, s, dh, NS, I / 32, mhp, ehp);
             mk.mark("pf_down");
             launch(mk, pf::k_pf_down<4>, g2, 256, 0, s, pa);
         } else if (bits == 8) {
             if (tap) launch(mk, pf::k_pf_gateup<8, true>, g1, 256, 0, s, pa);
             else launch(mk, pf::k_pf_gateup<8, false>, g1, 256, 0, s, pa);
+            mk.mark("scale_int_h");
+            launch(mk, pf::k_scale_int, (unsigned)((NS + 3) / 4), 256, 0, s, dh, NS, I / 32, mhp, ehp);
             mk.mark("pf_down");
             launch(mk, pf::k_pf_down<8>, g2, 256, 0, s, pa);
         } else {
             if (tap) launch(mk, pf::k_pf_gateup<2, true>, g1, 256, 0, s, pa);
             else launch(mk, pf::k_pf_gateup<2, false>, g1, 256, 0, s, pa);
+            mk.mark("scale_int_h");
+            launch(mk, pf::k_scale_int, (unsigned)((NS + 3) / 4), 256, 0, s, dh, NS, I / 32, mhp, ehp);
             mk.mark("pf_down");
             launch(mk, pf::k_pf_down<2>, g2, 256, 0, s, pa);
         }

@@ -39,6 +39,8 @@
 // banks); the loads scatter global pieces accordingly.
 #pragma once
 
+#include <type_traits>
+
 #include "coli_common.h"
 
 namespace pf {
@@ -99,7 +101,63 @@ struct PfArgs {
     float* ye;             // [slots, H]
     int32_t* tap;
     int tap_rows, tap_stride;
+    const int32_t* mx;     // integer form of dx (k_scale_int) and its exponents
+    const int32_t* ex;
+    const int32_t* mh;     // integer form of dh and its exponents
+    const int32_t* eh;
 };
+
+// Exponent marking a row whose block scales span more than 2^7 (no 31-bit
+// integer form): its items take the fp64 epilogue.
+constexpr int kWideRow = -0x40000000;
+
+// Integer form of block scales, one wave per row of NB scales (>= 0): with
+// d = M 2^e (M the 24-bit significand) and e0 the least e over the row's
+// nonzero scales, mi = M << (e - e0), so sum_b d_b I_b = 2^e0 sum_b mi_b I_b
+// exactly, and that integer sum fits in int64 (|mi| < 2^31, |I_b| < 2^19, at
+// most 2^19 blocks). exps[row] = e0, or kWideRow when some e - e0 exceeds 7 or
+// a scale is not finite.
+__global__ __launch_bounds__(256) void k_scale_int(const float* __restrict__ d, int64_t rows,
+                                                   int NB, int32_t* __restrict__ mi,
+                                                   int32_t* __restrict__ exps) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const float* dr = d + row * NB;
+    int emin = 0x7fffffff, emax = -0x7fffffff;
+    bool bad = false;
+    for (int b = lane; b < NB; b += 64) {
+        const uint32_t u = __float_as_uint(dr[b]);
+        const int E = (int)(u >> 23);  // d >= 0: no sign bit
+        if (E >= 255) bad = true;
+        if ((u & 0x7fffffffu) == 0) continue;
+        const int e = E == 0 ? -149 : E - 150;
+        emin = min(emin, e);
+        emax = max(emax, e);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        emin = min(emin, __shfl_xor(emin, o, 64));
+        emax = max(emax, __shfl_xor(emax, o, 64));
+    }
+    bad = __any(bad);
+    const bool empty = emin == 0x7fffffff;
+    const bool wide = bad || (!empty && emax - emin > 7);
+    const int e0 = empty ? 0 : emin;
+    int32_t* mr = mi + row * NB;
+    for (int b = lane; b < NB; b += 64) {
+        const uint32_t u = __float_as_uint(dr[b]);
+        const int E = (int)(u >> 23);
+        int32_t m = 0;
+        if (!wide && (u & 0x7fffffffu) != 0) {
+            const uint32_t M = E == 0 ? (u & 0x7fffffu) : ((u & 0x7fffffu) | 0x800000u);
+            const int e = E == 0 ? -149 : E - 150;
+            m = (int32_t)(M << (e - e0));
+        }
+        mr[b] = m;
+    }
+    if (lane == 0) exps[row] = wide ? kWideRow : e0;
+}
 
 __device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) {
     return *reinterpret_cast<const uint32_t*>(p);
@@ -136,7 +194,8 @@ __device__ __forceinline__ long a_op(const uint8_t* p, int q) {
     return (long)lo | ((long)hi << 32);
 }
 
-// 0.0f in global memory: the source of the block scales past a row's end
+// 0 (as 0.0f and as integer) in global memory: the source of the block
+// scales past a row's end
 __device__ const float kZeroScale = 0.0f;
 
 // Direct-to-LDS loads (lane l writes at LDS address lds + size * l). Issued
@@ -173,7 +232,7 @@ struct Plan {
     const int8_t* arow[AIW];         // this lane's activation row
     int apo[AIW];
     int arowb;                       // activation row bytes (H or I)
-    const float* srow;               // scale row of this lane's token
+    const uint8_t* srow;             // scale row of this lane's token (4-byte values)
     int sbk;                         // block of the stage this lane's scale is
     int NB;                          // blocks per row
     int wave;
@@ -183,7 +242,7 @@ struct Plan {
     // (j < n; tokens past n repeat token n - 1).
     __device__ __forceinline__ void init(const uint8_t* const (&tile)[2], const int (&nrow)[2],
                                          int64_t rowb_, const int8_t* act, int64_t arowb_,
-                                         const int32_t* rows_of, int n, const float* scales,
+                                         const int32_t* rows_of, int n, const void* scales,
                                          int NB_) {
         const int lane = threadIdx.x & 63;
         wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -208,7 +267,7 @@ struct Plan {
         // with CH = 4 waves 2 and 3 repeat the loads of waves 0 and 1
         const int js = (wave * TPI) % kTok + lane / G::CH;
         sbk = (lane % G::CH) ^ skey<G::CH>(js);
-        srow = scales + (int64_t)rows_of[min(js, n - 1)] * NB_;
+        srow = static_cast<const uint8_t*>(scales) + (int64_t)rows_of[min(js, n - 1)] * NB_ * 4;
     }
     // Issues the stage's loads into the slot at LDS address `slot`. Pieces
     // past a row's end are clamped to its last piece; their blocks read
@@ -223,27 +282,36 @@ struct Plan {
         for (int i = 0; i < AIW; ++i)
             dma_b128(arow[i] + min(c * G::ARB + apo[i], arowb - 16), adst + i * 1024);
         const int b = c * G::CH + sbk;
-        dma_b32(b < NB ? srow + b : &kZeroScale,
+        dma_b32(b < NB ? static_cast<const void*>(srow + 4 * b) : &kZeroScale,
                 slot + G::D_OFF + ((wave * TPI) % kTok) * G::CH * 4);
     }
 };
 
 // K loop: acc[t][g][i] = sum over blocks of d[token] * D(tile t, group g)[i].
-// TAP records the exact block dots of tile 0 for sampled rows.
-template <int BITS, int NG, bool TAP>
+// INT: the staged scales are the integer form (k_scale_int) and the sum is
+// exact in int64 (one v_mad_i64_i32 per element and block), scaled by
+// 2^ex[token] (etok[g]: this lane's token of group g) and rounded once at
+// the end; else the scales are floats and the sum is fp64 (one conversion
+// and one fma per element and block). TAP records the exact block dots of
+// tile 0 for sampled rows.
+template <int BITS, int NG, bool TAP, bool INT>
 __device__ __forceinline__ void mm_loop(const Plan<BITS, NG>& pl, uint8_t* smem,
-                                        double (&acc)[2][2][4], int nst, const PfArgs& a,
-                                        int tap_r0, int s0, int n) {
+                                        double (&acc)[2][2][4], const int (&etok)[2], int nst,
+                                        const PfArgs& a, int tap_r0, int s0, int n) {
     typedef Geo<BITS> G;
     constexpr int LD = Plan<BITS, NG>::LD;
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15, q = lane >> 4;
+    long acci[2][2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][g][i] = 0.0;
+            for (int i = 0; i < 4; ++i) {
+                acc[t][g][i] = 0.0;
+                acci[t][g][i] = 0;
+            }
     // slot-relative lane bases of the operand reads; the block index of the
     // stage is XORed into the piece bits (no carries: the other terms have
     // those bits clear)
@@ -297,15 +365,25 @@ __device__ __forceinline__ void mm_loop(const Plan<BITS, NG>& pl, uint8_t* smem,
                 for (int g = 0; g < NG; ++g) {
                     const long bv =
                         *reinterpret_cast<const long*>(cur + ao[bi] + g * 16 * G::ARB);
-                    const double dd = (double)*reinterpret_cast<const float*>(
-                        cur + dof[bi] + g * 16 * G::CH * 4);
+                    const uint8_t* dp = cur + dof[bi] + g * 16 * G::CH * 4;
                     const v4i c0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a0, bv, zero, 0, 0, 0);
                     const v4i c1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a1, bv, zero, 0, 0, 0);
+                    if constexpr (INT) {
+                        const long dm = *reinterpret_cast<const int*>(dp);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        acc[0][g][i] += dd * (double)c0[i];
-                        acc[1][g][i] += dd * (double)c1[i];
-                        asm volatile("" : "+v"(acc[0][g][i]), "+v"(acc[1][g][i]));
+                        for (int i = 0; i < 4; ++i) {
+                            acci[0][g][i] += dm * (long)c0[i];
+                            acci[1][g][i] += dm * (long)c1[i];
+                            asm volatile("" : "+v"(acci[0][g][i]), "+v"(acci[1][g][i]));
+                        }
+                    } else {
+                        const double dd = (double)*reinterpret_cast<const float*>(dp);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            acc[0][g][i] += dd * (double)c0[i];
+                            acc[1][g][i] += dd * (double)c1[i];
+                            asm volatile("" : "+v"(acc[0][g][i]), "+v"(acc[1][g][i]));
+                        }
                     }
                     if (TAP) {
                         const int b = c * G::CH + bi, j = 16 * g + lr, BH = pl.NB;
@@ -320,6 +398,15 @@ __device__ __forceinline__ void mm_loop(const Plan<BITS, NG>& pl, uint8_t* smem,
                 }
             }
         }
+    }
+    if constexpr (INT) {
+        // one rounding of the exact sum, then an exact power-of-two scale
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[t][g][i] = ldexp((double)acci[t][g][i], etok[g]);
     }
 }
 
@@ -355,15 +442,32 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
 
     const uint8_t* const tiles[2] = {gate + (int64_t)r0 * rowb, up + (int64_t)r0 * rowb};
     const int nrow[2] = {16, 16};
+    const int32_t* rows_of = a.slot_tok + s0;  // token of each of the item's slots
+    // integer scales unless a token of the item has none
+    const int tv = rows_of[min((int)threadIdx.x, n - 1)];
+    const bool wide = __syncthreads_or((int)threadIdx.x < n && a.ex[tv] == kWideRow);
+    int etok[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) etok[g] = a.ex[rows_of[min(16 * g + lr, n - 1)]];
     double acc[2][2][4];
-    if (n <= 16) {
-        Plan<BITS, 1> pl;
-        pl.init(tiles, nrow, rowb, a.qx, H, a.slot_tok + s0, n, a.dx, BH);
-        mm_loop<BITS, 1, TAP>(pl, smem, acc, nst, a, r0, s0, n);
+    auto run = [&](auto ng, auto in) {
+        constexpr int NG = decltype(ng)::value;
+        constexpr bool INT = decltype(in)::value;
+        Plan<BITS, NG> pl;
+        pl.init(tiles, nrow, rowb, a.qx, H, rows_of, n,
+                INT ? static_cast<const void*>(a.mx) : static_cast<const void*>(a.dx), BH);
+        mm_loop<BITS, NG, TAP, INT>(pl, smem, acc, etok, nst, a, r0, s0, n);
+    };
+    typedef std::integral_constant<int, 1> G1;
+    typedef std::integral_constant<int, 2> G2;
+    typedef std::integral_constant<bool, true> Int;
+    typedef std::integral_constant<bool, false> F64;
+    if (!wide) {
+        if (n <= 16) run(G1{}, Int{});
+        else run(G2{}, Int{});
     } else {
-        Plan<BITS, 2> pl;
-        pl.init(tiles, nrow, rowb, a.qx, H, a.slot_tok + s0, n, a.dx, BH);
-        mm_loop<BITS, 2, TAP>(pl, smem, acc, nst, a, r0, s0, n);
+        if (n <= 16) run(G1{}, F64{});
+        else run(G2{}, F64{});
     }
     __syncthreads();  // the ring is reused for h below
     float (*hbuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(smem);
@@ -435,15 +539,31 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     const int t0 = min(R0, H - 1), t1 = min(R0 + 16, H - 1);
     const uint8_t* const tiles[2] = {down + (int64_t)t0 * rowb, down + (int64_t)t1 * rowb};
     const int nrow[2] = {max(1, min(16, H - t0)), max(1, min(16, H - t1))};
+    // integer scales unless a slot of the item has none
+    const bool wide =
+        __syncthreads_or((int)threadIdx.x < n && a.eh[s0 + min((int)threadIdx.x, n - 1)] == kWideRow);
+    int etok[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) etok[g] = a.eh[s0 + min(16 * g + lr, n - 1)];
     double acc[2][2][4];
-    if (n <= 16) {
-        Plan<BITS, 1> pl;
-        pl.init(tiles, nrow, rowb, a.qh, I, s_rows, n, a.dh, BI);
-        mm_loop<BITS, 1, false>(pl, smem, acc, nst, a, 0, s0, n);
+    auto run = [&](auto ng, auto in) {
+        constexpr int NG = decltype(ng)::value;
+        constexpr bool INT = decltype(in)::value;
+        Plan<BITS, NG> pl;
+        pl.init(tiles, nrow, rowb, a.qh, I, s_rows, n,
+                INT ? static_cast<const void*>(a.mh) : static_cast<const void*>(a.dh), BI);
+        mm_loop<BITS, NG, false, INT>(pl, smem, acc, etok, nst, a, 0, s0, n);
+    };
+    typedef std::integral_constant<int, 1> G1;
+    typedef std::integral_constant<int, 2> G2;
+    typedef std::integral_constant<bool, true> Int;
+    typedef std::integral_constant<bool, false> F64;
+    if (!wide) {
+        if (n <= 16) run(G1{}, Int{});
+        else run(G2{}, Int{});
     } else {
-        Plan<BITS, 2> pl;
-        pl.init(tiles, nrow, rowb, a.qh, I, s_rows, n, a.dh, BI);
-        mm_loop<BITS, 2, false>(pl, smem, acc, nst, a, 0, s0, n);
+        if (n <= 16) run(G1{}, F64{});
+        else run(G2{}, F64{});
     }
     __syncthreads();  // the ring is reused for y below
     float (*ybuf)[kDnRows + 1] = reinterpret_cast<float (*)[kDnRows + 1]>(smem);
