@@ -305,6 +305,25 @@ int hip_status() {
     return e == hipSuccess ? COLI_OK : COLI_E_HIP;
 }
 
+// The grouped MFMA kernels of one weight width: gate/up (with debug taps or
+// not), the integer form of the h scales, down; KT tokens per item.
+template <int BITS, typename HS>
+void launch_pf(int kt, bool tap, dim3 g1, dim3 g2, const pf::PfArgs& pa, HS h_scales,
+               hipStream_t s, Marks& mk) {
+    mk.mark("pf_gateup");
+    if (kt == 64) {
+        if (tap) launch(mk, pf::k_pf_gateup<BITS, 64, true>, g1, 256, 0, s, pa);
+        else launch(mk, pf::k_pf_gateup<BITS, 64, false>, g1, 256, 0, s, pa);
+    } else {
+        if (tap) launch(mk, pf::k_pf_gateup<BITS, 32, true>, g1, 256, 0, s, pa);
+        else launch(mk, pf::k_pf_gateup<BITS, 32, false>, g1, 256, 0, s, pa);
+    }
+    h_scales();
+    mk.mark("pf_down");
+    if (kt == 64) launch(mk, pf::k_pf_down<BITS, 64>, g2, 256, 0, s, pa);
+    else launch(mk, pf::k_pf_down<BITS, 32>, g2, 256, 0, s, pa);
+}
+
 int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y, void* ws,
                  size_t ws_bytes, uint32_t flags, hipStream_t s, Marks& mk) {
     if (!w || T < 0) return COLI_E_INVAL;
@@ -383,7 +402,11 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
     launch_route(c, x, w->w_router, w->bias, T, logits,
                  reinterpret_cast<double*>(base + L.rpart), idx, wts, s, mk);
 
-    const int ch = mfma ? pf::kTok : L.ch;
+    // tokens per work item of the MFMA kernels: 64 once the routed experts
+    // average 48 tokens or more (fewer weight re-reads, each staged block used
+    // by up to four token groups), else 32 (more workgroups per CU)
+    const int kt = (T * K >= 48 * (int64_t)E) ? 64 : 32;
+    const int ch = mfma ? kt : L.ch;
     const int64_t n_it = max_items_for(c, T, ch);
     mk.mark("bucket_lists");
     launch(mk, k_bucket_lists, E + S, 256, 0, s, idx, (int)T, K, E, S, lists, counts);
@@ -408,31 +431,15 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         const int64_t NS = L.pub.n_slots;
         mk.mark("scale_int_x");
         launch(mk, pf::k_scale_int, (unsigned)((T + 3) / 4), 256, 0, s, dx, T, H / 32, mxp, exp_);
-        mk.mark("pf_gateup");
         const dim3 g1((unsigned)((I / pf::kRows) * n_it));
         const dim3 g2((unsigned)(((H + pf::kDnRows - 1) / pf::kDnRows) * n_it));
-        if (bits == 4) {
-            if (tap) launch(mk, pf::k_pf_gateup<4, true>, g1, 256, 0, s, pa);
-            else launch(mk, pf::k_pf_gateup<4, false>, g1, 256, 0, s, pa);
+        auto h_scales = [&] {
             mk.mark("scale_int_h");
             launch(mk, pf::k_scale_int, (unsigned)((NS + 3) / 4), 256, 0, s, dh, NS, I / 32, mhp, ehp);
-            mk.mark("pf_down");
-            launch(mk, pf::k_pf_down<4>, g2, 256, 0, s, pa);
-        } else if (bits == 8) {
-            if (tap) launch(mk, pf::k_pf_gateup<8, true>, g1, 256, 0, s, pa);
-            else launch(mk, pf::k_pf_gateup<8, false>, g1, 256, 0, s, pa);
-            mk.mark("scale_int_h");
-            launch(mk, pf::k_scale_int, (unsigned)((NS + 3) / 4), 256, 0, s, dh, NS, I / 32, mhp, ehp);
-            mk.mark("pf_down");
-            launch(mk, pf::k_pf_down<8>, g2, 256, 0, s, pa);
-        } else {
-            if (tap) launch(mk, pf::k_pf_gateup<2, true>, g1, 256, 0, s, pa);
-            else launch(mk, pf::k_pf_gateup<2, false>, g1, 256, 0, s, pa);
-            mk.mark("scale_int_h");
-            launch(mk, pf::k_scale_int, (unsigned)((NS + 3) / 4), 256, 0, s, dh, NS, I / 32, mhp, ehp);
-            mk.mark("pf_down");
-            launch(mk, pf::k_pf_down<2>, g2, 256, 0, s, pa);
-        }
+        };
+        if (bits == 4) launch_pf<4>(kt, tap != nullptr, g1, g2, pa, h_scales, s, mk);
+        else if (bits == 8) launch_pf<8>(kt, tap != nullptr, g1, g2, pa, h_scales, s, mk);
+        else launch_pf<2>(kt, tap != nullptr, g1, g2, pa, h_scales, s, mk);
     } else {
     const int nt = (T >= L.ch) ? L.ch : (int)T;  // tokens per item at most
     const int nbj_h = (H / 32 + 63) / 64;

@@ -1,6 +1,6 @@
 // Grouped int8 MFMA kernels for many tokens (prefill, stacked layers).
 //
-// Work item = (expert, first slot, n <= 32 of its tokens). A workgroup takes
+// Work item = (expert, first slot, n <= 32 or 64 of its tokens). A workgroup takes
 // one item and a tile of output rows; each wave owns two 16-row tiles (gate/up:
 // 16 gate rows and the matching 16 up rows, so SwiGLU needs no exchange; down:
 // 32 consecutive output rows). Per 32-wide block b every wave issues
@@ -48,13 +48,16 @@ namespace pf {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kTok = 32;      // tokens per work item
+// Tokens per work item, KT: 32 or 64 (groups of 16; the host takes 64 when
+// the routed experts average 48 tokens or more). Kernels are instantiated for
+// both, since the 64-token form needs more registers and LDS per workgroup.
+constexpr int kTokMax = 64;
 constexpr int kRows = 64;     // gate/up: h rows per workgroup (16 per wave)
 constexpr int kDnRows = 128;  // down: output rows per workgroup (32 per wave)
 constexpr int kSlots = 3;     // LDS ring: one stage computed, two loading
 
 // Stage geometry of one weight width (2, 4 or 8 bits).
-template <int BITS>
+template <int BITS, int KT>
 struct Geo {
     static constexpr int CH = 4;                         // 32-blocks per stage
     static constexpr int WB = 4 * BITS;                  // bytes of a row's block
@@ -69,14 +72,16 @@ struct Geo {
     static constexpr int AKS = ARB >= 256 ? 1 : 256 / ARB;
     static constexpr int ARPI = 1024 / ARB;              // token rows per load instruction
     static constexpr int A_OFF = 4 * WBYTES;
-    static constexpr int D_OFF = A_OFF + kTok * ARB;
-    static constexpr int SLOT = (D_OFF + kTok * CH * 4 + 255) & ~255;
+    static constexpr int kTok = KT;
+    static constexpr int kMaxG = KT / 16;
+    static constexpr int D_OFF = A_OFF + KT * ARB;
+    static constexpr int SLOT = (D_OFF + KT * CH * 4 + 255) & ~255;
     static constexpr int Scale = BITS == 4 ? 16 : BITS == 2 ? 64 : 1;  // code multiplier
     static constexpr double InvScale = 1.0 / Scale;                    // exact
     static constexpr int Layout = BITS == 4 ? 1 : BITS == 2 ? 2 : 0;   // activation order
     // activation loads per wave and stage for NG 16-token groups (they cover
     // 4 * AIW * ARPI >= 16 NG token rows)
-    static constexpr int aiw(int NG) { return NG * ARB / 256 > 0 ? NG * ARB / 256 : 1; }
+    static constexpr int aiw(int NG) { return (NG * ARB + 255) / 256; }
     static_assert(RB >= 32 && RB <= 256 && ARB <= 256, "stage geometry");
     // 16 rows / tokens span whole swizzle-key periods
     static_assert(16 % (NPC * KS) == 0 && 16 % (ANPC * AKS) == 0, "swizzle keys");
@@ -220,12 +225,16 @@ __device__ __forceinline__ int skey(int j) { return CH == 8 ? (j >> 3) & 1 : 0; 
 
 // Per-lane load plan of one wave for a stage: WINSTR weight loads (staged
 // rows 16t + i of tile t), AIW activation loads and one load of block scales.
-template <int BITS, int NG>
+template <int BITS, int KT, int NG>
 struct Plan {
-    typedef Geo<BITS> G;
+    typedef Geo<BITS, KT> G;
     static constexpr int AIW = G::aiw(NG);
     static constexpr int TPI = 64 / G::CH;         // tokens per scale load
     static constexpr int LD = G::WINSTR + AIW + 1;  // loads per wave and stage
+    // the waves' scale loads cover the item's tokens (with 32-token items
+    // waves 2 and 3 repeat those of waves 0 and 1)
+    static_assert(4 * TPI >= G::kTok && G::kTok % TPI == 0, "scale loads");
+    static_assert(4 * AIW * G::ARPI >= 16 * NG && 4 * AIW * G::ARPI <= G::kTok, "activation loads");
     const uint8_t* wrow[G::WINSTR];  // this lane's weight row
     int wpo[G::WINSTR];              // byte offset of its piece in the stage
     int rowb;
@@ -264,8 +273,7 @@ struct Plan {
             arow[i] = act + (int64_t)rows_of[min(j, n - 1)] * arowb_;
             apo[i] = piece * 16;
         }
-        // with CH = 4 waves 2 and 3 repeat the loads of waves 0 and 1
-        const int js = (wave * TPI) % kTok + lane / G::CH;
+        const int js = (wave * TPI) % G::kTok + lane / G::CH;
         sbk = (lane % G::CH) ^ skey<G::CH>(js);
         srow = static_cast<const uint8_t*>(scales) + (int64_t)rows_of[min(js, n - 1)] * NB_ * 4;
     }
@@ -283,7 +291,7 @@ struct Plan {
             dma_b128(arow[i] + min(c * G::ARB + apo[i], arowb - 16), adst + i * 1024);
         const int b = c * G::CH + sbk;
         dma_b32(b < NB ? static_cast<const void*>(srow + 4 * b) : &kZeroScale,
-                slot + G::D_OFF + ((wave * TPI) % kTok) * G::CH * 4);
+                slot + G::D_OFF + ((wave * TPI) % G::kTok) * G::CH * 4);
     }
 };
 
@@ -294,24 +302,25 @@ struct Plan {
 // the end; else the scales are floats and the sum is fp64 (one conversion
 // and one fma per element and block). TAP records the exact block dots of
 // tile 0 for sampled rows.
-template <int BITS, int NG, bool TAP, bool INT>
-__device__ __forceinline__ void mm_loop(const Plan<BITS, NG>& pl, uint8_t* smem,
-                                        double (&acc)[2][2][4], const int (&etok)[2], int nst,
+template <int BITS, int KT, int NG, bool TAP, bool INT>
+__device__ __forceinline__ void mm_loop(const Plan<BITS, KT, NG>& pl, uint8_t* smem,
+                                        double (&acc)[2][KT / 16][4], const int (&etok)[KT / 16], int nst,
                                         const PfArgs& a, int tap_r0, int s0, int n) {
-    typedef Geo<BITS> G;
-    constexpr int LD = Plan<BITS, NG>::LD;
+    typedef Geo<BITS, KT> G;
+    constexpr int kMaxG = G::kMaxG;
+    constexpr int LD = Plan<BITS, KT, NG>::LD;
     const int lane = threadIdx.x & 63;
     const int lr = lane & 15, q = lane >> 4;
-    long acci[2][2][4];
+    long acci[2][NG][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[t][g][i] = 0.0;
-                acci[t][g][i] = 0;
-            }
+            for (int g = 0; g < kMaxG; ++g) acc[t][g][i] = 0.0;
+#pragma unroll
+            for (int g = 0; g < NG; ++g) acci[t][g][i] = 0;
+        }
     // slot-relative lane bases of the operand reads; the block index of the
     // stage is XORed into the piece bits (no carries: the other terms have
     // those bits clear)
@@ -404,7 +413,7 @@ __device__ __forceinline__ void mm_loop(const Plan<BITS, NG>& pl, uint8_t* smem,
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
+            for (int g = 0; g < NG; ++g)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) acc[t][g][i] = ldexp((double)acci[t][g][i], etok[g]);
     }
@@ -421,11 +430,12 @@ __device__ __forceinline__ constexpr int act_elem(int p) {
 
 // Gate/up + SwiGLU + Q8_0(h) for one item and 64 intermediate rows; Q8_0(h)
 // is stored in the activation order of the down weights' width.
-template <int BITS, bool TAP>
+template <int BITS, int KT, bool TAP>
 __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
-    typedef Geo<BITS> G;
+    typedef Geo<BITS, KT> G;
+    constexpr int kMaxG = KT / 16;
     __shared__ __align__(1024) uint8_t smem[kSlots * G::SLOT];
-    static_assert(kSlots * G::SLOT >= kTok * (kRows + 1) * 4, "h reuses the ring");
+    static_assert(kSlots * G::SLOT >= KT * (kRows + 1) * 4, "h reuses the ring");
     const int nrt = a.I / kRows;
     const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
     if (it >= *a.n_items) return;
@@ -446,28 +456,31 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
     // integer scales unless a token of the item has none
     const int tv = rows_of[min((int)threadIdx.x, n - 1)];
     const bool wide = __syncthreads_or((int)threadIdx.x < n && a.ex[tv] == kWideRow);
-    int etok[2];
+    int etok[kMaxG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) etok[g] = a.ex[rows_of[min(16 * g + lr, n - 1)]];
-    double acc[2][2][4];
+    for (int g = 0; g < kMaxG; ++g) etok[g] = a.ex[rows_of[min(16 * g + lr, n - 1)]];
+    double acc[2][kMaxG][4];
     auto run = [&](auto ng, auto in) {
         constexpr int NG = decltype(ng)::value;
         constexpr bool INT = decltype(in)::value;
-        Plan<BITS, NG> pl;
+        Plan<BITS, KT, NG> pl;
         pl.init(tiles, nrow, rowb, a.qx, H, rows_of, n,
                 INT ? static_cast<const void*>(a.mx) : static_cast<const void*>(a.dx), BH);
-        mm_loop<BITS, NG, TAP, INT>(pl, smem, acc, etok, nst, a, r0, s0, n);
+        mm_loop<BITS, KT, NG, TAP, INT>(pl, smem, acc, etok, nst, a, r0, s0, n);
     };
     typedef std::integral_constant<int, 1> G1;
     typedef std::integral_constant<int, 2> G2;
+    typedef std::integral_constant<int, 4> G4;
     typedef std::integral_constant<bool, true> Int;
     typedef std::integral_constant<bool, false> F64;
     if (!wide) {
         if (n <= 16) run(G1{}, Int{});
-        else run(G2{}, Int{});
+        else if (KT == 32 || n <= 32) run(G2{}, Int{});
+        else if constexpr (KT == 64) run(G4{}, Int{});
     } else {
         if (n <= 16) run(G1{}, F64{});
-        else run(G2{}, F64{});
+        else if (KT == 32 || n <= 32) run(G2{}, F64{});
+        else if constexpr (KT == 64) run(G4{}, F64{});
     }
     __syncthreads();  // the ring is reused for h below
     float (*hbuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(smem);
@@ -480,7 +493,7 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
         const int r = r0 + 4 * q + i;
         const float gsr = gs[r], usr = us[r];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < kMaxG; ++g) {
             // the sums carry the multiplier of the weight codes: scale it away (exact)
             const float gv = (float)((double)gsr * (acc[0][g][i] * G::InvScale));
             const float uv = (float)((double)usr * (acc[1][g][i] * G::InvScale));
@@ -513,12 +526,13 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
 // Down projection for one item and 128 output rows: ye[slot, row] =
 // fp32(s_down[row] * sum_b d_h,b * I_b). The last row tile may pass H (rows
 // clamped for loading, not stored).
-template <int BITS>
+template <int BITS, int KT>
 __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
-    typedef Geo<BITS> G;
+    typedef Geo<BITS, KT> G;
+    constexpr int kMaxG = KT / 16;
     __shared__ __align__(1024) uint8_t smem[kSlots * G::SLOT];
-    static_assert(kSlots * G::SLOT >= kTok * (kDnRows + 1) * 4, "y reuses the ring");
-    __shared__ int s_rows[kTok];
+    static_assert(kSlots * G::SLOT >= KT * (kDnRows + 1) * 4, "y reuses the ring");
+    __shared__ int s_rows[KT];
     const int nrt = (a.H + kDnRows - 1) / kDnRows;
     const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
     if (it >= *a.n_items) return;
@@ -532,7 +546,7 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     const int R0 = rt * kDnRows + wave * 32;
     const int nst = (BI + G::CH - 1) / G::CH;
     // the item's slots are consecutive rows of q_h
-    if (threadIdx.x < kTok) s_rows[threadIdx.x] = s0 + threadIdx.x;
+    if (threadIdx.x < KT) s_rows[threadIdx.x] = s0 + threadIdx.x;
     __syncthreads();
 
     // rows past H are clamped to H - 1 (tile bases stay inside the matrix)
@@ -542,28 +556,31 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     // integer scales unless a slot of the item has none
     const bool wide =
         __syncthreads_or((int)threadIdx.x < n && a.eh[s0 + min((int)threadIdx.x, n - 1)] == kWideRow);
-    int etok[2];
+    int etok[kMaxG];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) etok[g] = a.eh[s0 + min(16 * g + lr, n - 1)];
-    double acc[2][2][4];
+    for (int g = 0; g < kMaxG; ++g) etok[g] = a.eh[s0 + min(16 * g + lr, n - 1)];
+    double acc[2][kMaxG][4];
     auto run = [&](auto ng, auto in) {
         constexpr int NG = decltype(ng)::value;
         constexpr bool INT = decltype(in)::value;
-        Plan<BITS, NG> pl;
+        Plan<BITS, KT, NG> pl;
         pl.init(tiles, nrow, rowb, a.qh, I, s_rows, n,
                 INT ? static_cast<const void*>(a.mh) : static_cast<const void*>(a.dh), BI);
-        mm_loop<BITS, NG, false, INT>(pl, smem, acc, etok, nst, a, 0, s0, n);
+        mm_loop<BITS, KT, NG, false, INT>(pl, smem, acc, etok, nst, a, 0, s0, n);
     };
     typedef std::integral_constant<int, 1> G1;
     typedef std::integral_constant<int, 2> G2;
+    typedef std::integral_constant<int, 4> G4;
     typedef std::integral_constant<bool, true> Int;
     typedef std::integral_constant<bool, false> F64;
     if (!wide) {
         if (n <= 16) run(G1{}, Int{});
-        else run(G2{}, Int{});
+        else if (KT == 32 || n <= 32) run(G2{}, Int{});
+        else if constexpr (KT == 64) run(G4{}, Int{});
     } else {
         if (n <= 16) run(G1{}, F64{});
-        else run(G2{}, F64{});
+        else if (KT == 32 || n <= 32) run(G2{}, F64{});
+        else if constexpr (KT == 64) run(G4{}, F64{});
     }
     __syncthreads();  // the ring is reused for y below
     float (*ybuf)[kDnRows + 1] = reinterpret_cast<float (*)[kDnRows + 1]>(smem);
@@ -576,7 +593,7 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
             const int rl = wave * 32 + 16 * t + 4 * q + i;
             const float dsr = ds[min(rt * kDnRows + rl, H - 1)];
 #pragma unroll
-            for (int g = 0; g < 2; ++g)  // undo the multiplier of the weight codes
+            for (int g = 0; g < kMaxG; ++g)  // undo the multiplier of the weight codes
                 ybuf[16 * g + lr][rl] = (float)((double)dsr * (acc[t][g][i] * G::InvScale));
         }
     __syncthreads();

@@ -3,7 +3,10 @@
 - The kernels without debug taps (the ones a caller runs) give the same
   output, bit for bit, as the tapped kernels the parity tests compare with the
   oracle: full-size prefill (T = 512, int4) and mid-size layers of every
-  weight width.
+  weight width, with 32-token items and with 64-token items (taken once the
+  routed experts average 48 tokens or more).
+- 64-token items (1, 2 or 4 groups of 16) at parity with the oracle on every
+  token of a small layer.
 - Rows whose Q8_0 block scales span more than 2^7 have no 31-bit integer form
   (the exact int64 sum of the K loop needs one), so their items take the fp64
   epilogue: an input token with one block scaled by 1e-4 (x side) and a shared
@@ -18,7 +21,7 @@ import pytest
 import torch
 
 import coli_synth as cs
-from gpu_util import gpu_layer, layer_input, lib_cfg
+from gpu_util import gpu_layer, layer_input, lib_cfg, oracle_layer_for
 from test_gpu_layer import compare, run_gpu
 
 pytestmark = pytest.mark.gpu
@@ -66,9 +69,10 @@ def test_untapped_kernels_match_tapped_full_prefill(C, ref):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("bits", [8, 4, 2])
-def test_untapped_kernels_match_tapped_widths(C, ref, bits):
-    cfg = dataclasses.replace(cs.CONFIGS[3], name="mid T200 H1024 E32 K4 I512", n_tok=200,
+@pytest.mark.parametrize("bits,n_tok", [(8, 200), (4, 200), (2, 200), (8, 800), (4, 800), (2, 800)])
+def test_untapped_kernels_match_tapped_widths(C, ref, bits, n_tok):
+    # 200 tokens: 25 per routed expert (32-token items); 800: 100 (64-token items)
+    cfg = dataclasses.replace(cs.CONFIGS[3], name=f"mid T{n_tok} H1024 E32 K4 I512", n_tok=n_tok,
                               hidden=1024, n_experts=32, top_k=4, inter=512)
     _note(cfg.name, "bits", bits)
     W = _bits_layer(C, cfg, bits)
@@ -79,8 +83,9 @@ def test_untapped_kernels_match_tapped_widths(C, ref, bits):
     np.testing.assert_array_equal(y0, y1)
 
 
-def _wide_cfg():
-    return dataclasses.replace(cs.CONFIGS[0], name="wide scales T40 H256 E16 K2 I128", n_tok=40)
+def _wide_cfg(n_tok=40):
+    return dataclasses.replace(cs.CONFIGS[0], name=f"wide scales T{n_tok} H256 E16 K2 I128",
+                               n_tok=n_tok)
 
 
 def _wide_layer(C, cfg):
@@ -112,8 +117,9 @@ def _wide_oracle(ref, cfg, x):
     return L
 
 
-def test_wide_scale_rows_take_the_fp64_epilogue(C, ref):
-    cfg = _wide_cfg()
+@pytest.mark.parametrize("n_tok", [40, 400])  # 32- and 64-token items
+def test_wide_scale_rows_take_the_fp64_epilogue(C, ref, n_tok):
+    cfg = _wide_cfg(n_tok)
     _note(cfg.name)
     W = _wide_layer(C, cfg)
     x = layer_input(ref, cfg)
@@ -133,3 +139,20 @@ def test_wide_scale_rows_take_the_fp64_epilogue(C, ref):
     assert err <= TOL_REL_L2
     y0 = _forward(C, W, x, 0)
     np.testing.assert_array_equal(y0, y)
+
+
+def test_64_token_items_at_oracle_parity(C, ref):
+    # 400 tokens x 2 of 16 experts: 50 per expert, items of 50 and 64 tokens
+    # (four groups of 16), 64-token items of the shared expert and a 16-token tail
+    cfg = dataclasses.replace(cs.CONFIGS[0], name="items64 T400 H256 E16 K2 I128", n_tok=400)
+    _note(cfg.name)
+    W = gpu_layer(C, cfg)
+    x = layer_input(ref, cfg)
+    y, taps = run_gpu(C, W, x)
+    tokens = list(range(cfg.n_tok))
+    OL = oracle_layer_for(ref, cfg, 0, x)
+    err, flips = compare(ref, cfg, OL, x, y, taps, tokens)
+    _note("rel_l2", err, "flips", flips)
+    assert flips == 0
+    assert err <= TOL_REL_L2
+    np.testing.assert_array_equal(_forward(C, W, x, 0), y)
