@@ -44,28 +44,36 @@ __global__ __launch_bounds__(256) void k_router_gemv(const float* __restrict__ x
 }
 
 // Router logits for many tokens: a 64-token x 64-expert tile per workgroup
-// over one of `ksplit` equal slices of the hidden dimension; each thread
-// accumulates a 4 x 4 block of the tile in fp64 (sequential over its slice).
-// Operands are converted to fp64 in LDS, stored k-major so a thread's four
-// tokens (four experts) are two 16-byte reads. Partial sums go to
+// over one of `ksplit` equal slices of the hidden dimension, on the fp64
+// matrix cores: each wave computes a 32 x 32 quarter as 2 x 2 tiles of
+// v_mfma_f64_16x16x4f64 (A: lane l holds token l % 16 at k = l / 16; B:
+// expert l % 16 at k = l / 16; result register i of lane l is token
+// l / 16 + 4 i, expert l % 16; checked on the device). Products of the fp32
+// inputs are exact in fp64; the slice's sum is fp64, four terms per step.
+// Operands are converted to fp64 in LDS ([row][k], pitch 33: the 16 rows x 4
+// k of an operand read hit distinct banks per 16 lanes). Partial sums go to
 // part[slice][t][e]; k_router_reduce adds the slices in order.
 constexpr int kRouterTile = 64;
 constexpr int kRouterK = 32;
+
+typedef double v4d __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x,
                                                      const float* __restrict__ wr, int T, int H,
                                                      int E, int ksplit,
                                                      double* __restrict__ part) {
-    __shared__ __align__(16) double xs[kRouterK][kRouterTile + 2];
-    __shared__ __align__(16) double ws[kRouterK][kRouterTile + 2];
+    __shared__ double xs[kRouterTile][kRouterK + 1];
+    __shared__ double ws[kRouterTile][kRouterK + 1];
     const int t0 = blockIdx.x * kRouterTile, e0 = blockIdx.y * kRouterTile;
     const int kper = H / ksplit, kbeg = blockIdx.z * kper;
-    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    double acc[4][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tr = (wave >> 1) * 32, ec = (wave & 1) * 32;  // this wave's quarter
+    const int r16 = lane & 15, kq = lane >> 4;
+    v4d acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+        for (int b = 0; b < 2; ++b) acc[a][b] = v4d{0.0, 0.0, 0.0, 0.0};
     for (int k0 = kbeg; k0 < kbeg + kper; k0 += kRouterK) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -73,39 +81,41 @@ __global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f), w = v;
             if (t0 + row < T) v = *reinterpret_cast<const float4*>(x + (int64_t)(t0 + row) * H + k0 + c4 * 4);
             if (e0 + row < E) w = *reinterpret_cast<const float4*>(wr + (int64_t)(e0 + row) * H + k0 + c4 * 4);
-            xs[c4 * 4 + 0][row] = v.x;
-            xs[c4 * 4 + 1][row] = v.y;
-            xs[c4 * 4 + 2][row] = v.z;
-            xs[c4 * 4 + 3][row] = v.w;
-            ws[c4 * 4 + 0][row] = w.x;
-            ws[c4 * 4 + 1][row] = w.y;
-            ws[c4 * 4 + 2][row] = w.z;
-            ws[c4 * 4 + 3][row] = w.w;
+            xs[row][c4 * 4 + 0] = v.x;
+            xs[row][c4 * 4 + 1] = v.y;
+            xs[row][c4 * 4 + 2] = v.z;
+            xs[row][c4 * 4 + 3] = v.w;
+            ws[row][c4 * 4 + 0] = w.x;
+            ws[row][c4 * 4 + 1] = w.y;
+            ws[row][c4 * 4 + 2] = w.z;
+            ws[row][c4 * 4 + 3] = w.w;
         }
         __syncthreads();
-#pragma unroll 8
-        for (int k = 0; k < kRouterK; ++k) {
-            const double2 a01 = *reinterpret_cast<const double2*>(&xs[k][ty * 4]);
-            const double2 a23 = *reinterpret_cast<const double2*>(&xs[k][ty * 4 + 2]);
-            const double2 b01 = *reinterpret_cast<const double2*>(&ws[k][tx * 4]);
-            const double2 b23 = *reinterpret_cast<const double2*>(&ws[k][tx * 4 + 2]);
-            const double av[4] = {a01.x, a01.y, a23.x, a23.y};
-            const double bv[4] = {b01.x, b01.y, b23.x, b23.y};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int k = 0; k < kRouterK; k += 4) {
+            double av[2], bv[2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * bv[j];
+            for (int a = 0; a < 2; ++a) av[a] = xs[tr + 16 * a + r16][k + kq];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) bv[b] = ws[ec + 16 * b + r16][k + kq];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
         }
         __syncthreads();
     }
     double* out = part + (int64_t)blockIdx.z * T * E;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
-            if (t < T && e < E) out[(int64_t)t * E + e] = acc[i][j];
-        }
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + tr + 16 * a + kq + 4 * i, e = e0 + ec + 16 * b + r16;
+                if (t < T && e < E) out[(int64_t)t * E + e] = acc[a][b][i];
+            }
 }
 
 // logits[i] = sum over slices s = 0 .. ksplit-1 of part[s][i], in that order.
