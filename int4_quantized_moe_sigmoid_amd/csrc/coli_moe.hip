@@ -471,7 +471,7 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
     }
     mk.mark("combine");
     {
-        dim3 grid((unsigned)(((H + 255) / 256) * T));
+        dim3 grid((unsigned)(((H + 1023) / 1024) * T));
         launch(mk, k_combine, grid, 256, 0, s, ye, slot_of, wts, K, S, H, y,
                                        (flags & COLI_FWD_ACCUM) ? 1 : 0);
     }

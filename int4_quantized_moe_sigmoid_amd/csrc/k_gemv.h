@@ -188,22 +188,51 @@ __global__ __launch_bounds__(256) void k_down_gemv(const uint8_t* __restrict__ e
 }
 
 // y[t] = fp32( sum_k w[t,k] * y_e[slot(t,k)] + y_e[slot(t,shared)] ), fp64, k ascending.
+// A thread takes four consecutive columns of one token (H % 32 == 0) and
+// issues the loads of up to eight slots before it adds them up.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ ye,
                                                  const int32_t* __restrict__ slot_of,
                                                  const float* __restrict__ w, int K, int S, int H,
                                                  float* __restrict__ y, int accum) {
-    const int nb = (H + 255) >> 8;
+    const int nb = (H + 1023) >> 10;
     const int t = blockIdx.x / nb;
-    const int c = (blockIdx.x - t * nb) * 256 + threadIdx.x;
+    const int c = ((blockIdx.x - t * nb) * 256 + threadIdx.x) * 4;
     if (c >= H) return;
     const int KS = K + S;
-    double acc = 0.0;
-    for (int k = 0; k < K; ++k) {
-        const int s = slot_of[(int64_t)t * KS + k];
-        acc += (double)w[(int64_t)t * K + k] * (double)ye[(int64_t)s * H + c];
+    const int32_t* so = slot_of + (int64_t)t * KS;
+    const float* wt = w + (int64_t)t * K;
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
+    constexpr int B = 8;
+    for (int k0 = 0; k0 < K; k0 += B) {
+        float4 v[B];
+        double wk[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (k0 + j < K) {
+                v[j] = *reinterpret_cast<const float4*>(ye + (int64_t)so[k0 + j] * H + c);
+                wk[j] = (double)wt[k0 + j];
+            }
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (k0 + j < K) {
+                a[0] += wk[j] * (double)v[j].x;
+                a[1] += wk[j] * (double)v[j].y;
+                a[2] += wk[j] * (double)v[j].z;
+                a[3] += wk[j] * (double)v[j].w;
+            }
     }
-    if (S) acc += (double)ye[(int64_t)slot_of[(int64_t)t * KS + K] * H + c];
-    const float v = (float)acc;
-    float* out = y + (int64_t)t * H + c;
-    *out = accum ? *out + v : v;
+    if (S) {
+        const float4 v = *reinterpret_cast<const float4*>(ye + (int64_t)so[K] * H + c);
+        a[0] += (double)v.x;
+        a[1] += (double)v.y;
+        a[2] += (double)v.z;
+        a[3] += (double)v.w;
+    }
+    float4 r = make_float4((float)a[0], (float)a[1], (float)a[2], (float)a[3]);
+    float4* out = reinterpret_cast<float4*>(y + (int64_t)t * H + c);
+    if (accum) {
+        const float4 o = *out;
+        r = make_float4(o.x + r.x, o.y + r.y, o.z + r.z, o.w + r.w);
+    }
+    *out = r;
 }
