@@ -230,9 +230,10 @@ struct Plan {
     typedef Geo<BITS, KT> G;
     static constexpr int AIW = G::aiw(NG);
     static constexpr int TPI = 64 / G::CH;         // tokens per scale load
-    static constexpr int LD = G::WINSTR + AIW + 1;  // loads per wave and stage
+    static constexpr int LD = G::WINSTR + AIW + 1;  // loads per wave and stage (with scales)
     // the waves' scale loads cover the item's tokens (with 32-token items
-    // waves 2 and 3 repeat those of waves 0 and 1)
+    // waves 0 and 1 load them all and waves 2 and 3 none: those waves wait
+    // on one load fewer per stage)
     static_assert(4 * TPI >= G::kTok && G::kTok % TPI == 0, "scale loads");
     static_assert(4 * AIW * G::ARPI >= 16 * NG && 4 * AIW * G::ARPI <= G::kTok, "activation loads");
     const uint8_t* wrow[G::WINSTR];  // this lane's weight row
@@ -245,6 +246,7 @@ struct Plan {
     int sbk;                         // block of the stage this lane's scale is
     int NB;                          // blocks per row
     int wave;
+    bool scl;                        // this wave loads block scales
 
     // tile[t]: row 0 of tile t (16 rows, `rowb` bytes apart, rows from
     // nrow[t] on clamped to its last); rows_of[j]: activation row of token j
@@ -273,7 +275,8 @@ struct Plan {
             arow[i] = act + (int64_t)rows_of[min(j, n - 1)] * arowb_;
             apo[i] = piece * 16;
         }
-        const int js = (wave * TPI) % G::kTok + lane / G::CH;
+        scl = wave * TPI < G::kTok;
+        const int js = min(wave * TPI, G::kTok - TPI) + lane / G::CH;
         sbk = (lane % G::CH) ^ skey<G::CH>(js);
         srow = static_cast<const uint8_t*>(scales) + (int64_t)rows_of[min(js, n - 1)] * NB_ * 4;
     }
@@ -289,9 +292,11 @@ struct Plan {
 #pragma unroll
         for (int i = 0; i < AIW; ++i)
             dma_b128(arow[i] + min(c * G::ARB + apo[i], arowb - 16), adst + i * 1024);
-        const int b = c * G::CH + sbk;
-        dma_b32(b < NB ? static_cast<const void*>(srow + 4 * b) : &kZeroScale,
-                slot + G::D_OFF + ((wave * TPI) % G::kTok) * G::CH * 4);
+        if (scl) {
+            const int b = c * G::CH + sbk;
+            dma_b32(b < NB ? static_cast<const void*>(srow + 4 * b) : &kZeroScale,
+                    slot + G::D_OFF + wave * TPI * G::CH * 4);
+        }
     }
 };
 
@@ -362,8 +367,12 @@ __device__ __forceinline__ void mm_loop(const Plan<BITS, KT, NG>& pl, uint8_t* s
             // not be); with TAP the stores of the taps share the counter and
             // need not complete in order with the loads, so that variant
             // waits for all
-            if (c + 1 < nst && !TAP) wait_vm<LD, false>();
-            else wait_vm<0, false>();
+            if (c + 1 < nst && !TAP) {
+                if (pl.scl) wait_vm<LD, false>();
+                else wait_vm<LD - 1, false>();
+            } else {
+                wait_vm<0, false>();
+            }
             stage_barrier();  // every wave's loads of stage c are in; slot c - 1 is free
             if (c + 2 < nst) pl.issue(c + 2, lds0 + ((sl + 2) % kSlots) * G::SLOT);
 #pragma unroll
