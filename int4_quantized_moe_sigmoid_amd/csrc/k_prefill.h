@@ -48,14 +48,14 @@ namespace pf {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Tokens per work item, KT: 32 or 64 (groups of 16; the host takes 64 when
-// the routed experts average 48 tokens or more). Kernels are instantiated for
-// both, since the 64-token form needs more registers and LDS per workgroup.
 constexpr int kRows = 64;     // gate/up: h rows per workgroup (16 per wave)
 constexpr int kDnRows = 128;  // down: output rows per workgroup (32 per wave)
 constexpr int kSlots = 3;     // LDS ring: one stage computed, two loading
 
-// Stage geometry of one weight width (2, 4 or 8 bits).
+// Stage geometry of one weight width (2, 4 or 8 bits) and item size KT (32
+// or 64 tokens, in groups of 16; the host takes 64 when the routed experts
+// average 48 tokens or more). Kernels are instantiated for both sizes, since
+// the 64-token form needs more registers and LDS per workgroup.
 template <int BITS, int KT>
 struct Geo {
     static constexpr int CH = 4;                         // 32-blocks per stage
