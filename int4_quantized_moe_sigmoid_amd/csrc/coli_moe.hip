@@ -427,13 +427,22 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         int32_t* exp_ = reinterpret_cast<int32_t*>(base + L.ex);
         int32_t* mhp = reinterpret_cast<int32_t*>(base + L.mh);
         int32_t* ehp = reinterpret_cast<int32_t*>(base + L.eh);
-        pa.mx = mxp; pa.ex = exp_; pa.mh = mhp; pa.eh = ehp;
+        // integer block scales (exact int64 sums in the K loop) from 16 tokens
+        // on; below that their two launches cost more than they save, and
+        // the kernels take the fp64 epilogue
+        const bool int_scales = T >= 16;
+        if (int_scales) {
+            pa.mx = mxp; pa.ex = exp_; pa.mh = mhp; pa.eh = ehp;
+        }
         const int64_t NS = L.pub.n_slots;
-        mk.mark("scale_int_x");
-        launch(mk, pf::k_scale_int, (unsigned)((T + 3) / 4), 256, 0, s, dx, T, H / 32, mxp, exp_);
+        if (int_scales) {
+            mk.mark("scale_int_x");
+            launch(mk, pf::k_scale_int, (unsigned)((T + 3) / 4), 256, 0, s, dx, T, H / 32, mxp, exp_);
+        }
         const dim3 g1((unsigned)((I / pf::kRows) * n_it));
         const dim3 g2((unsigned)(((H + pf::kDnRows - 1) / pf::kDnRows) * n_it));
         auto h_scales = [&] {
+            if (!int_scales) return;
             mk.mark("scale_int_h");
             launch(mk, pf::k_scale_int, (unsigned)((NS + 3) / 4), 256, 0, s, dh, NS, I / 32, mhp, ehp);
         };

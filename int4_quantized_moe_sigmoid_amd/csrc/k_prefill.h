@@ -461,12 +461,16 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
     const uint8_t* const tiles[2] = {gate + (int64_t)r0 * rowb, up + (int64_t)r0 * rowb};
     const int nrow[2] = {16, 16};
     const int32_t* rows_of = a.slot_tok + s0;  // token of each of the item's slots
-    // integer scales unless a token of the item has none
-    const int tv = rows_of[min((int)threadIdx.x, n - 1)];
-    const bool wide = __syncthreads_or((int)threadIdx.x < n && a.ex[tv] == kWideRow);
-    int etok[kMaxG];
+    // integer scales unless the call has none (few tokens) or a token of the
+    // item has none
+    bool wide = a.ex == nullptr;
+    int etok[kMaxG] = {};
+    if (!wide) {
+        const int tv = rows_of[min((int)threadIdx.x, n - 1)];
+        wide = __syncthreads_or((int)threadIdx.x < n && a.ex[tv] == kWideRow);
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g) etok[g] = a.ex[rows_of[min(16 * g + lr, n - 1)]];
+        for (int g = 0; g < kMaxG; ++g) etok[g] = a.ex[rows_of[min(16 * g + lr, n - 1)]];
+    }
     double acc[2][kMaxG][4];
     auto run = [&](auto ng, auto in) {
         constexpr int NG = decltype(ng)::value;
@@ -561,12 +565,16 @@ __global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
     const int t0 = min(R0, H - 1), t1 = min(R0 + 16, H - 1);
     const uint8_t* const tiles[2] = {down + (int64_t)t0 * rowb, down + (int64_t)t1 * rowb};
     const int nrow[2] = {max(1, min(16, H - t0)), max(1, min(16, H - t1))};
-    // integer scales unless a slot of the item has none
-    const bool wide =
-        __syncthreads_or((int)threadIdx.x < n && a.eh[s0 + min((int)threadIdx.x, n - 1)] == kWideRow);
-    int etok[kMaxG];
+    // integer scales unless the call has none (few tokens) or a slot of the
+    // item has none
+    bool wide = a.eh == nullptr;
+    int etok[kMaxG] = {};
+    if (!wide) {
+        wide = __syncthreads_or((int)threadIdx.x < n &&
+                                a.eh[s0 + min((int)threadIdx.x, n - 1)] == kWideRow);
 #pragma unroll
-    for (int g = 0; g < kMaxG; ++g) etok[g] = a.eh[s0 + min(16 * g + lr, n - 1)];
+        for (int g = 0; g < kMaxG; ++g) etok[g] = a.eh[s0 + min(16 * g + lr, n - 1)];
+    }
     double acc[2][kMaxG][4];
     auto run = [&](auto ng, auto in) {
         constexpr int NG = decltype(ng)::value;
