@@ -40,7 +40,7 @@ TRAFFIC = {
     ("dec_gateup", "mtp-verify T3 correlated"): (95923.0 * 2 + 84.8) * 1024,
     # profiles/pf_kernels_prefill_T512.txt, profiles/pf_kernels_prefill_T512_int8.txt
     ("pf_gateup", "prefill T512 zipf-bias"): (1819205.2 * 2 + 14437.5) * 1024,
-    ("pf_gateup", "prefill T512 zipf-bias int8 weights"): (3384531.1 * 2 + 14465.5) * 1024,
+    ("pf_gateup", "prefill T512 zipf-bias int8 weights"): (3383330.9 * 2 + 14460.6) * 1024,
     # profiles/pack_fp8_int4_layer.txt (the gate/up launch)
     ("pack_fp8_gateup", "pack_fp8 layer H6144 I2048 experts257"): (3164334.8 * 2 + 3166240.7) * 1024,
 }
