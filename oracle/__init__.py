@@ -48,6 +48,8 @@ def lib():
         L.coli_ref_block_dots.argtypes = [vp, i64, i64, vp, i64, vp]
         L.coli_ref_route.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                                      ctypes.c_double, i64, i64, vp, vp, vp]
+        L.coli_ref_gates.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                     ctypes.c_double, vp, vp]
         L.coli_ref_rmsnorm.argtypes = [vp, i64, i64, ctypes.c_double, vp]
         L.coli_ref_moe_forward.argtypes = [vp, vp, i64, vp, vp, vp, ctypes.c_int, vp]
         L.coli_ref_set_threads.argtypes = [ctypes.c_int]
@@ -183,6 +185,23 @@ def route(x, wr, bias, top_k: int, norm: bool = True, rho: float = 2.5, n_group:
                                 float(np.float32(rho)), int(n_group), int(topk_group), _p(idx),
                                 _p(w), _p(logits)), "route")
     return idx, w, logits
+
+
+def gates(x, wr, bias, idx, norm: bool = True, rho: float = 2.5) -> np.ndarray:
+    """Gate values the router gives the expert choice idx [T, K] (distinct
+    experts per token): w_k = s[idx_k] / sum_k s[idx_k] * rho (without the
+    division when norm is off), s the sigmoid of the router logits."""
+    x = _c(x, np.float32)
+    wr = _c(wr, np.float32)
+    bias = _c(bias, np.float32)
+    idx = _c(idx, np.int32)
+    T, H = x.shape
+    E = wr.shape[0]
+    K = idx.shape[1]
+    w = np.empty((T, K), np.float32)
+    _check(lib().coli_ref_gates(_p(x), _p(wr), _p(bias), T, H, E, K, int(norm),
+                                float(np.float32(rho)), _p(idx), _p(w)), "gates")
+    return w
 
 
 def rmsnorm(x, eps: float = 1e-5) -> np.ndarray:

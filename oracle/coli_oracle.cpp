@@ -256,10 +256,10 @@ static float ref_row_dot(const uint8_t* wrow, float s_r, const int8_t* q, const 
 // the lower group index) stay eligible and the K experts are chosen among
 // their experts only. n_group = 1 is the plain selection above.
 // ---------------------------------------------------------------------------
-static void ref_route_token(const float* x, const float* wr, const float* bias, int64_t H,
-                            int64_t E, int64_t K, int norm, double rho, int64_t n_group,
-                            int64_t topk_group, int32_t* idx, float* w, double* logits_out) {
-    std::vector<double> s(E), c(E);
+// Router scores of one token: l_e = x . W_r[e] (double sum over h), the
+// sigmoid s_e = 1 / (1 + exp(-l_e)) and the selection score c_e = s_e + b_e.
+static void ref_scores(const float* x, const float* wr, const float* bias, int64_t H,
+                       int64_t E, double* s, double* c, double* logits_out) {
     for (int64_t e = 0; e < E; ++e) {
         double l = 0.0;
         for (int64_t h = 0; h < H; ++h) l += (double)x[h] * (double)wr[e * H + h];
@@ -267,6 +267,27 @@ static void ref_route_token(const float* x, const float* wr, const float* bias, 
         s[e] = 1.0 / (1.0 + std::exp(-l));
         c[e] = s[e] + (double)bias[e];
     }
+}
+
+// Gate values of the chosen experts idx[0..K): the unbiased scores s, divided
+// by their sum (k ascending) when normalising, times rho, rounded to fp32.
+static void ref_gate_values(const double* s, const int32_t* idx, int64_t K, int norm,
+                            double rho, float* w) {
+    double sum = 0.0;
+    for (int64_t k = 0; k < K; ++k) sum += s[idx[k]];
+    for (int64_t k = 0; k < K; ++k) {
+        double v = s[idx[k]];
+        if (norm) v = v / sum;
+        v = v * rho;
+        w[k] = (float)v;
+    }
+}
+
+static void ref_route_token(const float* x, const float* wr, const float* bias, int64_t H,
+                            int64_t E, int64_t K, int norm, double rho, int64_t n_group,
+                            int64_t topk_group, int32_t* idx, float* w, double* logits_out) {
+    std::vector<double> s(E), c(E);
+    ref_scores(x, wr, bias, H, E, s.data(), c.data(), logits_out);
     std::vector<char> eligible(E, 1);
     if (n_group > 1) {
         const int64_t gs = E / n_group;
@@ -297,7 +318,6 @@ static void ref_route_token(const float* x, const float* wr, const float* bias, 
         for (int64_t e = 0; e < E; ++e) eligible[e] = kept[e / gs];
     }
     std::vector<char> taken(E, 0);
-    std::vector<double> wk(K);
     for (int64_t k = 0; k < K; ++k) {
         int64_t best = -1;
         for (int64_t e = 0; e < E; ++e) {
@@ -306,16 +326,8 @@ static void ref_route_token(const float* x, const float* wr, const float* bias, 
         }
         taken[best] = 1;
         idx[k] = (int32_t)best;
-        wk[k] = s[best];
     }
-    double sum = 0.0;
-    for (int64_t k = 0; k < K; ++k) sum += wk[k];
-    for (int64_t k = 0; k < K; ++k) {
-        double v = wk[k];
-        if (norm) v = v / sum;
-        v = v * rho;
-        w[k] = (float)v;
-    }
+    ref_gate_values(s.data(), idx, K, norm, rho, w);
 }
 
 // n_group >= 1 must divide n_experts; 1 <= topk_group <= n_group; the kept
@@ -335,6 +347,32 @@ int coli_ref_route(const float* x, const float* wr, const float* bias, int64_t n
         ref_route_token(x + t * hidden, wr, bias, hidden, n_experts, top_k, norm, rho, n_group,
                         topk_group, idx + t * top_k, w + t * top_k,
                         logits ? logits + t * n_experts : nullptr);
+    return REF_OK;
+}
+
+// Gate values the router gives a given choice of experts: for each token the
+// scores of ref_scores and the gate values of ref_gate_values for the K
+// experts idx[t][0..K) (distinct, in range), as coli_ref_route computes them
+// for its own choice. Used where several choices are correct (scores within a
+// tolerance of each other at the K-th place): the gate values of another
+// correct choice.
+int coli_ref_gates(const float* x, const float* wr, const float* bias, int64_t n_tok,
+                   int64_t hidden, int64_t n_experts, int64_t top_k, int norm, double rho,
+                   const int32_t* idx, float* w) {
+    if (!x || !wr || !bias || !idx || !w || n_tok < 0 || hidden <= 0 || n_experts <= 0 ||
+        top_k <= 0 || top_k > n_experts)
+        return REF_EINVAL;
+    std::vector<double> s(n_experts), c(n_experts);
+    for (int64_t t = 0; t < n_tok; ++t) {
+        const int32_t* it = idx + t * top_k;
+        for (int64_t k = 0; k < top_k; ++k) {
+            if (it[k] < 0 || it[k] >= n_experts) return REF_EINVAL;
+            for (int64_t j = 0; j < k; ++j)
+                if (it[j] == it[k]) return REF_EINVAL;
+        }
+        ref_scores(x + t * hidden, wr, bias, hidden, n_experts, s.data(), c.data(), nullptr);
+        ref_gate_values(s.data(), it, top_k, norm, rho, w + t * top_k);
+    }
     return REF_OK;
 }
 

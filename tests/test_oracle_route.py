@@ -84,3 +84,39 @@ def test_rejects_bad_k(ref):
     with pytest.raises(ValueError):
         ref.route(np.zeros((1, 32), np.float32), np.zeros((4, 32), np.float32),
                   np.zeros(4, np.float32), 5)
+
+
+def test_gates_of_the_router_choice_equal_its_weights(ref):
+    # invariant: the gate values the oracle gives its own choice are the
+    # router's weights, bit for bit, normalised and not
+    cfg = cs.CONFIGS[0]
+    x, wr, b = layer_inputs(cfg, n_tok=32)
+    for norm in (True, False):
+        idx, w, _ = ref.route(x, wr, b, cfg.top_k, norm, cfg.rho)
+        np.testing.assert_array_equal(ref.gates(x, wr, b, idx, norm, cfg.rho), w)
+
+
+def test_gates_of_another_choice(ref):
+    # closed form on any set of distinct experts, in any order: w_k =
+    # rho * s_k / sum s (k ascending) with s the sigmoid of the logits; the
+    # values follow the order of the given indices
+    rng = np.random.RandomState(12)
+    T, H, E, K = 16, 64, 20, 4
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (rng.standard_normal((E, H)) * 0.1).astype(np.float32)
+    b = (rng.standard_normal(E) * 0.01).astype(np.float32)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    lg = x.astype(np.float64) @ wr.astype(np.float64).T
+    s = np.take_along_axis(_sig(lg), idx.astype(np.int64), 1)
+    want = (2.5 * s / s.sum(axis=1, keepdims=True)).astype(np.float32)
+    got = ref.gates(x, wr, b, idx, True, 2.5)
+    np.testing.assert_allclose(got, want, rtol=2e-7)
+    np.testing.assert_allclose(got.astype(np.float64).sum(1), 2.5, rtol=1e-6)
+    # the bias plays no part in the gate value
+    np.testing.assert_array_equal(ref.gates(x, wr, np.zeros(E, np.float32), idx, True, 2.5), got)
+    rev = np.ascontiguousarray(idx[:, ::-1])
+    np.testing.assert_allclose(ref.gates(x, wr, b, rev, True, 2.5), got[:, ::-1], rtol=2e-7)
+    with pytest.raises(ValueError):
+        bad = idx.copy()
+        bad[0, 1] = bad[0, 0]
+        ref.gates(x, wr, b, bad, True, 2.5)
