@@ -72,3 +72,52 @@ def rel_l2(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+TIE_TOL = 1e-6
+
+
+def check_routing(ref, cfg, x, wr, b, gidx, gw, tol=TIE_TOL):
+    """Router parity of the GPU's choice (gidx, gw) for the token rows x.
+
+    Per token the index list equals the oracle's and the gate weights agree
+    within 1e-6 relative; or the GPU took another correct choice: distinct
+    experts in descending order of the oracle's selection score c = s + b
+    (neighbours within `tol` in either order), every expert in one list but
+    not the other with c within `tol` of the K-th largest c (the near-tie the
+    parity bar allows), and gate weights equal to the oracle's gate values for
+    that choice. Plain top-k only (no expert groups).
+
+    Returns (rows that took another correct choice, the oracle's gate values
+    for the GPU's choice, [rows, K])."""
+    K = cfg.top_k
+    x = np.ascontiguousarray(x, np.float32)
+    gidx = np.ascontiguousarray(gidx, np.int32)
+    ridx, rw, logits = ref.route(x, wr, b, K, cfg.norm_topk, cfg.rho)
+    c = 1.0 / (1.0 + np.exp(-logits)) + np.asarray(b, np.float64)
+    assert all(len(set(int(e) for e in row)) == K for row in gidx), "repeated expert"
+    w_for = ref.gates(x, wr, b, gidx, cfg.norm_topk, cfg.rho)
+    swaps = []
+    for t in range(x.shape[0]):
+        if list(gidx[t]) == list(ridx[t]):
+            np.testing.assert_allclose(gw[t], rw[t], rtol=1e-6)
+            continue
+        ct = c[t]
+        kth = np.sort(ct)[::-1][K - 1]
+        diff = set(int(e) for e in gidx[t]) ^ set(int(e) for e in ridx[t])
+        assert all(abs(ct[e] - kth) <= tol for e in diff), \
+            (t, list(gidx[t]), list(ridx[t]), [float(ct[e] - kth) for e in diff])
+        assert all(ct[gidx[t][k]] >= ct[gidx[t][k + 1]] - tol for k in range(K - 1)), \
+            (t, list(gidx[t]), "not in descending score order")
+        np.testing.assert_allclose(gw[t], w_for[t], rtol=1e-6)
+        swaps.append(t)
+    return swaps, w_for
+
+
+def add_missing_experts(ref, cfg, layer, OL, ids, draw_device="cuda", bits=4):
+    """Add (oracle-packed, from coli_synth's fp32 draw) the experts of ids that
+    OL does not hold yet."""
+    for e in sorted(set(int(v) for v in np.unique(ids)) - set(OL.experts)):
+        mats = [cs.expert_matrix(cfg, layer, e, w, draw_device).cpu().numpy()
+                for w in ("gate", "up", "down")]
+        OL.add_expert(e, ref.pack_expert(*mats, bits=bits))

@@ -59,3 +59,21 @@ def test_debug_tap_layout_for_the_largest_token_count():
         assert L.tap_rows == (2048 + L.tap_stride - 1) // L.tap_stride
         assert C.coli_moe_workspace_bytes(cfg, T, C.COLI_FWD_DEBUG_TAPS) >= L.total
     assert C.coli_moe_workspace_layout(cfg, 1 << 20, C.COLI_FWD_DEBUG_TAPS).tap_rows == 1
+
+
+def test_workspace_bytes_never_shrink_as_tokens_grow():
+    # a caller sizes the workspace once for its largest token count: every
+    # smaller count must fit (the few-token, router-split and tap regimes
+    # switch at different counts)
+    import int4_quantized_moe_sigmoid_amd as C
+    cfgs = [C.make_cfg(6144, 2048, 256, 8), C.make_cfg(256, 128, 16, 2),
+            C.make_cfg(32, 32, 1024, 16), C.make_cfg(6144, 2048, 256, 8, n_shared=0),
+            C.make_cfg(8192, 8192, 4, 2)]
+    counts = list(range(0, 70)) + [100, 511, 512, 513, 4096, 1 << 14, 1 << 17, 1 << 20]
+    for cfg in cfgs:
+        for flags in (0, C.COLI_FWD_DEBUG_TAPS):
+            sizes = [C.lib().coli_moe_workspace_bytes(cfg, n, flags) for n in counts]
+            assert all(b >= a for a, b in zip(sizes, sizes[1:])), (cfg.hidden, cfg.n_experts, flags)
+            for n, size in zip(counts, sizes):
+                L = C.coli_moe_workspace_layout(cfg, n, flags)
+                assert L.total == size

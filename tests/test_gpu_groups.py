@@ -63,6 +63,11 @@ def _check_choice(ref, cfg, x, wr, b, idx, w, tol=1e-6, ng=NG, tg=TG, must_diffe
         cand = np.sort(c[t][[e for e in range(cfg.n_experts) if e // gs in kept]])[::-1]
         near_kth = cand[cfg.top_k - 1] - cand[cfg.top_k] <= tol
         assert near_group or near_kth, (t, idx[t], ridx[t])
+        if not near_group:
+            # the same groups kept: the swapped experts sit at the K-th place
+            diff = set(int(e) for e in idx[t]) ^ set(int(e) for e in ridx[t])
+            assert all(abs(c[t][e] - cand[cfg.top_k - 1]) <= tol for e in diff), \
+                (t, idx[t], ridx[t])
 
 
 @pytest.mark.parametrize("n_tok", [1, 3, 300])
@@ -93,9 +98,13 @@ def test_grouped_layer_matches_oracle(C, ref, layer, n_tok, sample):
     tokens = list(range(n_tok)) if sample is None else \
         sorted(set(np.random.RandomState(7).choice(n_tok, sample, replace=False).tolist()) |
                {0, n_tok - 1})
-    OL = oracle_layer_for(ref, cfg, 0, x[tokens], forced_idx=taps["idx"][tokens], n_group=NG,
-                          topk_group=TG)
-    yo = OL.forward(x[tokens], forced_idx=taps["idx"][tokens], forced_w=taps["w"][tokens])
+    # the GPU's choice (checked above: the oracle's, or another correct one
+    # across a near-tie) with the oracle's own gate values for it
+    gidx = np.ascontiguousarray(taps["idx"][tokens])
+    OL = oracle_layer_for(ref, cfg, 0, x[tokens], forced_idx=gidx, n_group=NG, topk_group=TG)
+    w_for = ref.gates(x[tokens], wr.cpu().numpy(), b.cpu().numpy(), gidx, cfg.norm_topk, cfg.rho)
+    np.testing.assert_allclose(taps["w"][tokens], w_for, rtol=1e-6)
+    yo = OL.forward(x[tokens], forced_idx=gidx, forced_w=w_for)
     err = rel_l2(y[tokens], yo)
     _note("rel_l2", err)
     assert err <= TOL_REL_L2

@@ -83,3 +83,17 @@ def test_every_expert_chosen(C, ref, n_tok):
     cfg = dataclasses.replace(cs.CONFIGS[0], name="E4 K4", n_experts=4, top_k=4, n_tok=n_tok)
     _note(cfg.name, n_tok)
     _check(C, ref, cfg)
+
+
+# shapes the grouped MFMA kernels do not tile (I or H not a multiple of 64)
+# and the few-token kernels do not take (I % 64 != 0, or H > 6144): the GEMV
+# kernels with items of up to 4 tokens — one, two and four token slots per
+# item (NT = 1, 2, 4), experts split over several items, ragged last items
+@pytest.mark.parametrize("H,I,n_tok", [(8160, 256, 1), (256, 96, 1), (256, 96, 2),
+                                       (256, 96, 3), (256, 96, 5), (256, 96, 9),
+                                       (256, 96, 33)])
+def test_gemv_path(C, ref, H, I, n_tok):
+    cfg = dataclasses.replace(cs.CONFIGS[0], name=f"gemv H{H} I{I}", hidden=H, inter=I,
+                              n_experts=4, top_k=2, n_tok=n_tok)
+    _note(cfg.name, n_tok)
+    _check(C, ref, cfg)
