@@ -1,4 +1,8 @@
-"""Build libcoli_moe.so for gfx950 with hipcc (in-tree, next to this file)."""
+"""Build libcoli_moe.so for gfx950 with hipcc (in-tree, next to this file).
+
+The library is four translation units (the C ABI with the routing and small
+kernels, and one per kernel family), compiled in parallel and linked into one
+shared object."""
 from __future__ import annotations
 
 import os
@@ -7,11 +11,13 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "coli_moe.hip")
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = ["coli_moe.hip", "launch_decode.hip", "launch_prefill.hip", "launch_gemv.hip"]
 LIB = os.path.join(PKG, "libcoli_moe.so")
+OBJ_DIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fvisibility=hidden",
     # IEEE single-precision division: Q8_0 and int4 codes are decided by x/d
     "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -25,8 +31,20 @@ HIPCC_FLAGS = [
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(PKG, "csrc"), "-o", LIB + ".tmp", SRC]
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    procs, objs = [], []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc, *HIPCC_FLAGS, *inc, "-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        procs.append((src, subprocess.Popen(cmd)))
+        objs.append(obj)
+    failed = [src for src, p in procs if p.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)

@@ -1,5 +1,8 @@
 // Host side of the C ABI (include/coli_moe.h): argument checks, workspace
-// layout, kernel selection and launches. No allocation, no synchronisation.
+// layout, kernel selection and the launches of the routing and small kernels;
+// the few-token, grouped MFMA and GEMV kernel families are launched from
+// their own translation units (coli_launch.h). No allocation, no
+// synchronisation.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -10,10 +13,7 @@
 #include <cstring>
 
 #include "coli_moe.h"
-#include "coli_common.h"
-#include "k_decode.h"
-#include "k_gemv.h"
-#include "k_prefill.h"
+#include "coli_launch.h"
 #include "k_route.h"
 #include "k_small.h"
 
@@ -51,9 +51,6 @@ int check_cfg(const coli_moe_cfg* c) {
         return COLI_E_UNSUPPORTED;
     return COLI_OK;
 }
-
-// Width of the expert weight codes (0 reads as 4).
-inline int weight_bits(const coli_moe_cfg& c) { return c.weight_bits ? c.weight_bits : 4; }
 
 GroupSel group_sel(const coli_moe_cfg& c) {
     GroupSel g{1, c.n_experts, 1};
@@ -104,7 +101,9 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
     L->n_items = take(4);
     L->uinfo = take(4 * (1 + 4 * dec::kMaxEntries + 64));
     L->rpart = take(T > 8 ? (size_t)kMaxRouterSplit * T * E * 8 : 0);
-    L->sig = take(T <= dec::kMaxTok ? (size_t)2 * T * E * 8 : 0);  // s and c of the few-token path
+    // s and c of the few-token path; reserved for min(T, its token limit) at
+    // every T so that the total never shrinks as T grows
+    L->sig = take((size_t)2 * std::min<int64_t>(T, dec::kMaxTok) * E * 8);
 
     P.qh = take(NS * I);
     P.dh = take(NS * (I / 32) * 4);
@@ -121,81 +120,13 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
         while (stride < I && per_row * ((I + stride - 1) / stride) > kTapBudget) stride *= 2;
         P.tap_stride = stride;
         P.tap_rows = (I + stride - 1) / stride;
-        P.tap = take(NS * P.tap_rows * (H / 32) * 4);
+        // once rows are sampled the tap takes the whole budget, so that the
+        // total never shrinks as T grows (a caller sizes for its largest T)
+        const size_t tap_bytes = (size_t)NS * P.tap_rows * (H / 32) * 4;
+        P.tap = take(stride == 1 ? tap_bytes : std::max(tap_bytes, (size_t)kTapBudget * 4));
     }
 
     P.total = off;
-}
-
-// Optional per-launch timing (coli_moe_forward_profiled): mark() names the
-// next launch; launch j then carries events 2j (start) and 2j + 1 (stop),
-// which the packet processor stamps at the kernel's own begin and end.
-struct Marks {
-    hipStream_t s;
-    void* const* ev = nullptr;
-    const char** names = nullptr;
-    int n = 0, used = 0;  // n events, used launches so far
-    const char* pending = "";
-    void mark(const char* name) { pending = name; }
-    void take(hipEvent_t* e0, hipEvent_t* e1) {
-        *e0 = *e1 = nullptr;
-        if (ev && 2 * used + 1 < n) {
-            *e0 = (hipEvent_t)ev[2 * used];
-            *e1 = (hipEvent_t)ev[2 * used + 1];
-            if (names) names[used] = pending;
-        }
-        ++used;
-    }
-};
-
-// kernel<<<grid, block, shmem, s>>>(args...), with the launch's own start and
-// stop events when profiling.
-template <typename... P, typename... A>
-void launch(Marks& mk, void (*kernel)(P...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
-            A&&... args) {
-    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
-    hipEvent_t e0, e1;
-    mk.take(&e0, &e1);
-    if (e0)
-        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e0, e1, 0u, static_cast<P>(args)...);
-    else
-        kernel<<<grid, block, shmem, s>>>(static_cast<P>(args)...);
-}
-
-template <int NT>
-void launch_gateup_nt(int nbj, dim3 grid, hipStream_t s, const coli_moe_weights* w,
-                      int64_t blob_q, int64_t blob_s, const int8_t* qx, const float* dx,
-                      ItemArgs it, const int32_t* slot_tok, int8_t* qh, float* dh, int32_t* tap,
-                      int tap_rows, int tap_stride, Marks& mk) {
-    const int H = w->cfg.hidden, I = w->cfg.inter;
-#define COLI_GU(NBJ)                                                                          \
-    launch(mk, k_gateup_gemv<NT, NBJ>, grid, 256, 0, s, w->experts_q, w->experts_scale, blob_q, blob_s, \
-                                                qx, dx, it, slot_tok, H, I, qh, dh, tap,        \
-                                                tap_rows, tap_stride)
-    switch (nbj) {
-        case 1: COLI_GU(1); break;
-        case 2: COLI_GU(2); break;
-        case 3: COLI_GU(3); break;
-        default: COLI_GU(4); break;
-    }
-#undef COLI_GU
-}
-
-template <int NT>
-void launch_down_nt(int nbj, dim3 grid, hipStream_t s, const coli_moe_weights* w,
-                    int64_t blob_q, int64_t blob_s, const int8_t* qh, const float* dh,
-                    ItemArgs it, float* ye, Marks& mk) {
-    const int H = w->cfg.hidden, I = w->cfg.inter;
-#define COLI_DN(NBJ)                                                                          \
-    launch(mk, k_down_gemv<NT, NBJ>, grid, 256, 0, s, w->experts_q, w->experts_scale, blob_q, blob_s, \
-                                              qh, dh, it, H, I, ye)
-    switch (nbj) {
-        case 1: COLI_DN(1); break;
-        case 2: COLI_DN(2); break;
-        case 3: COLI_DN(3); break;
-        default: COLI_DN(4); break;
-    }
-#undef COLI_DN
 }
 
 // Router + top-k into ws (shared by coli_moe_route and coli_moe_forward).
@@ -248,80 +179,9 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
         launch(mk, k_topk<16>, gb, 256, tk_lds, s, logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
 }
 
-// Template selection for the fused few-token path.
-// Few-token path: three fused kernels (k_decode.h), every weight width.
-// Shapes it covers: hidden <= 6144, intermediate <= 2048, <= 256 routed
-// experts; up to four tokens (int2: two, where the grouped MFMA kernels
-// overtake it, their code expansion being paid once per token there).
-bool small_path_fits(const coli_moe_cfg& c, int64_t T) {
-    const int max_tok = weight_bits(c) == 2 ? 2 : 4;
-    return T <= max_tok && T * c.top_k <= dec::kMaxEntries && c.hidden <= 6144 &&
-           c.inter <= 2048 && c.inter % 64 == 0 && c.n_experts <= 256;
-}
-
-template <int NT, int NBJH, bool TAP, int BITS>
-void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
-    const int nrb = a.I / 32;
-    mk.mark("dec_router");
-    const int qb = (a.T * (a.H / 32) + 7) / 8;  // workgroups needed for Q8_0(x)
-    launch(mk, dec::k_dec_router<NT, BITS>, (a.E > qb) ? a.E : qb, 256, 0, s, a);
-    mk.mark("dec_gateup");
-    const int um = (a.T * a.K < a.E) ? a.T * a.K : a.E;
-    const int hbw = (NT > 1) ? 2 : 1;  // h-blocks per workgroup (k_dec_gateup)
-    launch(mk, dec::k_dec_gateup<NT, NBJH, TAP, BITS>, (a.S + um) * (nrb / hbw), 256, 0, s, a);
-    mk.mark("dec_down");
-    if (NT == 4)
-        launch(mk, dec::k_dec_down_x<NT, 1, BITS>, a.H / 8, 256, 0, s, a);
-    else
-        launch(mk, dec::k_dec_down<NT, 1, 2, 2, BITS>, a.H / 8, 256, 0, s, a);
-}
-
-template <int NT, int BITS>
-void launch_small_nt(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
-    if (a.H <= 2048) {
-        if (a.tap) launch_small_tap<NT, 1, true, BITS>(a, s, mk);
-        else launch_small_tap<NT, 1, false, BITS>(a, s, mk);
-    } else {
-        if (a.tap) launch_small_tap<NT, 3, true, BITS>(a, s, mk);
-        else launch_small_tap<NT, 3, false, BITS>(a, s, mk);
-    }
-}
-
-template <int BITS>
-void launch_small_bits(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
-    if (a.T <= 1) launch_small_nt<1, BITS>(a, s, mk);
-    else if (a.T <= 2) launch_small_nt<2, BITS>(a, s, mk);
-    else launch_small_nt<4, BITS>(a, s, mk);
-}
-
-void launch_small(const dec::DecArgs& a, int bits, hipStream_t s, Marks& mk) {
-    if (bits == 8) launch_small_bits<8>(a, s, mk);
-    else if (bits == 2) launch_small_bits<2>(a, s, mk);
-    else launch_small_bits<4>(a, s, mk);
-}
-
 int hip_status() {
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? COLI_OK : COLI_E_HIP;
-}
-
-// The grouped MFMA kernels of one weight width: gate/up (with debug taps or
-// not), the integer form of the h scales, down; KT tokens per item.
-template <int BITS, typename HS>
-void launch_pf(int kt, bool tap, dim3 g1, dim3 g2, const pf::PfArgs& pa, HS h_scales,
-               hipStream_t s, Marks& mk) {
-    mk.mark("pf_gateup");
-    if (kt == 64) {
-        if (tap) launch(mk, pf::k_pf_gateup<BITS, 64, true>, g1, 256, 0, s, pa);
-        else launch(mk, pf::k_pf_gateup<BITS, 64, false>, g1, 256, 0, s, pa);
-    } else {
-        if (tap) launch(mk, pf::k_pf_gateup<BITS, 32, true>, g1, 256, 0, s, pa);
-        else launch(mk, pf::k_pf_gateup<BITS, 32, false>, g1, 256, 0, s, pa);
-    }
-    h_scales();
-    mk.mark("pf_down");
-    if (kt == 64) launch(mk, pf::k_pf_down<BITS, 64>, g2, 256, 0, s, pa);
-    else launch(mk, pf::k_pf_down<BITS, 32>, g2, 256, 0, s, pa);
 }
 
 int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y, void* ws,
@@ -423,67 +283,23 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         pa.qh = qh; pa.dh = dh; pa.ye = ye; pa.tap = tap;
         pa.tap_rows = (int)L.pub.tap_rows;
         pa.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
-        int32_t* mxp = reinterpret_cast<int32_t*>(base + L.mx);
-        int32_t* exp_ = reinterpret_cast<int32_t*>(base + L.ex);
-        int32_t* mhp = reinterpret_cast<int32_t*>(base + L.mh);
-        int32_t* ehp = reinterpret_cast<int32_t*>(base + L.eh);
         // integer block scales (exact int64 sums in the K loop) from 16 tokens
         // on; below that their two launches cost more than they save, and
         // the kernels take the fp64 epilogue
-        const bool int_scales = T >= 16;
-        if (int_scales) {
-            pa.mx = mxp; pa.ex = exp_; pa.mh = mhp; pa.eh = ehp;
+        if (T >= 16) {
+            pa.mx = reinterpret_cast<int32_t*>(base + L.mx);
+            pa.ex = reinterpret_cast<int32_t*>(base + L.ex);
+            pa.mh = reinterpret_cast<int32_t*>(base + L.mh);
+            pa.eh = reinterpret_cast<int32_t*>(base + L.eh);
         }
-        const int64_t NS = L.pub.n_slots;
-        if (int_scales) {
-            mk.mark("scale_int_x");
-            launch(mk, pf::k_scale_int, (unsigned)((T + 3) / 4), 256, 0, s, dx, T, H / 32, mxp, exp_);
-        }
-        const dim3 g1((unsigned)((I / pf::kRows) * n_it));
-        const dim3 g2((unsigned)(((H + pf::kDnRows - 1) / pf::kDnRows) * n_it));
-        auto h_scales = [&] {
-            if (!int_scales) return;
-            mk.mark("scale_int_h");
-            launch(mk, pf::k_scale_int, (unsigned)((NS + 3) / 4), 256, 0, s, dh, NS, I / 32, mhp, ehp);
-        };
-        if (bits == 4) launch_pf<4>(kt, tap != nullptr, g1, g2, pa, h_scales, s, mk);
-        else if (bits == 8) launch_pf<8>(kt, tap != nullptr, g1, g2, pa, h_scales, s, mk);
-        else launch_pf<2>(kt, tap != nullptr, g1, g2, pa, h_scales, s, mk);
+        launch_pf_path(pa, bits, kt, T, L.pub.n_slots, n_it, s, mk);
     } else {
-    const int nt = (T >= L.ch) ? L.ch : (int)T;  // tokens per item at most
-    const int nbj_h = (H / 32 + 63) / 64;
-    const int nbj_i = (I / 32 + 63) / 64;
-    mk.mark("gateup");
-    {
-        dim3 grid((unsigned)((I / 32) * L.max_items));
-        const int tr = (int)L.pub.tap_rows, ts = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);
-        if (nt <= 1)
-            launch_gateup_nt<1>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
-                                tap, tr, ts, mk);
-        else if (nt <= 2)
-            launch_gateup_nt<2>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
-                                tap, tr, ts, mk);
-        else
-            launch_gateup_nt<4>(nbj_h, grid, s, w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh,
-                                tap, tr, ts, mk);
-    }
-    mk.mark("down");
-    {
-        dim3 grid((unsigned)((H / 32) * L.max_items));
-        if (nt <= 1)
-            launch_down_nt<1>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye, mk);
-        else if (nt <= 2)
-            launch_down_nt<2>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye, mk);
-        else
-            launch_down_nt<4>(nbj_i, grid, s, w, blob_q, blob_s, qh, dh, it, ye, mk);
-    }
+        launch_gemv_path(w, blob_q, blob_s, qx, dx, it, slot_tok, qh, dh, ye, tap,
+                         (int)L.pub.tap_rows, (int)(L.pub.tap_stride ? L.pub.tap_stride : 1), T,
+                         L.max_items, s, mk);
     }
     mk.mark("combine");
-    {
-        dim3 grid((unsigned)(((H + 1023) / 1024) * T));
-        launch(mk, k_combine, grid, 256, 0, s, ye, slot_of, wts, K, S, H, y,
-                                       (flags & COLI_FWD_ACCUM) ? 1 : 0);
-    }
+    launch_combine(ye, slot_of, wts, K, S, H, y, T, (flags & COLI_FWD_ACCUM) ? 1 : 0, s, mk);
     return hip_status();
 }
 

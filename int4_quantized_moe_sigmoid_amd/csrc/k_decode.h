@@ -17,11 +17,10 @@
 #pragma once
 
 #include "coli_common.h"
+#include "coli_args.h"
 
 namespace dec {
 
-constexpr int kMaxTok = 4;
-constexpr int kMaxEntries = 64;  // T * K
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
@@ -498,38 +497,6 @@ __device__ __forceinline__ void route_small(const double* sig, const double* cva
     __syncthreads();
 }
 
-struct DecArgs {
-    const float* x;
-    const float* wr;
-    const float* bias;
-    const uint8_t* eq;
-    const float* es;
-    int64_t blob_q, blob_s;
-    int T, H, I, E, K, S, norm;
-    double rho;
-    GroupSel gsel;  // group-limited selection (ng <= 1: none)
-    // workspace
-    double* logits;
-    double* sig;   // [T, E] sigmoid of the logits (written by the router kernel)
-    double* cval;  // [T, E] s + bias, the selection scores
-    int8_t* qx;
-    float* dx;
-    int32_t* idx;
-    float* wts;
-    int32_t* counts;
-    int32_t* offs;
-    int32_t* slot_of;
-    int32_t* slot_tok;
-    int32_t* uinfo;   // [0] = n_uniq, then (e, s0, n) triples, then slot weights
-    int8_t* qh;
-    float* dh;
-    int32_t* tap;
-    int tap_rows, tap_stride;
-    float* y;
-    int accum;
-};
-
-constexpr int kUinfoW = 1 + 3 * kMaxEntries;  // offset of the slot weights in uinfo
 
 
 // Gate/up GEMV for one expert, NT token slots and 32 intermediate rows

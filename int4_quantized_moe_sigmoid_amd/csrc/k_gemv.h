@@ -11,13 +11,8 @@
 #pragma once
 
 #include "coli_common.h"
+#include "coli_args.h"
 
-struct ItemArgs {
-    int32_t* item_e;
-    int32_t* item_s0;
-    int32_t* item_n;
-    int32_t* n_items;
-};
 
 // Gate/up for one item (an expert and up to NT of its tokens) and one block
 // of 32 intermediate rows, then SwiGLU and Q8_0 of the 32 h values per token.

@@ -42,14 +42,13 @@
 #include <type_traits>
 
 #include "coli_common.h"
+#include "coli_args.h"
 
 namespace pf {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kRows = 64;     // gate/up: h rows per workgroup (16 per wave)
-constexpr int kDnRows = 128;  // down: output rows per workgroup (32 per wave)
 constexpr int kSlots = 3;     // LDS ring: one stage computed, two loading
 
 // Stage geometry of one weight width (2, 4 or 8 bits) and item size KT (32
@@ -88,28 +87,6 @@ struct Geo {
 
 __device__ __forceinline__ int wkey(int r, int ks, int npc) { return (r / ks) % npc; }
 
-struct PfArgs {
-    const uint8_t* eq;
-    const float* es;
-    int64_t blob_q, blob_s;
-    int H, I;
-    const int8_t* qx;      // [T, H] Q8_0 codes of x (in the weight width's element order)
-    const float* dx;       // [T, H/32]
-    const int32_t* item_e;
-    const int32_t* item_s0;
-    const int32_t* item_n;
-    const int32_t* n_items;
-    const int32_t* slot_tok;
-    int8_t* qh;            // [slots, I]
-    float* dh;             // [slots, I/32]
-    float* ye;             // [slots, H]
-    int32_t* tap;
-    int tap_rows, tap_stride;
-    const int32_t* mx;     // integer form of dx (k_scale_int) and its exponents
-    const int32_t* ex;
-    const int32_t* mh;     // integer form of dh and its exponents
-    const int32_t* eh;
-};
 
 // Exponent marking a row whose block scales span more than 2^7 (no 31-bit
 // integer form): its items take the fp64 epilogue.
