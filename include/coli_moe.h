@@ -237,6 +237,26 @@ COLI_API int coli_moe_forward_profiled(const coli_moe_weights* w, const float* x
                                        uint32_t flags, void* stream, void* const* events,
                                        int n_events, int* n_used, const char** names);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * coli_moe_forward without a workspace argument. Its intermediates live in a
+ * fixed scratch array of COLI_STATIC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; the call itself allocates
+ * nothing. Results are identical to coli_moe_forward (same kernels).
+ *   w, x, n_tok, y, flags, stream: as coli_moe_forward.
+ * Errors: as coli_moe_forward, and COLI_E_WORKSPACE when the intermediates of
+ * n_tok tokens with these flags need more than the scratch array holds (for
+ * the GLM-5.2 layer shape about 120 tokens without COLI_FWD_DEBUG_TAPS;
+ * coli_moe_workspace_bytes gives the need); COLI_E_HIP when the array's
+ * address cannot be obtained.
+ * All calls on one GPU share its array, and each call overwrites it: calls
+ * that overlap in time on one GPU (different streams, different threads
+ * without ordering) race and give wrong results; order them, e.g. on one
+ * stream. */
+#define COLI_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+COLI_API int coli_moe_forward_static(const coli_moe_weights* w, const float* x, int64_t n_tok,
+                                     float* y, uint32_t flags, void* stream);
+
 /* RMSNorm with unit gain (the pre-norm between stacked layers):
  *   out = fp32(x / sqrt(mean(x^2) + eps)), computed in fp64.
  *   x [n_tok, dim] fp32 (in), out [n_tok, dim] fp32 (out, may alias x). */

@@ -28,7 +28,8 @@ COLI_FWD_DEBUG_TAPS = 2
 EXPORTS = ("coli_strerror", "coli_pack_weights", "coli_pack_int4", "coli_pack_fp8_int4",
            "coli_quant_q8", "coli_moe_workspace_bytes",
            "coli_moe_workspace_layout", "coli_moe_route", "coli_moe_forward",
-           "coli_moe_forward_profiled", "coli_rmsnorm", "coli_stream_read")
+           "coli_moe_forward_profiled", "coli_moe_forward_static", "coli_rmsnorm",
+           "coli_stream_read")
 
 
 class ColiError(RuntimeError):
@@ -85,6 +86,7 @@ def _load():
                                             sz, u32, vp, ctypes.POINTER(vp), i32,
                                             ctypes.POINTER(i32),
                                             ctypes.POINTER(ctypes.c_char_p)]
+    L.coli_moe_forward_static.argtypes = [ctypes.POINTER(coli_moe_weights), vp, i64, vp, u32, vp]
     L.coli_rmsnorm.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp]
     L.coli_stream_read.argtypes = [vp, i64, vp, vp]
     for name in EXPORTS:
@@ -254,6 +256,16 @@ def coli_moe_forward_profiled(weights: LayerWeights, x: torch.Tensor, y: torch.T
                                           _stream(stream), arr, n, ctypes.byref(used), names),
            "coli_moe_forward_profiled")
     return [names[i].decode() for i in range(min(used.value, n // 2))]
+
+
+def coli_moe_forward_static(weights: LayerWeights, x: torch.Tensor, y: torch.Tensor,
+                            flags: int = 0, stream=None):
+    """coli_moe_forward with the library's fixed per-GPU scratch array instead
+    of a workspace (no allocation; calls on one GPU must not overlap)."""
+    _check(_lib.coli_moe_forward_static(ctypes.byref(weights.struct),
+                                        _dev(x, "x", torch.float32), x.shape[0],
+                                        _dev(y, "y", torch.float32), flags, _stream(stream)),
+           "coli_moe_forward_static")
 
 
 def coli_rmsnorm(x: torch.Tensor, out: torch.Tensor, eps: float = 1e-5, stream=None):

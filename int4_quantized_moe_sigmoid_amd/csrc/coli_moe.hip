@@ -7,6 +7,7 @@
 #include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -426,6 +427,53 @@ COLI_API int coli_moe_forward(const coli_moe_weights* w, const float* x, int64_t
                               void* ws, size_t ws_bytes, uint32_t flags, void* stream) {
     Marks mk{(hipStream_t)stream};
     return forward_impl(w, x, n_tok, y, ws, ws_bytes, flags, (hipStream_t)stream, mk);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of coli_moe_forward_static: one array per GPU the library runs
+// on, alive until the process ends. In host code `scratch` is only a
+// stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kStaticScratchBytes = COLI_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (nullptr on failure).
+void* static_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);  // same value from any racing thread
+    return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+COLI_API int coli_moe_forward_static(const coli_moe_weights* w, const float* x, int64_t n_tok,
+                                     float* y, uint32_t flags, void* stream) {
+    Marks mk{(hipStream_t)stream};
+    if (!w || n_tok < 0) return COLI_E_INVAL;
+    const int rc = check_cfg(&w->cfg);
+    if (rc) return rc;
+    if (n_tok == 0)  // no-op after the argument checks; touches no scratch
+        return forward_impl(w, x, 0, y, nullptr, 0, flags, (hipStream_t)stream, mk);
+    if (n_tok > (int64_t)1 << 20) return COLI_E_UNSUPPORTED;
+    Layout L;
+    make_layout(w->cfg, n_tok, flags, &L);
+    if (L.pub.total > kStaticScratchBytes) return COLI_E_WORKSPACE;
+    void* ws = static_scratch();
+    if (!ws) return COLI_E_HIP;
+    return forward_impl(w, x, n_tok, y, ws, kStaticScratchBytes, flags, (hipStream_t)stream, mk);
 }
 
 COLI_API int coli_moe_forward_profiled(const coli_moe_weights* w, const float* x, int64_t n_tok,
