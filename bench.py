@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of one sigmoid-routed int4 x Q8_0 MoE layer on one MI355X.
 
-Default workload: GLM-5.2-shaped decode at batch 1 (1 token per step, hidden
-6144, 256 routed experts, top-8, one shared expert, intermediate 2048). A
-step is one full coli_moe_forward: Q8_0(x), router + top-k, bucketing,
-gate/up + SwiGLU + requant, down, weighted combine. Every step uses a new
-seeded token and the next of R layer replicas (distinct seeded weights), so
-the 256 MB Infinity Cache never serves a previous step's weights.
+Default run: the five synthetic workloads in one JSON line. The headline
+(`value`) is the GLM-5.2-shaped decode at batch 1 (1 token per step, hidden
+6144, 256 routed experts, top-8, one shared expert, intermediate 2048); a step
+is one full coli_moe_forward: Q8_0(x), router + top-k, bucketing, gate/up +
+SwiGLU + requant, down, weighted combine. Every step uses a new seeded token
+and the next of R layer replicas (distinct seeded weights), so the 256 MB
+Infinity Cache never serves a previous step's weights. `configs` holds the
+same measurement for the tiny layer, MTP verify (3 correlated tokens),
+prefill (512 tokens, zipf-skewed routing) and the 8-layer pre-norm residual
+stack at 4096 tokens, each with its roofline and an oracle CPU baseline.
 
-Prints one JSON line (see the fields below). Options: --config picks another
-workload (0 tiny, 1 decode, 2 MTP verify T=3, 3 prefill T=512, 4 the 8-layer
-pre-norm residual stack at T=4096); --gpus must be 1 (one GPU).
+Options: --config N measures one workload alone (0 tiny, 1 decode, 2 MTP
+verify T=3, 3 prefill T=512, 4 the stack); --gpus must be 1 (one GPU).
 """
 from __future__ import annotations
 
@@ -51,10 +54,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--config", type=int, default=None,
+                    help="measure one workload alone (default: all five, decode as the headline)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="time budget of the oracle CPU-baseline sample (0 = skip)")
+                    help="time budget of the headline's oracle CPU-baseline sample (the "
+                         "other workloads take about half; 0 = skip every baseline)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel event pass")
     ap.add_argument("--sweep", type=str, default="",
                     help="comma-separated token counts: time the layer of --config at each "
@@ -96,28 +101,110 @@ def main():
                                    "across GPUs (use --gpus 1)", "n_gpus": args.gpus}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import coli_synth as cs
     import int4_quantized_moe_sigmoid_amd as C
 
     torch.cuda.set_device(0)
-    cfg = cs.CONFIGS[args.config]
     if args.op == "pack_fp8":
-        run_pack_fp8(args, cfg)
-        return
-    if cfg.n_layers > 1:
-        run_stack(args, cfg)
+        run_pack_fp8(args, cs.CONFIGS[1 if args.config is None else args.config])
         return
     if args.sweep:
-        run_sweep(args, cfg, [int(v) for v in args.sweep.split(",") if v])
+        run_sweep(args, cs.CONFIGS[2 if args.config is None else args.config],
+                  [int(v) for v in args.sweep.split(",") if v])
         return
+    # the measured streaming-read ceiling first: it also brings the GPU out of idle
+    ceiling = read_ceiling_gbps(C)
+    if args.config is not None:
+        cfg = cs.CONFIGS[args.config]
+        res = measure_stack(args, cfg) if cfg.n_layers > 1 else measure_layer(args, cfg)
+        print(json.dumps(headline(res, ceiling)), flush=True)
+        return
+    head = measure_layer(args, cs.CONFIGS[1])
+    out = headline(head, ceiling)
+    sub = {}
+    half = argparse.Namespace(**{**vars(args), "cpu_seconds": args.cpu_seconds / 2})
+    for cid in (0, 2, 3, 4):
+        cfg = cs.CONFIGS[cid]
+        res = measure_stack(half, cfg) if cfg.n_layers > 1 else measure_layer(half, cfg)
+        sub[f"C{cid}"] = summary(res, ceiling)
+        torch.cuda.empty_cache()
+    out["configs"] = {"C1": summary(head, ceiling), **sub}
+    print(json.dumps(out), flush=True)
+
+
+def headline(res, ceiling):
+    """The JSON line of one workload (the driver's fields first)."""
+    out = {
+        "metric": "MoE-layer tokens/s; decode int4 expert-weight GB/s as % of HBM peak",
+        "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": res["steps"],
+        "warmup": res["warmup"], "ms_per_step": res["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": res["dtype"],
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights packed by "
+                "coli_pack_weights)",
+        "config": res["config"],
+        "read_ceiling_gbps": ceiling,
+    }
+    for k, v in res.items():
+        if k not in out and k not in ("tokens_per_s", "steps", "warmup"):
+            out[k] = v
+    if "expert_weight_gbps" in res:
+        out["expert_weight_frac_read_ceiling"] = round(res["expert_weight_gbps"] / ceiling, 4)
+    if out.get("roofline") and out["roofline"]["unit"] == "GB/s":
+        out["roofline"]["frac_of_read_ceiling"] = round(out["roofline"]["achieved"] / ceiling, 4)
+    return out
+
+
+def summary(res, ceiling):
+    """Per-workload entry of the default line."""
+    keep = ("config", "ms_per_step", "ms_per_layer", "tokens_per_s", "steps", "warmup",
+            "expert_weight_gbps", "expert_weight_frac_hbm", "unique_experts_per_step",
+            "unique_experts_per_layer", "algorithmic_bytes_per_step", "kernel_avg_us",
+            "kernel_avg_us_per_layer", "roofline", "cpu_baseline")
+    out = {k: res[k] for k in keep if k in res}
+    if out.get("roofline") and out["roofline"]["unit"] == "GB/s":
+        out["roofline"]["frac_of_read_ceiling"] = round(out["roofline"]["achieved"] / ceiling, 4)
+    return out
+
+
+def kernel_events(C, run_profiled, n_prof):
+    """Mean duration (ms) of each launch of a forward, from the launches' own
+    start and stop HIP events (coli_moe_forward_profiled; the events are
+    stamped by the packet processor on the launch stream). run_profiled(i,
+    handles) enqueues forward i and returns its launch names."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(40)]  # 2 per launch
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    hs = [e.cuda_event for e in evs]
+    sums = {}
+    for i in range(n_prof):
+        names = run_profiled(i, hs)
+        torch.cuda.synchronize()
+        for j, nm in enumerate(names):
+            sums[nm] = sums.get(nm, 0.0) + evs[2 * j].elapsed_time(evs[2 * j + 1])
+    return {k: v / n_prof for k, v in sums.items()}
+
+
+def measure_layer(args, cfg):
+    """One MoE layer per step over a new seeded batch of cfg.n_tok tokens, the
+    layer taken round robin from R independently seeded replicas."""
+    import numpy as np
+    import torch
+
+    import coli_synth as cs
+    import int4_quantized_moe_sigmoid_amd as C
+
     T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
     ng, tg = (int(v) for v in args.groups.split(",")) if args.groups else (1, 1)
     bits = args.bits
     lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, ng, tg, bits)
-    R = max(1, args.replicas)
+    # every step reads a different set of experts; a layer whose experts all fit
+    # the 256 MB last-level cache or that reads them all every step (prefill)
+    # needs no replicas
+    R = max(1, args.replicas) if T < 64 and E * cfg.expert_bytes() > (1 << 28) else 1
     n_steps, n_warm = args.steps, args.warmup
     n_inputs = n_steps + n_warm
 
@@ -127,12 +214,12 @@ def main():
     for r in range(R):
         wr, b, q, s = cs.build_layer(cfg, r, "cuda", pack, bits=bits)
         layers.append(C.LayerWeights(lc, wr, b, q, s))
-        print(f"[bench] replica {r} packed ({(q.numel() + 4 * s.numel()) / 1e9:.2f} GB)",
+        print(f"[bench] {cfg.name}: replica {r} packed ({(q.numel() + 4 * s.numel()) / 1e9:.2f} GB)",
               file=sys.stderr, flush=True)
     # distinct seeded inputs for every step, RMS-normalised on the GPU when the
     # workload's input is normalised
     xs = []
-    for i in range(n_inputs):
+    for i in range(n_inputs if T * H * n_inputs < (1 << 28) else 2 * R):
         raw = cs.activations(cfg, i % R, "cuda", n_tok=T, first_tok=(i // R) * T)
         if cfg.rmsnorm_input:
             xn = torch.empty_like(raw)
@@ -145,7 +232,7 @@ def main():
     setup_s = time.time() - t_setup
 
     def step(i):
-        C.coli_moe_forward(layers[i % R], xs[i], ys[i & 1], ws)
+        C.coli_moe_forward(layers[i % R], xs[i % len(xs)], ys[i & 1], ws)
 
     for i in range(n_warm):
         step(n_steps + i)
@@ -156,80 +243,175 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / n_steps
-    tok_s = T * n_steps / elapsed
+
+    # ---- per-kernel durations with HIP events on the launch stream -----------
+    lay = C.coli_moe_workspace_layout(lc, T, 0)
+    counts_view = ws[lay.counts:lay.counts + 4 * (E + S)].view(torch.int32)
+    kern, unique_counts = {}, []
+    if not args.no_profile:
+        def prof(i, hs):
+            names = C.coli_moe_forward_profiled(layers[i % R], xs[i % len(xs)], ys[i & 1], ws,
+                                                hs)
+            torch.cuda.synchronize()
+            unique_counts.append(int((counts_view[:E] > 0).sum().item()) + S)
+            return names
+        kern = kernel_events(C, prof, max(1, min(n_steps, 200)))
+    uniq_avg = float(np.mean(unique_counts)) if unique_counts else float(min(E, T * K) + S)
 
     # bytes that must cross HBM per step: unique experts' packed weights + scales,
     # the router weight, activations in and out
-    lay = C.coli_moe_workspace_layout(lc, T, 0)
     eb = 3 * I * H * bits // 8 + 4 * (2 * I + H)
-
-    # ---- per-kernel durations with HIP events on the same stream -------------
-    kern = {}
-    unique_counts = []
-    if not args.no_profile:
-        names = None
-        nev = 32  # start and stop of each launch
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)]
-        for e in evs:
-            e.record()
-        torch.cuda.synchronize()
-        handles = [e.cuda_event for e in evs]
-        sums = {}
-        n_prof = n_steps
-        counts_view = ws[lay.counts:lay.counts + 4 * (E + S)].view(torch.int32)
-        for i in range(n_prof):
-            names = C.coli_moe_forward_profiled(layers[i % R], xs[i], ys[i & 1], ws, handles)
-            torch.cuda.synchronize()
-            for j in range(len(names)):
-                sums[names[j]] = sums.get(names[j], 0.0) + \
-                    evs[2 * j].elapsed_time(evs[2 * j + 1])
-            unique_counts.append(int((counts_view[:E] > 0).sum().item()) + S)
-        kern = {k: v / n_prof for k, v in sums.items()}
-    uniq_avg = float(np.mean(unique_counts)) if unique_counts else float(min(E, T * K) + S)
-
     # algorithmic HBM bytes of the gate/up launch: the packed gate and up rows and
-    # their scales of every expert in use, Q8_0(x) in, Q8_0(h) out (+ the fp64
-    # router logits the decode kernel reads to redo the top-k)
+    # their scales of every expert in use, Q8_0(x) in, Q8_0(h) out
     gate_up_bytes = uniq_avg * (2 * I * H * bits // 8 + 4 * 2 * I) + T * (H + H // 8) + \
         T * (K + S) * (I + I // 8)
     step_bytes = uniq_avg * eb + 4 * E * H + 4 * E + 8 * T * H
     weight_gbps = uniq_avg * eb / (ms_per_step * 1e-3) / 1e9
-
-    roofline = gateup_roofline(kern, cfg, gate_up_bytes, T, bits)
-    ceiling = read_ceiling_gbps(C)
-    if roofline:
-        roofline["frac_of_read_ceiling"] = round(roofline["achieved"] / ceiling, 4)
-
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(cfg, args.cpu_seconds)
-
-    out = {
-        "metric": "MoE-layer tokens/s; decode int4 expert-weight GB/s as % of HBM peak",
-        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": n_steps,
-        "warmup": n_warm, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": f"int{bits}xint8 (int32 block dots, f64 scales)",
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights packed by "
-                "coli_pack_weights)",
-        "config": {"workload": cfg.name + (f" groups {ng}/{tg}" if ng > 1 else "") +
-                   (f" int{bits} weights" if bits != 4 else ""),
-                   "tokens_per_step": T, "hidden": H, "inter": I,
+    cpu = cpu_baseline(cfg, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    wl = cfg.name + (f" groups {ng}/{tg}" if ng > 1 else "") + \
+        (f" int{bits} weights" if bits != 4 else "")
+    res = {
+        "config": {"workload": wl, "tokens_per_step": T, "hidden": H, "inter": I,
                    "n_experts": E, "top_k": K, "n_shared": S, "weight_replicas": R,
                    "n_group": ng, "topk_group": tg, "weight_bits": bits,
                    "parallelism": "none (1 GPU)"},
+        "dtype": f"int{bits}xint8 (int32 block dots, f64 scales)",
+        "steps": n_steps, "warmup": n_warm,
+        "ms_per_step": round(ms_per_step, 5),
+        "tokens_per_s": round(T * n_steps / elapsed, 2),
         "expert_weight_gbps": round(weight_gbps, 1),
         "expert_weight_frac_hbm": round(weight_gbps / HBM_PEAK_GBPS, 4),
-        "read_ceiling_gbps": ceiling,
-        "expert_weight_frac_read_ceiling": round(weight_gbps / ceiling, 4),
         "unique_experts_per_step": round(uniq_avg, 2),
         "algorithmic_bytes_per_step": int(step_bytes),
         "kernel_avg_us": {k: round(v * 1e3, 2) for k, v in kern.items()},
-        "roofline": roofline,
+        "roofline": gateup_roofline(kern, cfg, wl, gate_up_bytes, T, mfma_bound=False),
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
-    print(json.dumps(out), flush=True)
+    del layers, xs, ws
+    return res
+
+
+def measure_stack(args, cfg):
+    """The stacked workload: x <- x + MoE_l(RMSNorm(x)) for every layer l, one
+    step = all layers over one batch of T tokens."""
+    import numpy as np
+    import torch
+
+    import coli_synth as cs
+    import int4_quantized_moe_sigmoid_amd as C
+
+    T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
+    NL = cfg.n_layers
+    bits = args.bits
+    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, weight_bits=bits)
+    n_steps, n_warm = args.steps, args.warmup
+    t_setup = time.time()
+    layers = []
+    for l in range(NL):
+        wr, b, q, s = cs.build_layer(cfg, l, "cuda",
+                                     lambda w, qv, sv: C.coli_pack_weights(w, bits, qv, sv),
+                                     bits=bits)
+        layers.append(C.LayerWeights(lc, wr, b, q, s))
+        print(f"[bench] {cfg.name}: layer {l} packed", file=sys.stderr, flush=True)
+    # distinct seeded batches (up to 32, then reused: each step adds its layers'
+    # outputs into its batch in place, as the residual stream does)
+    xs = [cs.activations(cfg, 0, "cuda", n_tok=T, first_tok=i * T)
+          for i in range(min(32, n_steps + n_warm))]
+    xn = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(C.coli_moe_workspace_bytes(lc, T), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    def step(i):
+        x = xs[i % len(xs)]
+        for l in range(NL):
+            C.coli_rmsnorm(x, xn, 1e-5)
+            C.coli_moe_forward(layers[l], xn, x, ws, C.COLI_FWD_ACCUM)
+
+    for i in range(n_warm):
+        step(n_steps + i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / n_steps
+
+    kern = {}
+    uniq = []
+    x = cs.activations(cfg, 0, "cuda", n_tok=T, first_tok=10 ** 6)
+    if not args.no_profile:
+        lay = C.coli_moe_workspace_layout(lc, T, 0)
+        counts_view = ws[lay.counts:lay.counts + 4 * (E + S)].view(torch.int32)
+
+        def prof(l, hs):
+            C.coli_rmsnorm(x, xn, 1e-5)
+            names = C.coli_moe_forward_profiled(layers[l], xn, x, ws, hs, C.COLI_FWD_ACCUM)
+            torch.cuda.synchronize()
+            uniq.append(int((counts_view[:E] > 0).sum().item()) + S)
+            return names
+        kern = kernel_events(C, prof, NL)
+    uniq_avg = float(np.mean(uniq)) if uniq else float(E + S)
+    gate_up_bytes = uniq_avg * (2 * I * H * bits // 8 + 4 * 2 * I) + T * (H + H // 8) + \
+        T * (K + S) * (I + I // 8)
+    cpu = cpu_baseline_stack(cfg, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    wl = cfg.name + (f" int{bits} weights" if bits != 4 else "")
+    res = {
+        "metric_note": "MoE-stack tokens/s (8 pre-norm residual MoE layers per step)",
+        "config": {"workload": wl, "tokens_per_step": T, "layers": NL, "hidden": H,
+                   "inter": I, "n_experts": E, "top_k": K, "n_shared": S, "weight_bits": bits,
+                   "parallelism": "none (1 GPU)"},
+        "dtype": f"int{bits}xint8 (int32 block dots, f64 scales)",
+        "steps": n_steps, "warmup": n_warm,
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_layer": round(ms_per_step / NL, 4),
+        "tokens_per_s": round(T * n_steps / elapsed, 2),
+        "unique_experts_per_layer": round(uniq_avg, 2),
+        "kernel_avg_us_per_layer": {k: round(v * 1e3, 2) for k, v in kern.items()},
+        "roofline": gateup_roofline(kern, cfg, wl, gate_up_bytes, T, mfma_bound=True),
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    del layers, ws
+    return res
+
+
+def gateup_roofline(kern, cfg, wl, gate_up_bytes, T, mfma_bound):
+    """Roofline of the gate/up kernel (the dominant launch of every path):
+    algorithmic HBM bytes per launch / its mean event-timed duration against
+    8 TB/s, with the stored counter traffic of that kernel and workload where
+    there is one; for the grouped MFMA kernel also the useful int8 ops (2 per
+    MAC over T*(K+S) (token, expert) pairs x 2I rows x H) against 5.0 POP/s.
+    mfma_bound: the stacked workload sits at the ridge and is reported against
+    the int8 MFMA peak."""
+    gk = next((k for k in ("dec_gateup", "pf_gateup", "gateup") if k in kern), None)
+    if gk is None:
+        return None
+    if gk == "dec_gateup":
+        # the fp64 sigmoid and selection scores (two per expert) the kernel reads
+        gate_up_bytes += 16 * T * cfg.n_experts
+    ms = kern[gk]
+    ach = gate_up_bytes / (ms * 1e-3) / 1e9
+    traffic = TRAFFIC.get((gk, wl))
+    out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+           "traffic": (int(traffic) if traffic is not None else None),
+           "kernel": gk, "bytes_per_launch": int(gate_up_bytes),
+           "avg_launch_us": round(ms * 1e3, 2)}
+    if gk == "pf_gateup":
+        ops = 2.0 * T * (cfg.top_k + cfg.n_shared) * 2 * cfg.inter * cfg.hidden
+        tops = ops / (ms * 1e-3) / 1e12
+        out["int8_tops"] = round(tops, 1)
+        out["int8_frac_of_5000_tops"] = round(tops / 5000.0, 4)
+        if mfma_bound:
+            out = {"bound": "mfma", "achieved": round(tops, 1), "peak": 5000.0,
+                   "unit": "TOP/s (int8)", "frac": round(tops / 5000.0, 4),
+                   "traffic": out["traffic"], "kernel": gk, "int8_ops_per_launch": ops,
+                   "hbm_gbps": round(ach, 1), "hbm_frac": round(ach / HBM_PEAK_GBPS, 4),
+                   "bytes_per_launch": int(gate_up_bytes), "avg_launch_us": round(ms * 1e3, 2)}
+    return out
 
 
 def run_pack_fp8(args, cfg):
@@ -339,32 +521,6 @@ def read_ceiling_gbps(C, gib=4, reps=10):
     return round(gbps, 1)
 
 
-def gateup_roofline(kern, cfg, gate_up_bytes, T, bits=4):
-    """Roofline of the gate/up kernel (the dominant launch of every path):
-    algorithmic HBM bytes per launch / its mean event-timed duration, with the
-    stored counter traffic of that kernel and workload where there is one."""
-    gk = next((k for k in ("dec_gateup", "pf_gateup", "gateup") if k in kern), None)
-    if gk is None:
-        return None
-    if gk == "dec_gateup":
-        gate_up_bytes += 8 * T * cfg.n_experts  # the fp64 logits the kernel reads
-    ms = kern[gk]
-    wl = cfg.name + (f" int{bits} weights" if bits != 4 else "")
-    ach = gate_up_bytes / (ms * 1e-3) / 1e9
-    out = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-           "traffic": (int(TRAFFIC[(gk, wl)]) if (gk, wl) in TRAFFIC else None),
-           "kernel": gk, "bytes_per_launch": int(gate_up_bytes),
-           "avg_launch_us": round(ms * 1e3, 2)}
-    if gk == "pf_gateup":
-        # useful int8 ops of the launch: 2 per MAC over T*(K+S) (token, expert)
-        # pairs x 2I rows x H
-        ops = 2.0 * T * (cfg.top_k + cfg.n_shared) * 2 * cfg.inter * cfg.hidden
-        out["int8_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
-        out["int8_frac_of_5000_tops"] = round(ops / (ms * 1e-3) / 5.0e15, 4)
-    return out
-
-
 def run_sweep(args, cfg, counts):
     """Layer time against the number of tokens per call, on the weights and
     input recipe of `cfg` (the few-token kernels serve T <= 4, with int2
@@ -418,134 +574,91 @@ def run_sweep(args, cfg, counts):
               flush=True)
 
 
-def run_stack(args, cfg):
-    """The stacked workload: x <- x + MoE_l(RMSNorm(x)) for every layer l, one
-    step = all layers over one batch of T tokens."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                        None)
+    except OSError:
+        return None
+
+
+def _oracle_layer(cfg, layer, x, OL=None):
+    """Oracle layer (from coli_synth's fp32 draws, packed by the oracle) holding
+    the experts tokens x select plus the shared expert."""
     import numpy as np
-    import torch
 
     import coli_synth as cs
-    import int4_quantized_moe_sigmoid_amd as C
-
-    T, H, I, E, K, S = cfg.n_tok, cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared
-    NL = cfg.n_layers
-    bits = args.bits
-    lc = C.make_cfg(H, I, E, K, S, cfg.norm_topk, cfg.rho, weight_bits=bits)
-    n_steps, n_warm = args.steps, args.warmup
-    t_setup = time.time()
-    layers = []
-    for l in range(NL):
-        wr, b, q, s = cs.build_layer(cfg, l, "cuda",
-                                     lambda w, qv, sv: C.coli_pack_weights(w, bits, qv, sv),
-                                     bits=bits)
-        layers.append(C.LayerWeights(lc, wr, b, q, s))
-        print(f"[bench] layer {l} packed", file=sys.stderr, flush=True)
-    xs = [cs.activations(cfg, 0, "cuda", n_tok=T, first_tok=i * T) for i in range(n_steps + n_warm)]
-    xn = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(C.coli_moe_workspace_bytes(lc, T), dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    setup_s = time.time() - t_setup
-
-    def step(x):
-        for l in range(NL):
-            C.coli_rmsnorm(x, xn, 1e-5)
-            C.coli_moe_forward(layers[l], xn, x, ws, C.COLI_FWD_ACCUM)
-
-    for i in range(n_warm):
-        step(xs[n_steps + i])
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(n_steps):
-        step(xs[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / n_steps
-
-    kern = {}
-    uniq = []
-    if not args.no_profile:
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(32)]  # 2 per launch
-        for e in evs:
-            e.record()
-        torch.cuda.synchronize()
-        hs = [e.cuda_event for e in evs]
-        lay = C.coli_moe_workspace_layout(lc, T, 0)
-        counts_view = ws[lay.counts:lay.counts + 4 * (E + S)].view(torch.int32)
-        x = cs.activations(cfg, 0, "cuda", n_tok=T, first_tok=10 ** 6)
-        for l in range(NL):
-            C.coli_rmsnorm(x, xn, 1e-5)
-            names = C.coli_moe_forward_profiled(layers[l], xn, x, ws, hs, C.COLI_FWD_ACCUM)
-            torch.cuda.synchronize()
-            for j in range(len(names)):
-                kern[names[j]] = kern.get(names[j], 0.0) + \
-                    evs[2 * j].elapsed_time(evs[2 * j + 1]) / NL
-            uniq.append(int((counts_view[:E] > 0).sum().item()) + S)
-    uniq_avg = float(np.mean(uniq)) if uniq else float(E + S)
-    gate_up_bytes = uniq_avg * (2 * I * H * bits // 8 + 4 * 2 * I) + T * (H + H // 8) + \
-        T * (K + S) * (I + I // 8)
-    out = {
-        "metric": "MoE-stack tokens/s (8 pre-norm residual MoE layers)",
-        "value": round(T * n_steps / elapsed, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": n_steps, "warmup": n_warm, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": f"int{bits}xint8 (int32 block dots, f64 scales)",
-        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights packed by coli_pack_weights)",
-        "config": {"workload": cfg.name + (f" int{bits} weights" if bits != 4 else ""),
-                   "tokens_per_step": T, "layers": NL, "hidden": H,
-                   "inter": I, "n_experts": E, "top_k": K, "n_shared": S, "weight_bits": bits,
-                   "parallelism": "none (1 GPU)"},
-        "ms_per_layer": round(ms_per_step / NL, 4),
-        "unique_experts_per_layer": round(uniq_avg, 2),
-        "kernel_avg_us_per_layer": {k: round(v * 1e3, 2) for k, v in kern.items()},
-        "roofline": gateup_roofline(kern, cfg, gate_up_bytes, T, bits),
-        "cpu_baseline": None,
-        "setup_s": round(setup_s, 1),
-    }
-    print(json.dumps(out), flush=True)
+    import oracle
+    wr, b = cs.router(cfg, layer, "cpu")
+    wr, b = wr.numpy(), b.numpy()
+    if OL is None:
+        OL = oracle.OracleLayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
+                                cfg.norm_topk, cfg.rho, wr, b, {})
+    idx, _, _ = oracle.route(x, wr, b, cfg.top_k, cfg.norm_topk, cfg.rho)
+    need = set(int(e) for e in np.unique(idx)) | ({cfg.n_experts} if cfg.n_shared else set())
+    for e in sorted(need - set(OL.experts)):
+        OL.add_expert(e, oracle.pack_expert(*[cs.expert_matrix(cfg, layer, e, m, "cuda").cpu()
+                                              .numpy() for m in ("gate", "up", "down")]))
+    return OL
 
 
 def cpu_baseline(cfg, budget_s):
     """The oracle (plain C++ CPU reference, fp64) on a bounded sample of the
-    same workload: tokens of replica 0, one forward per token, until the time
-    budget is spent. Expert fp32 weights are drawn by coli_synth (on the GPU for
-    speed; the draw is bit-identical to the CPU draw) and packed by the oracle."""
+    same workload: batches of cfg.n_tok tokens of replica 0 (at most 32 tokens
+    per forward), until the time budget is spent. Expert fp32 weights are drawn
+    by coli_synth (on the GPU for speed; the draw is bit-identical to the CPU
+    draw) and packed by the oracle; drawing and packing are not timed."""
     import numpy as np
-    import torch
 
     import coli_synth as cs
     import oracle
 
-    H, I = cfg.hidden, cfg.inter
-    wr, b = cs.router(cfg, 0, "cpu")
-    wr, b = wr.numpy(), b.numpy()
-    OL = oracle.OracleLayer(H, I, cfg.n_experts, cfg.top_k, cfg.n_shared, cfg.norm_topk,
-                            cfg.rho, wr, b, {})
-    timed = 0.0
-    n_tok = 0
+    B = min(cfg.n_tok, 32)
+    timed, n_tok = 0.0, 0
+    OL = None
     while timed < budget_s and n_tok < 4096:
-        x = cs.activations(cfg, 0, "cpu", n_tok=cfg.n_tok, first_tok=n_tok).numpy()
+        x = cs.activations(cfg, 0, "cpu", n_tok=B, first_tok=n_tok).numpy()
         if cfg.rmsnorm_input:
             x = oracle.rmsnorm(x, float(np.float32(1e-5)))
-        idx, _, _ = oracle.route(x, wr, b, cfg.top_k, cfg.norm_topk, cfg.rho)
-        need = set(int(e) for e in np.unique(idx)) | ({cfg.n_experts} if cfg.n_shared else set())
-        for e in sorted(need - set(OL.experts)):
-            OL.add_expert(e, oracle.pack_expert(*[cs.expert_matrix(cfg, 0, e, m, "cuda").cpu().numpy()
-                                                  for m in ("gate", "up", "down")]))
+        OL = _oracle_layer(cfg, 0, x, OL)
         t0 = time.perf_counter()
         OL.forward(x)
         timed += time.perf_counter() - t0
-        n_tok += cfg.n_tok
-    cpu_model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
-                             None)
-    except OSError:
-        pass
+        n_tok += B
+    part = "" if B == cfg.n_tok else f" (a {B}-token part of each {cfg.n_tok}-token batch)"
     return {"value": round(n_tok / timed, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "cpu_model": cpu_model, "kind": "oracle",
-            "sample": f"{n_tok} tokens of {cfg.name}, replica 0, one oracle forward per "
-                      f"{cfg.n_tok} token(s), {timed:.1f} s timed"}
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"{n_tok} tokens of {cfg.name}{part}, replica 0, {B} token(s) per oracle "
+                      f"forward, {timed:.1f} s timed"}
+
+
+def cpu_baseline_stack(cfg, budget_s):
+    """The oracle on a bounded sample of the stacked workload: layer 0 only, on
+    batches of 32 RMS-normalised tokens of the stack's input, until the time
+    budget is spent; the stack's rate is that layer rate divided by the number
+    of layers (every layer has the same shape and the same per-token work)."""
+    import numpy as np
+
+    import coli_synth as cs
+    import oracle
+
+    B = 32
+    timed, n_tok = 0.0, 0
+    OL = None
+    while timed < budget_s and n_tok < cfg.n_tok:
+        x = cs.activations(cfg, 0, "cpu", n_tok=B, first_tok=n_tok).numpy()
+        xn = oracle.rmsnorm(x, float(np.float32(1e-5)))
+        OL = _oracle_layer(cfg, 0, xn, OL)
+        t0 = time.perf_counter()
+        OL.forward(xn, y_in=x)
+        timed += time.perf_counter() - t0
+        n_tok += B
+    return {"value": round(n_tok / timed / cfg.n_layers, 4), "unit": "tokens/s",
+            "cores": oracle.num_threads(), "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"layer 0 of {cfg.name} on {n_tok} tokens ({B} per oracle forward, "
+                      f"RMSNorm + residual), {timed:.1f} s timed; stack rate = layer rate / "
+                      f"{cfg.n_layers}"}
 
 
 if __name__ == "__main__":
