@@ -69,9 +69,11 @@ def parse():
                          "MFMA kernels at every token count)")
     ap.add_argument("--groups", type=str, default="",
                     help="NG,TG: group-limited expert selection (NG groups, the TG best kept)")
-    ap.add_argument("--op", choices=("layer", "pack_fp8"), default="layer",
+    ap.add_argument("--op", choices=("layer", "pack_fp8", "mfma_ceiling"), default="layer",
                     help="pack_fp8: time the FP8 e4m3 (128 x 128 block scales) -> int4 "
-                         "conversion of one layer's expert weights instead of the layer")
+                         "conversion of one layer's expert weights instead of the layer; "
+                         "mfma_ceiling: issue rates of the int8 MFMA forms and of the exact "
+                         "per-block epilogue (coli_mfma_probe)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB a few times (the "
                          "reference kernel that scales HBM byte counters) and exit")
@@ -109,6 +111,9 @@ def main():
     torch.cuda.set_device(0)
     if args.op == "pack_fp8":
         run_pack_fp8(args, cs.CONFIGS[1 if args.config is None else args.config])
+        return
+    if args.op == "mfma_ceiling":
+        run_mfma_ceiling()
         return
     if args.sweep:
         run_sweep(args, cs.CONFIGS[2 if args.config is None else args.config],
@@ -498,6 +503,43 @@ def run_pack_fp8(args, cfg):
                      "traffic": TRAFFIC.get(("pack_fp8_gateup", workload))},
         "cpu_baseline": None,
     }), flush=True)
+
+
+def run_mfma_ceiling():
+    """Issue rates of the int8 MFMA forms and of the exact per-block epilogue
+    (coli_mfma_probe) at 1, 2 and 4 waves per SIMD (256 x 1, 2, 4 workgroups
+    of 4 waves), one JSON line per mix: shader-clock cycles per loop
+    iteration per wave, and the int8 rate against 5.0 POP/s from the launch's
+    event time. The epilogue mixes bound the grouped kernels: every MFMA
+    result needs one scaled add per 32-block."""
+    import torch
+
+    import int4_quantized_moe_sigmoid_amd as C
+    mixes = {0: ("8 x mfma_i32_16x16x32_i8", 8 * 16384), 1: ("8 x mfma_i32_16x16x64_i8", 8 * 32768),
+             2: ("4 x mfma_i32_32x32x32_i8", 4 * 65536), 3: ("16 x v_mad_i64_i32", 0),
+             4: ("16 x (v_cvt_f64_i32 + v_fma_f64)", 0),
+             5: ("2 x 32x32x32 + int64 epilogue (32 v_mad_i64_i32)", 2 * 65536),
+             6: ("2 x 32x32x32 + fp64 epilogue (32 cvt + 32 fma)", 2 * 65536),
+             7: ("4 x 16x16x32 + int64 epilogue (16 v_mad_i64_i32)", 4 * 16384)}
+    iters = 4000
+    for wpc in (1, 2, 4):
+        nwg = 256 * wpc
+        cyc = torch.zeros(4 * nwg + 1, dtype=torch.int64, device="cuda")
+        for kind, (name, ops) in mixes.items():
+            C.coli_mfma_probe(kind, nwg, iters, cyc)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            C.coli_mfma_probe(kind, nwg, iters, cyc)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            per_it = float(cyc[:4 * nwg].double().mean().item()) / iters
+            tops = ops * iters * nwg * 4 / (ms * 1e-3) / 1e12
+            print(json.dumps({"probe": name, "waves_per_simd": wpc,
+                              "cycles_per_iter_per_wave": round(per_it, 1),
+                              "int8_tops": round(tops, 1),
+                              "int8_frac_of_5000_tops": round(tops / 5000.0, 4),
+                              "ms": round(ms, 3)}), flush=True)
 
 
 def read_ceiling_gbps(C, gib=4, reps=10):

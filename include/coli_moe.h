@@ -276,6 +276,23 @@ COLI_API int coli_rmsnorm(const float* x, int64_t n_tok, int64_t dim, float eps,
  * COLI_E_ALIGN. Enqueues one kernel on `stream`. */
 COLI_API int coli_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
+/* Measurement helper, not a step of the layer: issue rates of the int8 MFMA
+ * forms and of the exact per-block epilogue the grouped kernels apply to
+ * every MFMA result (one scaled add per row, token and 32-block, fixed by the
+ * Q8_0 format). Enqueues n_workgroups workgroups of 4 waves; every wave runs
+ * `iters` iterations of one instruction mix and stores the shader-clock
+ * cycles its loop took. kind: 0 = 8 v_mfma_i32_16x16x32_i8, 1 = 8
+ * v_mfma_i32_16x16x64_i8, 2 = 4 v_mfma_i32_32x32x32_i8, 3 = 16
+ * v_mad_i64_i32, 4 = 16 (v_cvt_f64_i32 + v_fma_f64), 5 = 2 32x32x32 each
+ * followed by the int64 epilogue of its 16 results, 6 = the same with the
+ * fp64 epilogue, 7 = 4 16x16x32 with the int64 epilogue of their 4 results.
+ *   cycles: device int64 [4 n_workgroups + 1] (out; entry 4 w + v = wave v of
+ *   workgroup w; the last entry is scratch). Errors: COLI_E_INVAL (kind
+ *   outside 0..7, n_workgroups outside 1..2^20, iters <= 0, null pointer),
+ *   COLI_E_ALIGN (cycles not 8-byte aligned). */
+COLI_API int coli_mfma_probe(int kind, int64_t n_workgroups, int iters, int64_t* cycles,
+                             void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ EXPORTS = ("coli_strerror", "coli_pack_weights", "coli_pack_int4", "coli_pack_fp
            "coli_quant_q8", "coli_moe_workspace_bytes",
            "coli_moe_workspace_layout", "coli_moe_route", "coli_moe_forward",
            "coli_moe_forward_profiled", "coli_moe_forward_static", "coli_rmsnorm",
-           "coli_stream_read")
+           "coli_stream_read", "coli_mfma_probe")
 
 
 class ColiError(RuntimeError):
@@ -89,6 +89,7 @@ def _load():
     L.coli_moe_forward_static.argtypes = [ctypes.POINTER(coli_moe_weights), vp, i64, vp, u32, vp]
     L.coli_rmsnorm.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp]
     L.coli_stream_read.argtypes = [vp, i64, vp, vp]
+    L.coli_mfma_probe.argtypes = [i32, i64, i32, vp, vp]
     for name in EXPORTS:
         getattr(L, name)
     return L
@@ -279,3 +280,12 @@ def coli_stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     _check(_lib.coli_stream_read(_dev(buf, "buf", torch.uint8), buf.numel(),
                                  _dev(sink, "sink", torch.int32), _stream(stream)),
            "coli_stream_read")
+
+
+def coli_mfma_probe(kind: int, n_workgroups: int, iters: int, cycles: torch.Tensor, stream=None):
+    """Issue-rate probe (see coli_moe.h): cycles is int64 [4 n_workgroups + 1]."""
+    if cycles.numel() < 4 * n_workgroups + 1:
+        raise ValueError("cycles must hold 4 * n_workgroups + 1 entries")
+    _check(_lib.coli_mfma_probe(int(kind), int(n_workgroups), int(iters),
+                                _dev(cycles, "cycles", torch.int64), _stream(stream)),
+           "coli_mfma_probe")

@@ -15,6 +15,7 @@
 
 #include "coli_moe.h"
 #include "coli_launch.h"
+#include "k_probe.h"
 #include "k_route.h"
 #include "k_small.h"
 
@@ -484,6 +485,25 @@ COLI_API int coli_moe_forward_profiled(const coli_moe_weights* w, const float* x
     const int rc = forward_impl(w, x, n_tok, y, ws, ws_bytes, flags, (hipStream_t)stream, mk);
     if (n_used) *n_used = mk.used;
     return rc;
+}
+
+COLI_API int coli_mfma_probe(int kind, int64_t n_workgroups, int iters, int64_t* cycles,
+                             void* stream) {
+    if (kind < 0 || kind > 7 || n_workgroups <= 0 || n_workgroups > (1 << 20) || iters <= 0 ||
+        !cycles)
+        return COLI_E_INVAL;
+    if (reinterpret_cast<uintptr_t>(cycles) & 7u) return COLI_E_ALIGN;
+    const hipStream_t st = (hipStream_t)stream;
+    const unsigned g = (unsigned)n_workgroups;
+    long long* c = reinterpret_cast<long long*>(cycles);
+    switch (kind) {
+#define COLI_PROBE(k) \
+    case k: probe::k_mfma_probe<k><<<g, 256, 0, st>>>(iters, 1, c); break;
+        COLI_PROBE(0) COLI_PROBE(1) COLI_PROBE(2) COLI_PROBE(3)
+        COLI_PROBE(4) COLI_PROBE(5) COLI_PROBE(6) COLI_PROBE(7)
+#undef COLI_PROBE
+    }
+    return hip_status();
 }
 
 COLI_API int coli_rmsnorm(const float* x, int64_t n_tok, int64_t dim, float eps, float* out,
