@@ -33,6 +33,11 @@ HBM_PEAK_GBPS = 8000.0
 # WRITE_SIZE (two runs), scaled by what the counters read for a plain device
 # copy of known size (FETCH_SIZE x 2, WRITE_SIZE x 1). Keyed by (kernel,
 # workload as the JSON line names it); dropped whenever that kernel changes.
+# int8 MFMA + exact int64 per-block epilogue at 2 waves per SIMD (the grouped
+# gate/up kernel's occupancy), as a fraction of 5.0 POP/s: bench.py --op
+# mfma_ceiling, profiles/mfma_epilogue_ceiling.txt
+EPILOGUE_CEILING = 0.300
+
 TRAFFIC = {
     # profiles/dec_kernels_decode_T1.txt
     ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55670.6 * 2 + 38.4) * 1024,
@@ -44,6 +49,8 @@ TRAFFIC = {
     # profiles/pf_kernels_prefill_T512.txt, profiles/pf_kernels_prefill_T512_int8.txt
     ("pf_gateup", "prefill T512 zipf-bias"): (1819205.2 * 2 + 14437.5) * 1024,
     ("pf_gateup", "prefill T512 zipf-bias int8 weights"): (3383330.9 * 2 + 14460.6) * 1024,
+    # profiles/pf_kernels_stack_T4096.txt (k_pf32_gateup, per layer)
+    ("pf_gateup", "stack8 T4096 uniform"): (3497540.8 * 2 + 92160.2) * 1024,
     # profiles/pack_fp8_int4_layer.txt (the gate/up launch)
     ("pack_fp8_gateup", "pack_fp8 layer H6144 I2048 experts257"): (3164334.8 * 2 + 3166240.7) * 1024,
 }
@@ -415,7 +422,9 @@ def gateup_roofline(kern, cfg, wl, gate_up_bytes, T, mfma_bound):
                    "unit": "TOP/s (int8)", "frac": round(tops / 5000.0, 4),
                    "traffic": out["traffic"], "kernel": gk, "int8_ops_per_launch": ops,
                    "hbm_gbps": round(ach, 1), "hbm_frac": round(ach / HBM_PEAK_GBPS, 4),
-                   "bytes_per_launch": int(gate_up_bytes), "avg_launch_us": round(ms * 1e3, 2)}
+                   "bytes_per_launch": int(gate_up_bytes), "avg_launch_us": round(ms * 1e3, 2),
+                   "epilogue_ceiling_frac": EPILOGUE_CEILING,
+                   "frac_of_epilogue_ceiling": round(tops / 5000.0 / EPILOGUE_CEILING, 4)}
     return out
 
 
