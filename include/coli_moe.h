@@ -200,7 +200,17 @@ COLI_API int coli_moe_workspace_layout(const coli_moe_cfg* cfg, int64_t n_tok, u
  *   cfg->routed_scale, rounded to fp32.
  *   x [n_tok, H] fp32, w_router [E, H], bias [E] (in); topk_idx [n_tok, K]
  *   int32 and topk_w [n_tok, K] fp32 (out); ws: workspace of at least
- *   coli_moe_workspace_bytes(cfg, n_tok, 0) bytes. */
+ *   coli_moe_workspace_bytes(cfg, n_tok, 0) bytes, overwritten. The
+ *   selection needs every expert's logit of a token at once, so the logits
+ *   l [n_tok, E] (fp64) pass through ws between the GEMV/GEMM and the top-k
+ *   launch; above 8 tokens the router GEMM also cuts H into up to 16 slices
+ *   whose fp64 partial sums [slices, n_tok, E] live in ws until a second
+ *   launch adds them in slice order (a fixed order, so results do not depend
+ *   on scheduling). Nothing in ws is a result.
+ * Errors: COLI_E_INVAL (null pointer, bad cfg, n_tok < 0), COLI_E_ALIGN,
+ *   COLI_E_WORKSPACE (ws_bytes too small), COLI_E_UNSUPPORTED (n_tok > 2^20),
+ *   COLI_E_HIP (a launch failed);
+ *   nothing is launched on error. n_tok == 0 is a no-op. */
 COLI_API int coli_moe_route(const float* x, const float* w_router, const float* bias,
                             int64_t n_tok, const coli_moe_cfg* cfg, int32_t* topk_idx,
                             float* topk_w, void* ws, size_t ws_bytes, void* stream);
