@@ -209,8 +209,8 @@ COLI_API int coli_moe_workspace_layout(const coli_moe_cfg* cfg, int64_t n_tok, u
  *   on scheduling). Nothing in ws is a result.
  * Errors: COLI_E_INVAL (null pointer, bad cfg, n_tok < 0), COLI_E_ALIGN,
  *   COLI_E_WORKSPACE (ws_bytes too small), COLI_E_UNSUPPORTED (n_tok > 2^20),
- *   COLI_E_HIP (a launch failed);
- *   nothing is launched on error. n_tok == 0 is a no-op. */
+ *   COLI_E_HIP (a launch failed); nothing is launched on the other errors.
+ *   n_tok == 0 is a no-op. */
 COLI_API int coli_moe_route(const float* x, const float* w_router, const float* bias,
                             int64_t n_tok, const coli_moe_cfg* cfg, int32_t* topk_idx,
                             float* topk_w, void* ws, size_t ws_bytes, void* stream);
