@@ -76,7 +76,8 @@ def parse():
                          "MFMA kernels at every token count)")
     ap.add_argument("--groups", type=str, default="",
                     help="NG,TG: group-limited expert selection (NG groups, the TG best kept)")
-    ap.add_argument("--op", choices=("layer", "pack_fp8", "mfma_ceiling"), default="layer",
+    ap.add_argument("--op", choices=("layer", "pack_fp8", "mfma_ceiling", "graph"),
+                    default="layer",
                     help="pack_fp8: time the FP8 e4m3 (128 x 128 block scales) -> int4 "
                          "conversion of one layer's expert weights instead of the layer; "
                          "mfma_ceiling: issue rates of the int8 MFMA forms and of the exact "
@@ -121,6 +122,9 @@ def main():
         return
     if args.op == "mfma_ceiling":
         run_mfma_ceiling()
+        return
+    if args.op == "graph":
+        run_graph_compare(args, cs.CONFIGS[1 if args.config is None else args.config])
         return
     if args.sweep:
         run_sweep(args, cs.CONFIGS[2 if args.config is None else args.config],
@@ -549,6 +553,83 @@ def run_mfma_ceiling():
                               "int8_tops": round(tops, 1),
                               "int8_frac_of_5000_tops": round(tops / 5000.0, 4),
                               "ms": round(ms, 3)}), flush=True)
+
+
+def run_graph_compare(args, cfg, per_graph=8):
+    """Layer steps launched one by one against replays of a HIP graph that
+    holds `per_graph` of them (captured from the same calls, replicas round
+    robin): whether launching from a graph shortens the gaps between the
+    layer's data-dependent launches. Every replay is checked bit for bit
+    against the eager results, with eager work and synchronisations between
+    replays. Prints one JSON line per mode and round."""
+    import torch
+
+    import coli_synth as cs
+    import int4_quantized_moe_sigmoid_amd as C
+
+    T, H = cfg.n_tok, cfg.hidden
+    lc = C.make_cfg(H, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared, cfg.norm_topk,
+                    cfg.rho, 1, 1, 4)
+    R = max(1, args.replicas) if T < 64 and cfg.n_experts * cfg.expert_bytes() > (1 << 28) else 1
+    pack = lambda w, qv, sv: C.coli_pack_weights(w, 4, qv, sv)
+    layers = []
+    for r in range(R):
+        wr, b, q, s = cs.build_layer(cfg, r, "cuda", pack, bits=4)
+        layers.append(C.LayerWeights(lc, wr, b, q, s))
+    xs = []
+    for i in range(per_graph):
+        raw = cs.activations(cfg, i % R, "cuda", n_tok=T, first_tok=(i // R) * T)
+        if cfg.rmsnorm_input:
+            xn = torch.empty_like(raw)
+            C.coli_rmsnorm(raw, xn, 1e-5)
+            raw = xn
+        xs.append(raw)
+    ys = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in range(per_graph)]
+    ws = torch.empty(C.coli_moe_workspace_bytes(lc, T), dtype=torch.uint8, device="cuda")
+
+    def eager():
+        for j in range(per_graph):
+            C.coli_moe_forward(layers[j % R], xs[j], ys[j], ws)
+
+    eager()
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        eager()
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        eager()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in ys:
+            y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(ys, ref)):
+            raise RuntimeError(f"graph replay {rep} differs from the eager forward")
+        eager()
+        torch.cuda.synchronize()
+    rounds = max(1, args.steps // per_graph)
+    for k in range(2):
+        for mode in ("eager", "graph"):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(rounds):
+                if mode == "eager":
+                    eager()
+                else:
+                    g.replay()
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            print(json.dumps({"op": "graph", "workload": cfg.name, "mode": mode, "round": k,
+                              "steps": rounds * per_graph,
+                              "us_per_step": round(1e6 * dt / (rounds * per_graph), 2),
+                              "replays_checked": 3}), flush=True)
 
 
 def read_ceiling_gbps(C, gib=4, reps=10):
