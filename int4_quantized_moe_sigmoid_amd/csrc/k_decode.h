@@ -983,11 +983,13 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 double p = 0.0;
+                if (i < n) {  // n is wave-uniform: no dot products for absent tokens
 #pragma unroll
-                for (int j = 0; j < NBJ; ++j) {
-                    const bool ok = i < n && lane + 64 * j < BI;
-                    const double hd = ok ? (double)o.hdf[i][j] * F::kInv : 0.0;
-                    p += hd * (double)F::dot(o.w[r][j], o.ha[i][j][0], o.ha[i][j][1]);
+                    for (int j = 0; j < NBJ; ++j) {
+                        const bool ok = lane + 64 * j < BI;
+                        const double hd = ok ? (double)o.hdf[i][j] * F::kInv : 0.0;
+                        p += hd * (double)F::dot(o.w[r][j], o.ha[i][j][0], o.ha[i][j][1]);
+                    }
                 }
                 vals[r * NT + i] = p;
             }
@@ -1108,20 +1110,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n_ent = T * K;
-    if (threadIdx.x == 0) {
-        int nu = a.uinfo[0];
-        for (int v = 0; v < nu; ++v) {
-            s_e[v] = a.uinfo[1 + 3 * v];
-            s_s0[v] = a.uinfo[2 + 3 * v];
-            s_n[v] = a.uinfo[3 + 3 * v];
+    // the published route in one round trip: lane v of wave 0 reads entry v
+    // (unconditionally: the entries past n_uniq are in-bounds leftovers)
+    if (wave == 0) {
+        const int nu = a.uinfo[0];
+        const int ue = a.uinfo[1 + 3 * lane];
+        const int us0 = a.uinfo[2 + 3 * lane];
+        const int un = a.uinfo[3 + 3 * lane];
+        if (lane < nu) {
+            s_e[lane] = ue;
+            s_s0[lane] = us0;
+            s_n[lane] = un;
         }
-        if (S) {
-            s_e[nu] = E;
-            s_s0[nu] = n_ent;
-            s_n[nu] = T;
-            ++nu;
+        if (lane == 0) {
+            if (S) {
+                s_e[nu] = E;
+                s_s0[nu] = n_ent;
+                s_n[nu] = T;
+            }
+            s_nu = nu + (S ? 1 : 0);
         }
-        s_nu = nu;
     }
     for (int i = threadIdx.x; i < n_ent + S * T; i += 256) {
         s_w[i] = (i < n_ent) ? reinterpret_cast<const float*>(a.uinfo + kUinfoW)[i] : 1.0f;
@@ -1174,7 +1182,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             const int s0 = __builtin_amdgcn_readfirstlane(s_s0[vc]);
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
-                const bool ok = i < n && lane < BI;
+                // the expert's tokens only (n is wave-uniform; most routed
+                // experts of a few-token call hold one)
+                if (v >= nu || i >= n) break;
+                const bool ok = lane < BI;
                 const double hd = ok ? (double)hdf[m][i] * F::kInv : 0.0;
                 double vals[RW];
 #pragma unroll
@@ -1183,7 +1194,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 const double sum = wave_reduce_tr<RW>(vals, lane);
                 const int r = lane >> 3;  // 64 / RW lanes per value
                 const float ds = __shfl(dsm[m], r, 64);
-                if (v < nu && i < n && (lane & 7) == 0) s_y[r][s0 + i] = (float)((double)ds * sum);
+                if ((lane & 7) == 0) s_y[r][s0 + i] = (float)((double)ds * sum);
             }
         }
     }
