@@ -793,6 +793,16 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
         const int h = min((int)threadIdx.x * 4 + 1024 * it, H - 4);
         wv[it] = *reinterpret_cast<const float4*>(wrow + h);
     }
+    // every token's activations requested with the router row (clamped,
+    // unconditional loads), before any arithmetic
+    float4 xv[NT][kIt];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int it = 0; it < kIt; ++it) {
+            const int h = min((int)threadIdx.x * 4 + 1024 * it, H - 4);
+            xv[t][it] = *reinterpret_cast<const float4*>(a.x + (int64_t)min(t, T - 1) * H + h);
+        }
     {
         const int blk = e * 8 + (int)(threadIdx.x >> 5);
         const int k = threadIdx.x & 31;
@@ -816,11 +826,10 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
             for (int it = 0; it < kIt; ++it) {
                 const int h = threadIdx.x * 4 + 1024 * it;
                 if (h < H) {
-                    const float4 xv = *reinterpret_cast<const float4*>(a.x + (int64_t)t * H + h);
-                    acc[t] += (double)xv.x * (double)wv[it].x;
-                    acc[t] += (double)xv.y * (double)wv[it].y;
-                    acc[t] += (double)xv.z * (double)wv[it].z;
-                    acc[t] += (double)xv.w * (double)wv[it].w;
+                    acc[t] += (double)xv[t][it].x * (double)wv[it].x;
+                    acc[t] += (double)xv[t][it].y * (double)wv[it].y;
+                    acc[t] += (double)xv[t][it].z * (double)wv[it].z;
+                    acc[t] += (double)xv[t][it].w * (double)wv[it].w;
                 }
             }
         }
