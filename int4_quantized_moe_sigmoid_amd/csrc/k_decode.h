@@ -450,48 +450,49 @@ __device__ __forceinline__ void route_small(const double* sig, const double* cva
         topk_wave<false>(sig + (int64_t)wv * E, cval + (int64_t)wv * E, E, K, S, norm, rho, gsel,
                          R, Z, wv);
     __syncthreads();
-    // Bucketing by wave 0, lane i holding entry i = t K + k ((token, k)
-    // order, T K <= 64): its sorted position is the number of entries with a
-    // smaller expert plus those of the same expert from earlier tokens; the
-    // expert's list index is the number of distinct smaller experts (entries
-    // that open an expert's run). Uniform loops over the entries, broadcast by
-    // lane reads.
+    // Bucketing by wave 0: entry i = t K + k ((token, k) order, T K <= 64)
+    // takes its sorted position (expert ascending, then token) from a bitonic
+    // sort of the keys (e, t, k) over the wave's 64 lanes, absent entries
+    // last, so that lane p ends up holding the p-th entry. An entry opens its
+    // expert's run when the entry before it has another expert; the run's
+    // list index is the number of runs opened before it (a ballot). No loop
+    // over the entries.
     if (threadIdx.x < 64) {
         const int n = T * K;
         const int lane = threadIdx.x;
-        const bool has = lane < n;
-        const int t = has ? lane / K : 0, k = has ? lane - t * K : 0;
-        const int e = has ? R.flat[lane] : 0x7fffffff;
-        int rank = 0, cnt = 0, first = 1;
-        for (int j = 0, tj = 0, kj = 0; j < n; ++j) {  // uniform
-            const int ej = __builtin_amdgcn_readlane(e, j);
-            rank += (ej < e || (ej == e && tj < t)) ? 1 : 0;
-            cnt += (ej == e) ? 1 : 0;
-            if (ej == e && tj < t) first = 0;
-            if (++kj == K) {
-                kj = 0;
-                ++tj;
+        unsigned key = 0xffffffffu;  // E <= 256, T <= 4, K <= 16: 14-bit keys
+        if (lane < n) {
+            const int t = lane / K, k = lane - t * K;
+            key = ((unsigned)R.flat[lane] << 6) | ((unsigned)t << 4) | (unsigned)k;
+        }
+#pragma unroll
+        for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const unsigned other = __shfl_xor(key, stride, 64);
+                const bool keep_min = ((lane & stride) == 0) == ((lane & size) == 0);
+                key = keep_min ? min(key, other) : max(key, other);
             }
-        }
-        int u = 0;
-        for (int j = 0; j < n; ++j) {  // uniform
-            const int ej = __builtin_amdgcn_readlane(e, j);
-            const int fj = __builtin_amdgcn_readlane(first, j);
-            u += (fj && ej < e) ? 1 : 0;
-        }
+        const bool has = lane < n;
+        const int e = (int)(key >> 6), t = (int)((key >> 4) & 3), k = (int)(key & 15);
+        const unsigned prev = __shfl_up(key, 1, 64);
+        const bool first = has && (lane == 0 || (prev >> 6) != (key >> 6));
+        const unsigned long long runs = __ballot(first);
+        const int u = __popcll(runs & ((1ull << lane) - 1ull));
+        const unsigned long long later = runs & ~((2ull << lane) - 1ull);
+        const int next = later ? __builtin_ctzll(later) : n;  // where the next run opens
         if (has) {
-            R.ent_e[rank] = e;
-            R.ent_t[rank] = t;
-            R.ent_w[rank] = R.w[t][k];
-            R.slot_of[t][k] = rank;
+            R.ent_e[lane] = e;
+            R.ent_t[lane] = t;
+            R.ent_w[lane] = R.w[t][k];
+            R.slot_of[t][k] = lane;
             if (first) {
                 R.u_e[u] = e;
-                R.u_s0[u] = rank;
-                R.u_n[u] = cnt;
-                // the largest expert's run ends the sorted entries: u + 1 experts
-                if (rank + cnt == n) R.n_uniq = u + 1;
+                R.u_s0[u] = lane;
+                R.u_n[u] = next - lane;
             }
         }
+        if (lane == 0) R.n_uniq = __popcll(runs);
         if (lane < T && S) R.slot_of[lane][K] = n + lane;
     }
     __syncthreads();
