@@ -152,6 +152,7 @@ struct Route {
     int u_e[kMaxEntries];       // unique experts, ascending
     int u_s0[kMaxEntries];      // first sorted entry (= slot) of each
     int u_n[kMaxEntries];       // tokens of each
+    int u_w0[kMaxEntries];      // several tokens: first work unit of each (below)
 };
 
 // LDS scratch of the top-k, dead once the routing is done.
@@ -494,6 +495,11 @@ __device__ __forceinline__ void route_small(const double* sig, const double* cva
         }
         if (lane == 0) R.n_uniq = __popcll(runs);
         if (lane < T && S) R.slot_of[lane][K] = n + lane;
+        // gate/up work units (k_dec_gateup): an expert with one token takes
+        // one unit, one with several (more arithmetic per weight byte) two
+        const bool multi = first && next - lane > 1;
+        const int mb = __popcll(__ballot(multi) & ((1ull << lane) - 1ull));
+        if (first) R.u_w0[u] = u + mb;
     }
     __syncthreads();
 }
@@ -630,7 +636,9 @@ __device__ __forceinline__ void gateup_block_lds(const DecArgs& a, int e, int hb
                                                  const float* xds, float (*hbuf)[32]) {
     typedef DW<BITS> F;
     typedef typename F::blk Blk;
-    constexpr int HR = F::HR, RQ = 2 * HR, NS = 8 / HR;
+    // half the one-token step: two steps of weight loads in flight stay within
+    // the registers of three workgroups per CU
+    constexpr int HR = (F::HR > 1) ? F::HR / 2 : 1, RQ = 2 * HR, NS = 8 / HR;
     const int H = a.H, I = a.I, BH = H >> 5;
     const int64_t rowb = (int64_t)H * BITS / 8;
     const int lane = threadIdx.x & 63;
@@ -869,59 +877,89 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecArgs a) {
     __shared__ int s_tok[NT];
     uint8_t* xs = act;
     float* xds = reinterpret_cast<float*>(act + NT * a.H);
-    // a workgroup covers HB consecutive h-blocks of 32 rows (one at a single
-    // token; two with several, so fewer workgroups redo the routing)
-    constexpr int HB = (NT > 1) ? 2 : 1;
-    const int nw = (a.I >> 5) / HB;  // workgroups per expert
+    // One token: a workgroup per (expert, h-block of 32 rows). Several
+    // tokens: work units of nrb / 2 workgroups; an expert holding one token
+    // takes one unit (two h-blocks per workgroup, so fewer workgroups redo
+    // the routing), one holding several (and the shared expert) takes two
+    // (one h-block per workgroup: its steps carry the arithmetic of every
+    // token and would otherwise make the tail). The grid covers the most
+    // units a routing can produce (one per entry T K, two per expert).
+    const int nrb = a.I >> 5;
+    const int nw = (NT > 1) ? nrb / 2 : nrb;  // workgroups per unit / per expert
     int b = blockIdx.x;
-    if (a.S) {
-        if (b < nw) {
-            if ((int)threadIdx.x < NT) s_tok[threadIdx.x] = min((int)threadIdx.x, a.T - 1);
-            if (NT > 1) {
-                stage_all_tokens(a, xs, xds, 0, 256);
-                __syncthreads();
-#pragma unroll 1
-                for (int h = 0; h < HB; ++h)
-                    gateup_block_lds<NT, NBJ, TAP, BITS>(a, a.E, b * HB + h, a.T, s_tok, a.T * a.K,
-                                                         xs, xds, hbuf);
-            } else {
+    if (NT == 1) {
+        if (a.S) {
+            if (b < nrb) {
+                if (threadIdx.x == 0) s_tok[0] = 0;
                 __syncthreads();
                 gateup_block<NT, NBJ, TAP, BITS>(a, a.E, b, a.T, s_tok, a.T * a.K, hbuf);
+                return;
             }
-            return;
+            b -= nrb;
         }
-        b -= nw;
-    }
-    // the routing waves win issue slots over co-resident streaming waves:
-    // routing latency sits on the path to this workgroup's first weight load
-    // with fewer than four tokens the last wave, which routes none, stages
-    // the activations while the others route
-    const bool stage_early = NT > 1 && a.T < 4;
-    if (stage_early && threadIdx.x >= 192) stage_all_tokens(a, xs, xds, 192, 64);
-    __builtin_amdgcn_s_setprio(3);
-    if (NT == 1)
+        // routing latency sits on the path to this workgroup's first weight
+        // load: the routing wave wins issue slots over co-resident streaming
+        // waves
+        __builtin_amdgcn_s_setprio(3);
         route_one(a.sig, a.cval, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, Z);
-    else
-        route_small(a.sig, a.cval, a.T, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, Z);
-    __builtin_amdgcn_s_setprio(0);
-    if (b == 0) publish_route(a, R);
-    const int u = b / nw, hw = b - u * nw;
-    if (u >= R.n_uniq) return;
-    const int e = __builtin_amdgcn_readfirstlane(R.u_e[u]);
-    const int s0 = __builtin_amdgcn_readfirstlane(R.u_s0[u]);
-    const int n = __builtin_amdgcn_readfirstlane(R.u_n[u]);
-    if (NT > 1) {
-        if (!stage_early) {
-            stage_all_tokens(a, xs, xds, 0, 256);
-            __syncthreads();
-        }
-#pragma unroll 1
-        for (int h = 0; h < HB; ++h)
-            gateup_block_lds<NT, NBJ, TAP, BITS>(a, e, hw * HB + h, n, &R.ent_t[s0], s0, xs, xds,
-                                                 hbuf);
-    } else {
+        __builtin_amdgcn_s_setprio(0);
+        if (b == 0) publish_route(a, R);
+        const int u = b / nw, hw = b - u * nw;
+        if (u >= R.n_uniq) return;
+        const int e = __builtin_amdgcn_readfirstlane(R.u_e[u]);
+        const int s0 = __builtin_amdgcn_readfirstlane(R.u_s0[u]);
+        const int n = __builtin_amdgcn_readfirstlane(R.u_n[u]);
         gateup_block<NT, NBJ, TAP, BITS>(a, e, hw, n, &R.ent_t[s0], s0, hbuf);
+        return;
     }
+    // several tokens: the work of this workgroup as (expert, first h-block,
+    // h-blocks, tokens, their slots); one call site below
+    int e, hb0, nhb, n, s0;
+    const int* tok;
+    bool staged = false;
+    if (a.S && b < nrb) {
+        if ((int)threadIdx.x < NT) s_tok[threadIdx.x] = min((int)threadIdx.x, a.T - 1);
+        e = a.E;
+        hb0 = b;
+        nhb = 1;
+        n = a.T;
+        s0 = a.T * a.K;
+        tok = s_tok;
+    } else {
+        if (a.S) b -= nrb;
+        // with fewer than four tokens the last wave, which routes none, stages
+        // the activations while the others route
+        staged = a.T < 4;
+        if (staged && threadIdx.x >= 192) stage_all_tokens(a, xs, xds, 192, 64);
+        __builtin_amdgcn_s_setprio(3);
+        route_small(a.sig, a.cval, a.T, a.E, a.K, a.S, a.norm, a.rho, a.gsel, R, Z);
+        __builtin_amdgcn_s_setprio(0);
+        if (b == 0) publish_route(a, R);
+        // the expert whose units hold unit b / nw: lane v tests expert v (every
+        // wave computes the same ballot)
+        const int unit = b / nw, hw = b - unit * nw;
+        const int lane = threadIdx.x & 63;
+        const int nu = R.n_uniq;
+        const int w0 = R.u_w0[min(lane, nu - 1)], nv = R.u_n[min(lane, nu - 1)];
+        const unsigned long long hm =
+            __ballot(lane < nu && unit >= w0 && unit < w0 + (nv > 1 ? 2 : 1));
+        if (hm == 0ull) return;  // no expert: nothing to do
+        const int u = __builtin_ctzll(hm);
+        e = __builtin_amdgcn_readfirstlane(R.u_e[u]);
+        s0 = __builtin_amdgcn_readfirstlane(R.u_s0[u]);
+        n = __builtin_amdgcn_readfirstlane(R.u_n[u]);
+        const int uw0 = __builtin_amdgcn_readfirstlane(R.u_w0[u]);
+        hb0 = (n > 1) ? (unit - uw0) * nw + hw : 2 * hw;
+        nhb = (n > 1) ? 1 : 2;
+        tok = &R.ent_t[s0];
+    }
+    if (!staged) {
+        stage_all_tokens(a, xs, xds, 0, 256);
+        __syncthreads();
+    }
+#pragma unroll 1
+    for (int h = 0; h < nhb; ++h)
+        gateup_block_lds<NT, NBJ, TAP, BITS>(a, e, hb0 + h, n, tok, s0, xs, xds, hbuf);
 }
 
 // C: down projection of every expert in use and the weighted combine.

@@ -1,4 +1,6 @@
 // Launches of the few-token kernels (k_decode.h).
+#include <algorithm>
+
 #include "coli_launch.h"
 #include "k_decode.h"
 
@@ -20,8 +22,13 @@ void launch_small_tap(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     launch(mk, dec::k_dec_router<NT, BITS>, (a.E > qb) ? a.E : qb, 256, 0, s, a);
     mk.mark("dec_gateup");
     const int um = (a.T * a.K < a.E) ? a.T * a.K : a.E;
-    const int hbw = (NT > 1) ? 2 : 1;  // h-blocks per workgroup (k_dec_gateup)
-    launch(mk, dec::k_dec_gateup<NT, NBJH, TAP, BITS>, (a.S + um) * (nrb / hbw), 256, 0, s, a);
+    // one token: a workgroup per h-block of every expert that can be in use;
+    // several: the shared expert's h-blocks, then work units of nrb / 2
+    // workgroups (an expert with one token takes one unit, with several two,
+    // so never more units than entries T K, nor than 2 E)
+    const int gu = (NT > 1) ? a.S * nrb + std::min(a.T * a.K, 2 * a.E) * (nrb / 2)
+                            : (a.S + um) * nrb;
+    launch(mk, dec::k_dec_gateup<NT, NBJH, TAP, BITS>, gu, 256, 0, s, a);
     mk.mark("dec_down");
     if (NT == 4)
         launch(mk, dec::k_dec_down_x<NT, 1, BITS>, a.H / 8, 256, 0, s, a);
