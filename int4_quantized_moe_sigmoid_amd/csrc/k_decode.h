@@ -1021,9 +1021,11 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
             }
         }
     };
-    // y_e of this wave's rows for the n tokens of one expert, added into
-    // s_acc with the slot weights (callers go in ascending expert order,
-    // the shared expert last)
+    // y_e of this wave's rows for the n tokens of one expert, added with the
+    // slot weights (callers go in ascending expert order, the shared expert
+    // last): into s_acc, or with one token into racc, a register of the lane
+    // that holds row r's value (no LDS round trip in the chain of experts)
+    double racc = 0.0;
     auto compute = [&](const Operands& o, int s0, int n) {
         double vals[V];
 #pragma unroll
@@ -1051,7 +1053,10 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
                 for (int rr = 1; rr < RPW; ++rr)
                     if (r == rr) dsr = o.dsv[rr];
                 const float yv = (float)((double)dsr * sum);
-                s_acc[wave * RPW + r][s_t[s0 + i]] += (double)s_w[s0 + i] * (double)yv;
+                if constexpr (NT == 1)
+                    racc += (double)s_w[s0] * (double)yv;
+                else
+                    s_acc[wave * RPW + r][s_t[s0 + i]] += (double)s_w[s0 + i] * (double)yv;
             }
         }
     };
@@ -1125,7 +1130,14 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
         compute_batch(v0 + NB, b1);
     }
     if (S) compute(sh, n_ent, T);
-    if (lane < RPW * NT) {
+    if constexpr (NT == 1) {
+        const int r = lane >> kShift;
+        if (lane == (r << kShift) && T > 0) {
+            float* out = a.y + c0 + r;
+            const float yv = (float)racc;
+            *out = a.accum ? *out + yv : yv;
+        }
+    } else if (lane < RPW * NT) {
         const int r = lane / NT, t = lane - r * NT;
         if (t < T) {
             float* out = a.y + (int64_t)t * H + c0 + r;
