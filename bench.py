@@ -514,8 +514,34 @@ def run_pack_fp8(args, cfg):
                      "kernel": "k_pack_fp8_int4_wave (gate/up rows)",
                      "algorithmic_bytes": int(gu_bytes),
                      "traffic": TRAFFIC.get(("pack_fp8_gateup", workload))},
-        "cpu_baseline": None,
+        "cpu_baseline": (cpu_baseline_pack_fp8(mats[0][0], mats[0][1], args.cpu_seconds)
+                         if args.cpu_seconds > 0 else None),
     }), flush=True)
+
+
+def cpu_baseline_pack_fp8(q8, bs, budget_s, rows=1024):
+    """The oracle's FP8 -> int4 conversion on a bounded sample of the same
+    workload: consecutive 1024-row chunks (whole 128-row scale blocks) of the
+    gate/up matrix, copied to the host untimed, until the time budget is spent;
+    the rate counts the same algorithmic bytes as the GPU figure."""
+    import oracle
+    timed, done, r0, chunks = 0.0, 0, 0, 0
+    n_rows, cols = q8.shape
+    while timed < budget_s and r0 < n_rows:
+        r1 = min(n_rows, r0 + rows)
+        qh = q8[r0:r1].cpu().numpy()
+        bh = bs[r0 // 128:(r1 + 127) // 128].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.pack_fp8_int4(qh, bh)
+        timed += time.perf_counter() - t0
+        done += r1 - r0
+        chunks += 1
+        r0 = r1
+    nbytes = done * cols * 1.5 + 4 * done + 4 * ((done + 127) // 128) * ((cols + 127) // 128)
+    return {"value": round(nbytes / timed / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "cpu_model": _cpu_model(), "kind": "oracle",
+            "sample": f"{done} gate/up rows of {cols} codes ({chunks} chunks of up to {rows} "
+                      f"rows), {timed:.1f} s timed"}
 
 
 def run_mfma_ceiling():
