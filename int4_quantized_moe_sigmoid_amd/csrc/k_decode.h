@@ -1119,15 +1119,79 @@ __global__ __launch_bounds__(256) void k_dec_down(DecArgs a) {
     };
     Batch b0, b1;
     if (nr > 0) load(0, b0);
+    if constexpr (NT == 1 && NB == 1) {
+        // one token: the dot products of two experts, then one reduction of
+        // their four row sums (the same addition tree per value as two
+        // separate reductions, so the same results, in fewer dependent steps)
+        auto partial = [&](const Operands& o, double (&pp)[RPW]) {
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                double p = 0.0;
+#pragma unroll
+                for (int j = 0; j < NBJ; ++j) {
+                    const bool ok = lane + 64 * j < BI;
+                    const double hd = ok ? (double)o.hdf[0][j] * F::kInv : 0.0;
+                    p += hd * (double)F::dot(o.w[r][j], o.ha[0][j][0], o.ha[0][j][1]);
+                }
+                pp[r] = p;
+            }
+        };
+        constexpr int V2 = 2 * RPW;
+        constexpr int kShift2 = (V2 == 8) ? 3 : (V2 == 4) ? 4 : 5;
 #pragma unroll 1
-    for (int v0 = 0; v0 < nr; v0 += 2 * NB) {
-        if (v0 + NB < nr) load(v0 + NB, b1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_batch(v0, b0);
-        if (v0 + NB >= nr) break;
-        if (v0 + 2 * NB < nr) load(v0 + 2 * NB, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute_batch(v0 + NB, b1);
+        for (int v0 = 0; v0 < nr; v0 += 2) {
+            if (v0 + 1 >= nr) {  // odd count: the last one alone
+                compute(b0.o[0], __builtin_amdgcn_readfirstlane(s_s0[v0]), 1);
+                break;
+            }
+            load(v0 + 1, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            double vals[V2];
+            double pa[RPW], pb[RPW];
+            partial(b0.o[0], pa);
+            float dsa[RPW];
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) dsa[r] = b0.o[0].dsv[r];
+            // unconditional (the index is clamped: the last pair requests
+            // expert nr - 1 again), so that the wait for b1 does not also wait
+            // for these loads, as it would after a conditional issue
+            load(v0 + 2, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            partial(b1.o[0], pb);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                vals[r] = pa[r];
+                vals[RPW + r] = pb[r];
+            }
+            const double sum = wave_reduce_tr<V2>(vals, lane);
+            // value (expert m, row r) sits in lanes (m RPW + r) << kShift2; row
+            // r's combine lives in lane r << kShift: experts added in order
+            const int r = lane >> kShift;
+            float dsr_a = dsa[0], dsr_b = b1.o[0].dsv[0];
+#pragma unroll
+            for (int rr = 1; rr < RPW; ++rr)
+                if (r == rr) {
+                    dsr_a = dsa[rr];
+                    dsr_b = b1.o[0].dsv[rr];
+                }
+            const double sa = __shfl(sum, r << kShift2, 64);
+            const double sb = __shfl(sum, (RPW + r) << kShift2, 64);
+            const float ya = (float)((double)dsr_a * sa);
+            const float yb = (float)((double)dsr_b * sb);
+            racc += (double)s_w[__builtin_amdgcn_readfirstlane(s_s0[v0])] * (double)ya;
+            racc += (double)s_w[__builtin_amdgcn_readfirstlane(s_s0[v0 + 1])] * (double)yb;
+        }
+    } else {
+#pragma unroll 1
+        for (int v0 = 0; v0 < nr; v0 += 2 * NB) {
+            if (v0 + NB < nr) load(v0 + NB, b1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_batch(v0, b0);
+            if (v0 + NB >= nr) break;
+            if (v0 + 2 * NB < nr) load(v0 + 2 * NB, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_batch(v0 + NB, b1);
+        }
     }
     if (S) compute(sh, n_ent, T);
     if constexpr (NT == 1) {
