@@ -165,6 +165,35 @@ def test_full_size_layers(C, ref, cid, n_tok):
     assert err <= TOL_REL_L2
 
 
+# the two ends of the several-token work split at full size (E256 K8, four
+# tokens): one token repeated four times (8 experts, each holding every token:
+# two work units each, one h-block per workgroup) and four independent tokens
+# (about 32 experts of one token each: as many units as entries, the most the
+# grid holds)
+@pytest.mark.parametrize("kind", ["same", "independent"])
+def test_several_token_work_units(C, ref, kind):
+    if kind == "same":
+        cfg = cs.with_tokens(cs.CONFIGS[2], 4)
+        x1 = layer_input(ref, cs.with_tokens(cs.CONFIGS[2], 1))
+        x = np.ascontiguousarray(np.repeat(x1, 4, axis=0))
+    else:
+        cfg = cs.with_tokens(cs.CONFIGS[1], 4)
+        x = layer_input(ref, cfg)
+    _note("work units", kind)
+    W = _layer(C, cfg)
+    y_plain, _ = run_gpu(C, W, x, taps=False)
+    y, taps = run_gpu(C, W, x)
+    np.testing.assert_array_equal(y_plain, y)
+    if kind == "same":  # every token's output equals the others'
+        for t in range(1, 4):
+            np.testing.assert_array_equal(y[t], y[0])
+    OL = oracle_layer_for(ref, cfg, 0, x)
+    err, flips = compare(ref, cfg, OL, x, y, taps, list(range(4)))
+    _note("rel_l2", err, "flips", flips)
+    assert flips == 0
+    assert err <= TOL_REL_L2
+
+
 def test_accumulate_and_zero_tokens(C, ref):
     cfg = cs.CONFIGS[0]
     _note("accumulate")
