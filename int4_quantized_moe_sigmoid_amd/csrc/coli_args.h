@@ -71,6 +71,7 @@ struct PfArgs {
     const int32_t* item_s0;
     const int32_t* item_n;
     const int32_t* n_items;
+    const int32_t* offs;   // [E + S + 1] first slot of each expert (its items follow it)
     const int32_t* slot_tok;
     int8_t* qh;            // [slots, I]
     float* dh;             // [slots, I/32]

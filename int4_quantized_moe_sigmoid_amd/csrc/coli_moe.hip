@@ -281,7 +281,7 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
         pa.eq = w->experts_q; pa.es = w->experts_scale; pa.blob_q = blob_q; pa.blob_s = blob_s;
         pa.H = H; pa.I = I; pa.qx = qx; pa.dx = dx;
         pa.item_e = it.item_e; pa.item_s0 = it.item_s0; pa.item_n = it.item_n;
-        pa.n_items = it.n_items; pa.slot_tok = slot_tok;
+        pa.n_items = it.n_items; pa.offs = offs; pa.slot_tok = slot_tok;
         pa.qh = qh; pa.dh = dh; pa.ye = ye; pa.tap = tap;
         pa.tap_rows = (int)L.pub.tap_rows;
         pa.tap_stride = (int)(L.pub.tap_stride ? L.pub.tap_stride : 1);

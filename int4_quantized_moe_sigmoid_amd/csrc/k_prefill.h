@@ -51,6 +51,35 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kSlots = 3;     // LDS ring: one stage computed, two loading
 
+// Work of a gate/up workgroup: item `it` and row tile `rt` (nrt tiles per
+// item). Workgroups go to the 8 XCDs in turn (block b to XCD b % 8, each XCD
+// taking its blocks in order), and each XCD has its own L2. The work list --
+// experts in ascending order, each one's items interleaved per row tile
+// ((i0, r0), (i1, r0), .., (i0, r1), ..) -- is cut into 8 equal runs, run x
+// going to XCD x, so the items of one expert ask for each weight tile at
+// about the same time on one XCD and one fill of its L2 serves them (the
+// expert's weights are fetched about once however many items it has). The
+// grid is a multiple of 8 of at least items x nrt blocks; false: no work for
+// this block.
+template <int KT>
+__device__ __forceinline__ bool work_of(const PfArgs& a, int nrt, int& it, int& rt) {
+    const int N = *a.n_items * nrt;
+    const int L = (N + 7) >> 3;
+    const int l = blockIdx.x >> 3;
+    const int p = (blockIdx.x & 7) * L + l;
+    if (l >= L || p >= N) return false;
+    // expert e owns positions nrt io .. nrt (io + m) - 1 of the list (io its
+    // first item, m its item count), so p / nrt is one of its items
+    const int i0 = p / nrt;
+    const int e = a.item_e[i0];
+    const int io = i0 - (a.item_s0[i0] - a.offs[e]) / KT;
+    const int m = (a.offs[e + 1] - a.offs[e] + KT - 1) / KT;
+    const int q = p - nrt * io;
+    rt = q / m;
+    it = io + (q - rt * m);
+    return true;
+}
+
 // Stage geometry of one weight width (2, 4 or 8 bits) and item size KT (32
 // or 64 tokens, in groups of 16; the host takes 64 when the routed experts
 // average 48 tokens or more). Kernels are instantiated for both sizes, since
@@ -422,8 +451,8 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
     __shared__ __align__(1024) uint8_t smem[kSlots * G::SLOT];
     static_assert(kSlots * G::SLOT >= KT * (kRows + 1) * 4, "h reuses the ring");
     const int nrt = a.I / kRows;
-    const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
-    if (it >= *a.n_items) return;
+    int it, rt;
+    if (!work_of<KT>(a, nrt, it, rt)) return;
     const int e = a.item_e[it], s0 = a.item_s0[it], n = a.item_n[it];
     const int H = a.H, I = a.I, BH = H >> 5;
     const int lane = threadIdx.x & 63;

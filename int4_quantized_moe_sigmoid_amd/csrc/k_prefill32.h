@@ -299,8 +299,8 @@ __global__ __launch_bounds__(256) void k_pf32_gateup(PfArgs a) {
     __shared__ __align__(1024) uint8_t smem[kSlots * G::SLOT];
     static_assert(kSlots * G::SLOT >= KT * (kRows32 + 1) * 4, "h reuses the ring");
     const int nrt = a.I / kRows32;
-    const int it = blockIdx.x / nrt, rt = blockIdx.x - it * nrt;
-    if (it >= *a.n_items) return;
+    int it, rt;
+    if (!work_of<KT>(a, nrt, it, rt)) return;
     const int e = a.item_e[it], s0 = a.item_s0[it], n = a.item_n[it];
     const int H = a.H, I = a.I, BH = H >> 5;
     const int lane = threadIdx.x & 63;

@@ -41,6 +41,10 @@ void launch_pf32_64(bool tap, dim3 g1, dim3 g2, const pf::PfArgs& pa, HS h_scale
     launch(mk, pf::k_pf_down<4, 64>, g2, 256, 0, s, pa);
 }
 
+// Grid of a gate/up kernel with nrt row tiles per item (pf::work_of): a
+// multiple of 8 blocks covering every (item, row tile) of up to n_it items.
+dim3 gateup_grid(int64_t nrt, int64_t n_it) { return dim3((unsigned)((nrt * n_it + 7) / 8 * 8)); }
+
 }  // namespace
 
 void launch_pf_path(const pf::PfArgs& pa, int bits, int kt, int64_t T, int64_t n_slots,
@@ -52,7 +56,7 @@ void launch_pf_path(const pf::PfArgs& pa, int bits, int kt, int64_t T, int64_t n
         launch(mk, pf::k_scale_int, (unsigned)((T + 3) / 4), 256, 0, s, pa.dx, T, H / 32,
                const_cast<int32_t*>(pa.mx), const_cast<int32_t*>(pa.ex));
     }
-    const dim3 g1((unsigned)((I / pf::kRows) * n_it));
+    const dim3 g1 = gateup_grid(I / pf::kRows, n_it);
     const dim3 g2((unsigned)(((H + pf::kDnRows - 1) / pf::kDnRows) * n_it));
     auto h_scales = [&] {
         if (!int_scales) return;
@@ -62,7 +66,7 @@ void launch_pf_path(const pf::PfArgs& pa, int bits, int kt, int64_t T, int64_t n
     };
     const bool tap = pa.tap != nullptr;
     if (bits == 4 && kt == 64 && I % pf::kRows32 == 0) {
-        const dim3 h1((unsigned)((I / pf::kRows32) * n_it));
+        const dim3 h1 = gateup_grid(I / pf::kRows32, n_it);
         launch_pf32_64(tap, h1, g2, pa, h_scales, s, mk);
     } else if (bits == 4) launch_pf<4>(kt, tap, g1, g2, pa, h_scales, s, mk);
     else if (bits == 8) launch_pf<8>(kt, tap, g1, g2, pa, h_scales, s, mk);

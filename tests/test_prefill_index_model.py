@@ -19,6 +19,13 @@ no multiple of the stage) the model checks that
 The formulas are those of the kernels' Plan/Plan32 init and issue and the
 lane bases of mm_loop/mm_loop32, transcribed; the GPU parity tests check the
 kernels' results end to end.
+
+It also models work_of, the XCD-aware order of the gate/up workgroups: over
+the items the bucketing makes (each expert's tokens cut into chunks of the
+item size, experts in ascending order) every (item, row tile) is taken by
+exactly one block of the launch grid, whatever upper bound on the items the
+grid was sized for, and each XCD's run holds an expert's items side by side
+per row tile.
 """
 import itertools
 
@@ -322,3 +329,72 @@ def test_integer_block_scales_are_exact():
         exact = sum(Fraction(d) * I for d, I in zip(ds, dots))
         assert Fraction(sum(m * I for m, I in zip(ms, dots))) * Fraction(2) ** e0 == exact
         assert abs(sum(m * I for m, I in zip(ms, dots))) < 2 ** 63
+
+
+def bucket_items(counts, ch):
+    """The items of k_bucket_scan, (expert, first slot, n) in expert order, and
+    the slot offsets (expert e owns slots offs[e] .. offs[e + 1] - 1)."""
+    offs, items, o = [], [], 0
+    for e, c in enumerate(counts):
+        offs.append(o)
+        for j in range((c + ch - 1) // ch):
+            items.append((e, o + j * ch, min(ch, c - j * ch)))
+        o += c
+    offs.append(o)
+    return items, offs
+
+
+def work_of(b, n_items, nrt, items, offs, kt):
+    N = n_items * nrt
+    L = (N + 7) >> 3
+    l = b >> 3
+    p = (b & 7) * L + l
+    if l >= L or p >= N:
+        return None
+    i0 = p // nrt
+    e = items[i0][0]
+    io = i0 - (items[i0][1] - offs[e]) // kt
+    m = (offs[e + 1] - offs[e] + kt - 1) // kt
+    q = p - nrt * io
+    rt = q // m
+    return io + (q - rt * m), rt
+
+
+WORK_CASES = [
+    # (tokens per expert, routed then shared; item size; row tiles per item)
+    ([3, 0, 40, 1, 64, 65, 0, 7], 32, 32),
+    ([0] * 255 + [1, 512], 32, 32),
+    ([128] * 16 + [4096], 64, 16),
+    ([33] * 5 + [0, 2], 32, 3),
+    ([1], 32, 1),
+    ([0, 0, 5], 64, 7),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WORK_CASES)))
+def test_xcd_work_order_covers_every_item_and_tile_once(case):
+    counts, kt, nrt = WORK_CASES[case]
+    items, offs = bucket_items(counts, kt)
+    n = len(items)
+    for n_max in (n, n + 5):  # the host sizes the grid for an upper bound
+        grid = (nrt * n_max + 7) // 8 * 8
+        seen = {}
+        for b in range(grid):
+            w = work_of(b, n, nrt, items, offs, kt)
+            if w is None:
+                continue
+            it, rt = w
+            assert 0 <= it < n and 0 <= rt < nrt
+            assert w not in seen, (w, b, seen.get(w))
+            seen[w] = b
+        assert len(seen) == n * nrt
+        # per XCD in dispatch order: experts ascending; within an expert row
+        # tiles ascending, and its items side by side at each row tile
+        for x in range(8):
+            run = [work_of(b, n, nrt, items, offs, kt) for b in range(x, grid, 8)]
+            run = [w for w in run if w is not None]
+            for (i1, r1), (i2, r2) in zip(run, run[1:]):
+                e1, e2 = items[i1][0], items[i2][0]
+                assert e1 <= e2
+                if e1 == e2:
+                    assert (r1, i1) < (r2, i2)
