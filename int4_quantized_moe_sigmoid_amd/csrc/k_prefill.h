@@ -467,6 +467,16 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
     const uint8_t* const tiles[2] = {gate + (int64_t)r0 * rowb, up + (int64_t)r0 * rowb};
     const int nrow[2] = {16, 16};
     const int32_t* rows_of = a.slot_tok + s0;  // token of each of the item's slots
+    // the row scales of this lane's results, loaded before the K loop so that
+    // the epilogue does not wait for them
+    const float* gs = a.es + (int64_t)e * a.blob_s;
+    const float* us = gs + I;
+    float gsr[4], usr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        gsr[i] = gs[r0 + 4 * q + i];
+        usr[i] = us[r0 + 4 * q + i];
+    }
     // integer scales unless the call has none (few tokens) or a token of the
     // item has none
     bool wide = a.ex == nullptr;
@@ -503,41 +513,53 @@ __global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
     __syncthreads();  // the ring is reused for h below
     float (*hbuf)[kRows + 1] = reinterpret_cast<float (*)[kRows + 1]>(smem);
 
-    // SwiGLU, then Q8_0 over each 32 consecutive h rows of a token
-    const float* gs = a.es + (int64_t)e * a.blob_s;
-    const float* us = gs + I;
+    // SwiGLU (token groups that hold tokens only), then Q8_0 over each 32
+    // consecutive h rows of a token
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = r0 + 4 * q + i;
-        const float gsr = gs[r], usr = us[r];
 #pragma unroll
         for (int g = 0; g < kMaxG; ++g) {
+            if (16 * g >= n) continue;  // uniform
             // the sums carry the multiplier of the weight codes: scale it away (exact)
-            const float gv = (float)((double)gsr * (acc[0][g][i] * G::InvScale));
-            const float uv = (float)((double)usr * (acc[1][g][i] * G::InvScale));
+            const float gv = (float)((double)gsr[i] * (acc[0][g][i] * G::InvScale));
+            const float uv = (float)((double)usr[i] * (acc[1][g][i] * G::InvScale));
             hbuf[16 * g + lr][wave * 16 + 4 * q + i] = swiglu_f32(gv, uv);
         }
     }
     __syncthreads();
-    if ((int)threadIdx.x < 2 * n) {
-        const int j = threadIdx.x >> 1, kb = threadIdx.x & 1;
+    // P consecutive threads per 32-row block of a token, each taking VPT of
+    // its bytes (in the activation order of the down weights' width); the
+    // block's amax is the maximum over the P threads
+    constexpr int P = 256 / (2 * KT), VPT = 32 / P;
+    static_assert(P == 2 || P == 4, "threads per h block");
+    if ((int)threadIdx.x < 2 * P * n) {
+        const int j = threadIdx.x / (2 * P), kb = (threadIdx.x / P) & 1, sp = threadIdx.x % P;
         const float* hv = &hbuf[j][32 * kb];
         float amax = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(hv[k]));
-        const float d = amax / 127.0f;
-        uint32_t w[8];
+        for (int k = 0; k < VPT; ++k)
+            amax = fmaxf(amax, fabsf(hv[act_elem<G::Layout>(VPT * sp + k)]));
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            w[i] = pack4_i8(q8_code(hv[act_elem<G::Layout>(4 * i)], d),
-                            q8_code(hv[act_elem<G::Layout>(4 * i + 1)], d),
-                            q8_code(hv[act_elem<G::Layout>(4 * i + 2)], d),
-                            q8_code(hv[act_elem<G::Layout>(4 * i + 3)], d));
-        typedef unsigned v4u __attribute__((ext_vector_type(4)));
-        v4u* o = reinterpret_cast<v4u*>(a.qh + (int64_t)(s0 + j) * I + rt * kRows + 32 * kb);
-        o[0] = v4u{w[0], w[1], w[2], w[3]};
-        o[1] = v4u{w[4], w[5], w[6], w[7]};
-        a.dh[(int64_t)(s0 + j) * (I >> 5) + rt * 2 + kb] = d;
+        for (int o = 1; o < P; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float d = amax / 127.0f;
+        uint32_t w[VPT / 4];
+#pragma unroll
+        for (int i = 0; i < VPT / 4; ++i) {
+            const int p0 = VPT * sp + 4 * i;
+            w[i] = pack4_i8(q8_code(hv[act_elem<G::Layout>(p0)], d),
+                            q8_code(hv[act_elem<G::Layout>(p0 + 1)], d),
+                            q8_code(hv[act_elem<G::Layout>(p0 + 2)], d),
+                            q8_code(hv[act_elem<G::Layout>(p0 + 3)], d));
+        }
+        int8_t* o = a.qh + (int64_t)(s0 + j) * I + rt * kRows + 32 * kb + VPT * sp;
+        if constexpr (VPT == 8) {
+            typedef unsigned v2u __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<v2u*>(o) = v2u{w[0], w[1]};
+        } else {
+            typedef unsigned v4u __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<v4u*>(o) = v4u{w[0], w[1], w[2], w[3]};
+        }
+        if (sp == 0) a.dh[(int64_t)(s0 + j) * (I >> 5) + rt * 2 + kb] = d;
     }
 }
 
