@@ -236,10 +236,14 @@ struct Plan {
     static constexpr int AIW = G::aiw(NG);
     static constexpr int TPI = 64 / G::CH;         // tokens per scale load
     static constexpr int LD = G::WINSTR + AIW + 1;  // loads per wave and stage (with scales)
-    // the waves' scale loads cover the item's tokens (with 32-token items
-    // waves 0 and 1 load them all and waves 2 and 3 none: those waves wait
-    // on one load fewer per stage)
+    // The block scales of a stage: when a row's block count is a multiple of
+    // CH, wave 0 loads them all with one 16-byte load per token (lane j: the
+    // CH scales of token j, lanes past the item size idle); else the waves'
+    // 4-byte loads cover the item's tokens (with 32-token items waves 0 and
+    // 1 load them all and waves 2 and 3 none). Waves without a scale load
+    // wait on one load fewer per stage.
     static_assert(4 * TPI >= G::kTok && G::kTok % TPI == 0, "scale loads");
+    static_assert(G::CH * 4 == 16 && G::kTok <= 64, "one 16-byte scale load per token");
     static_assert(4 * AIW * G::ARPI >= 16 * NG && 4 * AIW * G::ARPI <= G::kTok, "activation loads");
     const uint8_t* wrow[G::WINSTR];  // this lane's weight row
     int wpo[G::WINSTR];              // byte offset of its piece in the stage
@@ -252,6 +256,7 @@ struct Plan {
     int NB;                          // blocks per row
     int wave;
     bool scl;                        // this wave loads block scales
+    bool sx4;                        // ... with one 16-byte load per token
 
     // tile[t]: row 0 of tile t (16 rows, `rowb` bytes apart, rows from
     // nrow[t] on clamped to its last); rows_of[j]: activation row of token j
@@ -280,10 +285,19 @@ struct Plan {
             arow[i] = act + (int64_t)rows_of[min(j, n - 1)] * arowb_;
             apo[i] = piece * 16;
         }
-        scl = wave * TPI < G::kTok;
-        const int js = min(wave * TPI, G::kTok - TPI) + lane / G::CH;
-        sbk = (lane % G::CH) ^ skey<G::CH>(js);
-        srow = static_cast<const uint8_t*>(scales) + (int64_t)rows_of[min(js, n - 1)] * NB_ * 4;
+        sx4 = NB_ % G::CH == 0;
+        if (sx4) {
+            scl = wave == 0;
+            sbk = 0;
+            srow = static_cast<const uint8_t*>(scales) +
+                   (int64_t)rows_of[min(lane, n - 1)] * NB_ * 4;
+        } else {
+            scl = wave * TPI < G::kTok;
+            const int js = min(wave * TPI, G::kTok - TPI) + lane / G::CH;
+            sbk = (lane % G::CH) ^ skey<G::CH>(js);
+            srow = static_cast<const uint8_t*>(scales) +
+                   (int64_t)rows_of[min(js, n - 1)] * NB_ * 4;
+        }
     }
     // Issues the stage's loads into the slot at LDS address `slot`. Pieces
     // past a row's end are clamped to its last piece; their blocks read
@@ -298,9 +312,16 @@ struct Plan {
         for (int i = 0; i < AIW; ++i)
             dma_b128(arow[i] + min(c * G::ARB + apo[i], arowb - 16), adst + i * 1024);
         if (scl) {
-            const int b = c * G::CH + sbk;
-            dma_b32(b < NB ? static_cast<const void*>(srow + 4 * b) : &kZeroScale,
-                    slot + G::D_OFF + wave * TPI * G::CH * 4);
+            if (sx4) {
+                // token j's scales land at D_OFF + 16 j, the layout of the
+                // 4-byte loads (the swizzle key is 0 with 4-block stages)
+                if ((int)(threadIdx.x & 63) < G::kTok)
+                    dma_b128(srow + 4 * c * G::CH, slot + G::D_OFF);
+            } else {
+                const int b = c * G::CH + sbk;
+                dma_b32(b < NB ? static_cast<const void*>(srow + 4 * b) : &kZeroScale,
+                        slot + G::D_OFF + wave * TPI * G::CH * 4);
+            }
         }
     }
 };

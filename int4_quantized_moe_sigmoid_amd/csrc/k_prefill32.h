@@ -92,7 +92,9 @@ __device__ __forceinline__ v4i a_op32(const uint8_t* p) {
 // Per-lane load plan of one wave for a stage (see k_prefill.h Plan): WINSTR
 // weight loads (rows 16 i + lane / 4 of the wave's 64; rows 0..31 tile 0,
 // 32..63 tile 1), AIW activation loads and SIW scale loads for the waves that
-// have them.
+// have them. With 4-block stages and a block count that is a multiple of 4,
+// wave 0 loads the stage's scales with one 16-byte load per token instead
+// (lane j: token j's four scales, at the same LDS bytes).
 template <int BITS, int KT>
 struct Plan32 {
     typedef Geo32<BITS, KT> G;
@@ -107,6 +109,7 @@ struct Plan32 {
     int NB;
     int wave;
     bool act, scl;   // this wave loads activation rows / block scales
+    bool sx4;        // ... scales with one 16-byte load per token
 
     __device__ __forceinline__ void init(const uint8_t* const (&tile)[2], const int (&nrow)[2],
                                          int64_t rowb_, const int8_t* act_, int64_t arowb_,
@@ -133,6 +136,15 @@ struct Plan32 {
             arow[i] = act_ + (int64_t)rows_of[min(j, n - 1)] * arowb_;
             apo[i] = piece * 16;
         }
+        sx4 = G::CH == 4 && NB_ % 4 == 0;
+        if (sx4) {
+            static_assert(G::CH != 4 || (G::SIW == 1 && KT <= 64), "one 16-byte scale load");
+            scl = wave == 0;
+            sbk[0] = 0;
+            srow[0] = static_cast<const uint8_t*>(scales) +
+                      (int64_t)rows_of[min(lane, n - 1)] * NB_ * 4;
+            return;
+        }
         scl = wave * G::SIW < G::SINSTR;
 #pragma unroll
         for (int i = 0; i < G::SIW; ++i) {
@@ -154,7 +166,9 @@ struct Plan32 {
             for (int i = 0; i < G::AIW; ++i)
                 dma_b128(arow[i] + min(c * G::ARB + apo[i], arowb - 16), adst + i * 1024);
         }
-        if (scl) {
+        if (scl && sx4) {
+            if ((int)(threadIdx.x & 63) < KT) dma_b128(srow[0] + 16 * c, slot + G::D_OFF);
+        } else if (scl) {
 #pragma unroll
             for (int i = 0; i < G::SIW; ++i) {
                 const int b = c * G::CH + sbk[i];

@@ -124,7 +124,15 @@ def stage_map(form, bits, kt, ng, c, nrow, n, NB, rowb, arowb):
                 for k in range(16):
                     put(base + k, ("a", rows_of[min(j, n - 1)], gofs + k))
         # block scales
-        if form == 16:
+        if form == 16 and NB % g["CH"] == 0:
+            # one 16-byte load per token by wave 0 (lane j: token j's CH
+            # scales of the stage), lanes past the item size idle
+            if wave == 0 and lane < kt:
+                tok = rows_of[min(lane, n - 1)]
+                for bk in range(g["CH"]):
+                    for k in range(4):
+                        put(g["D_OFF"] + 16 * lane + 4 * bk + k, ("s", tok, c * g["CH"] + bk, k))
+        elif form == 16:
             TPI = 64 // g["CH"]
             if wave * TPI < kt:
                 js = min(wave * TPI, kt - TPI) + lane // g["CH"]
@@ -133,6 +141,13 @@ def stage_map(form, bits, kt, ng, c, nrow, n, NB, rowb, arowb):
                 src = ("s", rows_of[min(js, n - 1)], b) if b < NB else ZERO
                 for k in range(4):
                     put(g["D_OFF"] + wave * TPI * g["CH"] * 4 + 4 * lane + k, src + (k,))
+        elif g["CH"] == 4 and NB % 4 == 0:
+            # 32x32 form, int4: one 16-byte load per token by wave 0
+            if wave == 0 and lane < kt:
+                tok = rows_of[min(lane, n - 1)]
+                for bk in range(4):
+                    for k in range(4):
+                        put(g["D_OFF"] + 16 * lane + 4 * bk + k, ("s", tok, c * 4 + bk, k))
         else:
             if wave * g["SIW"] < g["SINSTR"]:
                 for i in range(g["SIW"]):
