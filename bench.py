@@ -47,10 +47,10 @@ TRAFFIC = {
     # profiles/dec_kernels_mtp_verify_T3.txt (mean over the counter run's steps)
     ("dec_gateup", "mtp-verify T3 correlated"): (95841.8 * 2 + 103.2) * 1024,
     # profiles/pf_kernels_prefill_T512.txt, profiles/pf_kernels_prefill_T512_int8.txt
-    ("pf_gateup", "prefill T512 zipf-bias"): (1655972.6 * 2 + 14214.5) * 1024,
-    ("pf_gateup", "prefill T512 zipf-bias int8 weights"): (3238032.8 * 2 + 12925.3) * 1024,
+    ("pf_gateup", "prefill T512 zipf-bias"): (1661012.2 * 2 + 14304.2) * 1024,
+    ("pf_gateup", "prefill T512 zipf-bias int8 weights"): (3234193.0 * 2 + 13049.4) * 1024,
     # profiles/pf_kernels_stack_T4096.txt (k_pf32_gateup, per layer)
-    ("pf_gateup", "stack8 T4096 uniform"): (2755868.0 * 2 + 96007.4) * 1024,
+    ("pf_gateup", "stack8 T4096 uniform"): (2743552.1 * 2 + 96107.1) * 1024,
     # profiles/pack_fp8_int4_layer.txt (the gate/up launch)
     ("pack_fp8_gateup", "pack_fp8 layer H6144 I2048 experts257"): (3164334.8 * 2 + 3166240.7) * 1024,
 }
