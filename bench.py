@@ -29,15 +29,15 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 
-# HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE (two runs), scaled by what the counters read for a plain device
-# copy of known size (FETCH_SIZE x 2, WRITE_SIZE x 1). Keyed by (kernel,
-# workload as the JSON line names it); dropped whenever that kernel changes.
 # int8 MFMA + exact int64 per-block epilogue at 2 waves per SIMD (the grouped
 # gate/up kernel's occupancy), as a fraction of 5.0 POP/s: bench.py --op
 # mfma_ceiling, profiles/mfma_epilogue_ceiling.txt
 EPILOGUE_CEILING = 0.300
 
+# HBM bytes per launch of the dominant kernel from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (two runs), scaled by what the counters read for a plain device
+# copy of known size (FETCH_SIZE x 2, WRITE_SIZE x 1). Keyed by (kernel,
+# workload as the JSON line names it); dropped whenever that kernel changes.
 TRAFFIC = {
     # profiles/dec_kernels_decode_T1.txt
     ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55669.1 * 2 + 38.4) * 1024,
