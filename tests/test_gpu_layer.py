@@ -144,9 +144,11 @@ def test_tiny_layer_token_counts(C, ref, n_tok):
 
 
 # every token at full size: decode (1 token), MTP verify at 2, 3 and 4
-# correlated tokens (the few-token kernels at each of their token counts) and
-# the 512-token prefill chunk (grouped MFMA kernels, every item tail)
-@pytest.mark.parametrize("cid,n_tok", [(1, 1), (2, 2), (2, 3), (2, 4), (3, 512)])
+# correlated tokens (the few-token kernels at each of their token counts), at
+# 5 and 6 (drafts of 4 and 5: the grouped MFMA kernels with the fp64 epilogue,
+# below the 16 tokens from which integer block scales are used) and the
+# 512-token prefill chunk (grouped MFMA kernels, every item tail)
+@pytest.mark.parametrize("cid,n_tok", [(1, 1), (2, 2), (2, 3), (2, 4), (2, 5), (2, 6), (3, 512)])
 def test_full_size_layers(C, ref, cid, n_tok):
     cfg = cs.with_tokens(cs.CONFIGS[cid], n_tok)
     _note(cfg.name, n_tok)
