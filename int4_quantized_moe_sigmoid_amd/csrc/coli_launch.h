@@ -54,6 +54,12 @@ inline int weight_bits(const coli_moe_cfg& c) { return c.weight_bits ? c.weight_
 bool small_path_fits(const coli_moe_cfg& c, int64_t T);
 void launch_small(const dec::DecArgs& a, int bits, hipStream_t s, Marks& mk);
 
+// Top-k of T tokens' logits with the few-token path's wave selection
+// (launch_decode.hip); E <= 256, K <= 16.
+void launch_topk_wave(const double* logits, const float* bias, int64_t T, int E, int K,
+                      int norm, double rho, GroupSel gsel, int32_t* idx, float* wts,
+                      hipStream_t s, Marks& mk);
+
 // Grouped int8-MFMA gate/up and down over n_it work items of kt (32 or 64)
 // tokens, with the integer block scales of x and h when pa.mx is set.
 void launch_pf_path(const pf::PfArgs& pa, int bits, int kt, int64_t T, int64_t n_slots,

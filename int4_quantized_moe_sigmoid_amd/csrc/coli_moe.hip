@@ -169,7 +169,9 @@ void launch_route(const coli_moe_cfg& c, const float* x, const float* wr, const 
     const GroupSel gsel = group_sel(c);
     // with groups, each wave stages its token's biased scores in LDS
     const size_t tk_lds = gsel.ng > 1 ? (size_t)4 * E * sizeof(double) : 0;
-    if (E <= 64)
+    if (E <= 256 && K <= 16)
+        launch_topk_wave(logits, bias, T, E, K, norm, rho, gsel, idx, wts, s, mk);
+    else if (E <= 64)
         launch(mk, k_topk<1>, gb, 256, tk_lds, s, logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);
     else if (E <= 128)
         launch(mk, k_topk<2>, gb, 256, tk_lds, s, logits, bias, (int)T, E, K, norm, rho, gsel, idx, wts);

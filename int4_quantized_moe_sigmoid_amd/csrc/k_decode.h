@@ -862,6 +862,46 @@ __global__ __launch_bounds__(256) void k_dec_router(DecArgs a) {
     }
 }
 
+// Sigmoid, correction bias and top-k for the many-token path (E <= 256,
+// K <= 16): one wave per token runs topk_wave, the few-token selection
+// (group maxima bound the K-th score from below; the experts at or above it
+// are compacted and ranked), on its token's s and c staged in LDS. It picks
+// the same experts in the same order, and sums and scales the same gates, as
+// K rounds of a wave arg-max would.
+__global__ __launch_bounds__(256) void k_topk_wave(const double* __restrict__ logits,
+                                                   const float* __restrict__ bias, int T, int E,
+                                                   int K, int norm, double rho, GroupSel gsel,
+                                                   int32_t* __restrict__ idx,
+                                                   float* __restrict__ wout) {
+    __shared__ TopkScratch Z;
+    __shared__ Route R;
+    __shared__ double sc[2][kMaxTok][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;  // the whole wave; no workgroup barrier follows
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E) {
+            const double l = logits[(int64_t)t * E + e];
+            const double sg = 1.0 / (1.0 + exp(-l));
+            sc[0][wave][e] = sg;
+            sc[1][wave][e] = sg + (double)bias[e];
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    topk_wave<false>(sc[0][wave], sc[1][wave], E, K, 0, norm, rho, gsel, R, Z, wave);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < K) {
+        idx[(int64_t)t * K + lane] = R.idx[wave][lane];
+        wout[(int64_t)t * K + lane] = R.w[wave][lane];
+    }
+}
+
 // B: blocks [0, S*nrb) shared-expert h-blocks, then (u, hb) for the u-th
 // expert in use (u < min(E, T*K)); block (u = 0, hb = 0) publishes routing.
 template <int NT, int NBJ, bool TAP, int BITS>

@@ -6,28 +6,45 @@
 
 // ---------------------------------------------------------------------------
 // Router logits for few tokens: one workgroup per expert row streams its
-// H floats once and dots them with every token (tokens come from L2).
+// H floats once and dots them with every token (tokens come from L2). The
+// row goes in chunks of kU float4 per thread; a chunk's loads (the row's and
+// every token slot's, clamped and unconditional) are all issued before its
+// arithmetic, so a 6144-wide row costs one round trip, not six.
 // ---------------------------------------------------------------------------
 template <int NT>
 __global__ __launch_bounds__(256) void k_router_gemv(const float* __restrict__ x,
                                                      const float* __restrict__ wr, int T, int H,
                                                      int E, double* __restrict__ logits) {
     __shared__ double red[NT][4];
+    constexpr int kU = 6;
     const int e = blockIdx.x;
     const float* wrow = wr + (int64_t)e * H;
     double acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0;
-    for (int h = threadIdx.x * 4; h < H; h += 1024) {
-        const float4 wv = *reinterpret_cast<const float4*>(wrow + h);
+    for (int h0 = threadIdx.x * 4; h0 < H; h0 += 1024 * kU) {
+        float4 wv[kU], xv[NT][kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+            wv[u] = *reinterpret_cast<const float4*>(wrow + min(h0 + 1024 * u, H - 4));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                xv[t][u] = *reinterpret_cast<const float4*>(
+                    x + (int64_t)min(t, T - 1) * H + min(h0 + 1024 * u, H - 4));
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             if (t < T) {
-                const float4 xv = *reinterpret_cast<const float4*>(x + (int64_t)t * H + h);
-                acc[t] += (double)xv.x * (double)wv.x;
-                acc[t] += (double)xv.y * (double)wv.y;
-                acc[t] += (double)xv.z * (double)wv.z;
-                acc[t] += (double)xv.w * (double)wv.w;
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    if (h0 + 1024 * u < H) {
+                        acc[t] += (double)xv[t][u].x * (double)wv[u].x;
+                        acc[t] += (double)xv[t][u].y * (double)wv[u].y;
+                        acc[t] += (double)xv[t][u].z * (double)wv[u].z;
+                        acc[t] += (double)xv[t][u].w * (double)wv[u].w;
+                    }
+                }
             }
         }
     }

@@ -56,6 +56,13 @@ void launch_small_bits(const dec::DecArgs& a, hipStream_t s, Marks& mk) {
     else launch_small_nt<4, BITS>(a, s, mk);
 }
 
+void launch_topk_wave(const double* logits, const float* bias, int64_t T, int E, int K,
+                      int norm, double rho, GroupSel gsel, int32_t* idx, float* wts,
+                      hipStream_t s, Marks& mk) {
+    launch(mk, dec::k_topk_wave, (unsigned)((T + 3) / 4), 256, 0, s, logits, bias, (int)T, E, K,
+           norm, rho, gsel, idx, wts);
+}
+
 void launch_small(const dec::DecArgs& a, int bits, hipStream_t s, Marks& mk) {
     if (bits == 8) launch_small_bits<8>(a, s, mk);
     else if (bits == 2) launch_small_bits<2>(a, s, mk);
