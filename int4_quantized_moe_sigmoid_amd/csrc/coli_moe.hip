@@ -515,7 +515,8 @@ COLI_API int coli_rmsnorm(const float* x, int64_t n_tok, int64_t dim, float eps,
     if (!x || !out) return COLI_E_INVAL;
     if (misaligned(x) || misaligned(out)) return COLI_E_ALIGN;
     if (n_tok > 0x7fffffffll) return COLI_E_UNSUPPORTED;
-    k_rmsnorm<<<(unsigned)n_tok, 256, 0, (hipStream_t)stream>>>(x, dim, (double)eps, out);
+    const int vec = dim % 4 == 0 && dim <= 8192;  // rows then 16-byte aligned too
+    k_rmsnorm<<<(unsigned)n_tok, 256, 0, (hipStream_t)stream>>>(x, dim, (double)eps, out, vec);
     return hip_status();
 }
 

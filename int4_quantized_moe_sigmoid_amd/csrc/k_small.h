@@ -121,22 +121,52 @@ __global__ __launch_bounds__(256) void k_pack_bits(const float* __restrict__ w, 
 }
 
 // RMSNorm with unit gain, one workgroup per token, sums in fp64.
+// vec: dim a multiple of 4 up to 1024 kV (x and out 16-byte aligned); the
+// row is then read once, as float4 loads all in flight together, and written
+// from registers (out may alias x: every read of the row precedes the
+// barrier, every write follows it).
 __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, int64_t dim, double eps,
-                                                 float* out) {
+                                                 float* out, int vec) {
+    constexpr int kV = 8;
     __shared__ double red[4];
     const int64_t t = blockIdx.x;
     const float* row = x + t * dim;
     double ss = 0.0;
-    for (int64_t i = threadIdx.x; i < dim; i += 256) {
-        const double v = (double)row[i];
-        ss += v * v;
+    float4 v[kV];
+    if (vec) {
+#pragma unroll
+        for (int u = 0; u < kV; ++u) {
+            const int64_t i = 4 * (int64_t)threadIdx.x + 1024 * u;
+            v[u] = (i < dim) ? *reinterpret_cast<const float4*>(row + i) : make_float4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < kV; ++u)
+            ss += (double)v[u].x * v[u].x + (double)v[u].y * v[u].y + (double)v[u].z * v[u].z +
+                  (double)v[u].w * v[u].w;
+    } else {
+        for (int64_t i = threadIdx.x; i < dim; i += 256) {
+            const double e = (double)row[i];
+            ss += e * e;
+        }
     }
     ss = wave_sum_f64(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     const double tot = (red[0] + red[1]) + (red[2] + red[3]);
     const double rms = sqrt(tot / (double)dim + eps);
-    for (int64_t i = threadIdx.x; i < dim; i += 256) out[t * dim + i] = (float)((double)row[i] / rms);
+    if (vec) {
+#pragma unroll
+        for (int u = 0; u < kV; ++u) {
+            const int64_t i = 4 * (int64_t)threadIdx.x + 1024 * u;
+            if (i < dim)
+                *reinterpret_cast<float4*>(out + t * dim + i) =
+                    make_float4((float)((double)v[u].x / rms), (float)((double)v[u].y / rms),
+                                (float)((double)v[u].z / rms), (float)((double)v[u].w / rms));
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < dim; i += 256)
+            out[t * dim + i] = (float)((double)row[i] / rms);
+    }
 }
 
 // Streaming read of n16 16-byte words (the HBM read ceiling the layer's
