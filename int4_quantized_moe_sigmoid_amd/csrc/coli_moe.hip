@@ -274,9 +274,9 @@ int forward_impl(const coli_moe_weights* w, const float* x, int64_t T, float* y,
     const int64_t n_it = max_items_for(c, T, ch);
     mk.mark("bucket_lists");
     launch(mk, k_bucket_lists, E + S, 256, 0, s, idx, (int)T, K, E, S, lists, counts);
-    mk.mark("bucket_scan");
-    launch(mk, k_bucket_scan, 1, 1024, 0, s, counts, lists, (int)T, K, E, S, ch, offs, slot_of,
-                                     slot_tok, it.item_e, it.item_s0, it.item_n, n_items);
+    mk.mark("bucket_fill");
+    launch(mk, k_bucket_fill, E + S, 256, 0, s, counts, lists, (int)T, K, E, S, ch, offs, slot_of,
+           slot_tok, it.item_e, it.item_s0, it.item_n, n_items);
 
     if (mfma) {
         pf::PfArgs pa{};

@@ -275,86 +275,58 @@ __global__ __launch_bounds__(256) void k_bucket_lists(const int32_t* __restrict_
     if (threadIdx.x == 0) counts[e] = base;
 }
 
-// In-place exclusive scan of n <= 4 * 1024 ints in LDS by a 1024-thread block;
-// returns the total.
-__device__ int block_exclusive_scan_1024(int* v, int n, int* part) {
-    const int tid = threadIdx.x;
-    int loc[4];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = tid * 4 + i;
-        loc[i] = (j < n) ? v[j] : 0;
-        sum += loc[i];
-    }
-    part[tid] = sum;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {
-        const int add = (tid >= o) ? part[tid - o] : 0;
-        __syncthreads();
-        part[tid] += add;
-        __syncthreads();
-    }
-    const int total = part[1023];
-    int run = part[tid] - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = tid * 4 + i;
-        if (j < n) v[j] = run;
-        run += loc[i];
-    }
-    __syncthreads();
-    return total;
-}
-
 // ---------------------------------------------------------------------------
-// Bucketing, step 2 (one 1024-thread workgroup): exclusive scan of the
-// per-expert counts into slot offsets, slot <-> (t, k) maps, and the work
-// items of the expert kernels: each expert's slots cut into chunks of <= CH
-// tokens (item = expert, first slot, count), experts in ascending order.
+// Bucketing, step 2 (one workgroup per expert, E + S in all): expert e's
+// first slot (the counts of the experts before it) and first item (their
+// item counts, ceil(count / CH)) as sums over the count array, exact in any
+// order; then its work items (expert, first slot, <= CH tokens) and, from its
+// list, the slot <-> (t, k) maps. Experts are in ascending order, so slots
+// and items follow expert order; the last workgroup writes the totals.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_bucket_scan(
+__global__ __launch_bounds__(256) void k_bucket_fill(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ lists, int T, int K, int E,
     int S, int CH, int32_t* __restrict__ offs, int32_t* __restrict__ slot_of,
     int32_t* __restrict__ slot_tok, int32_t* __restrict__ item_e, int32_t* __restrict__ item_s0,
     int32_t* __restrict__ item_n, int32_t* __restrict__ n_items) {
-    __shared__ int s_off[1040];
-    __shared__ int s_ioff[1040];
-    __shared__ int s_part[1024];
+    __shared__ int red[2][4];
     const int NE = E + S, KS = K + S;
-    const int tid = threadIdx.x;
-    for (int e = tid; e < NE; e += 1024) {
-        const int c = counts[e];
-        s_off[e] = c;
-        s_ioff[e] = (c + CH - 1) / CH;
+    const int e = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int so = 0, io = 0;
+    for (int f = threadIdx.x; f < e; f += 256) {
+        const int c = counts[f];
+        so += c;
+        io += (c + CH - 1) / CH;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        so += __shfl_xor(so, o, 64);
+        io += __shfl_xor(io, o, 64);
+    }
+    if (lane == 0) {
+        red[0][wave] = so;
+        red[1][wave] = io;
     }
     __syncthreads();
-    const int total = block_exclusive_scan_1024(s_off, NE, s_part);
-    const int total_items = block_exclusive_scan_1024(s_ioff, NE, s_part);
-    for (int e = tid; e < NE; e += 1024) offs[e] = s_off[e];
-    if (tid == 0) {
-        offs[NE] = total;
-        *n_items = total_items;
-    }
-    for (int e = tid; e < NE; e += 1024) {
-        const int c = counts[e];
-        const int ni = (c + CH - 1) / CH;
-        for (int j = 0; j < ni; ++j) {
-            const int it = s_ioff[e] + j;
-            item_e[it] = e;
-            item_s0[it] = s_off[e] + j * CH;
-            item_n[it] = min(CH, c - j * CH);
+    so = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    io = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    const int c = counts[e];
+    const int ni = (c + CH - 1) / CH;
+    if (threadIdx.x == 0) {
+        offs[e] = so;
+        if (e == NE - 1) {
+            offs[NE] = so + c;
+            *n_items = io + ni;
         }
     }
-    for (int g = tid; g < total; g += 1024) {
-        int lo = 0, hi = NE - 1;  // last e with s_off[e] <= g owns slot g
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_off[mid] <= g) lo = mid; else hi = mid - 1;
-        }
-        const int pos = g - s_off[lo];
-        const int entry = lists[(int64_t)lo * T + pos];
-        slot_of[entry] = g;
-        slot_tok[g] = entry / KS;
+    for (int j = threadIdx.x; j < ni; j += 256) {
+        item_e[io + j] = e;
+        item_s0[io + j] = so + j * CH;
+        item_n[io + j] = min(CH, c - j * CH);
+    }
+    for (int p = threadIdx.x; p < c; p += 256) {
+        const int entry = lists[(int64_t)e * T + p];
+        slot_of[entry] = so + p;
+        slot_tok[so + p] = entry / KS;
     }
 }

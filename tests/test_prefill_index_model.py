@@ -347,7 +347,7 @@ def test_integer_block_scales_are_exact():
 
 
 def bucket_items(counts, ch):
-    """The items of k_bucket_scan, (expert, first slot, n) in expert order, and
+    """The items of k_bucket_fill, (expert, first slot, n) in expert order, and
     the slot offsets (expert e owns slots offs[e] .. offs[e + 1] - 1)."""
     offs, items, o = [], [], 0
     for e, c in enumerate(counts):
