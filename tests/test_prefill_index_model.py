@@ -25,7 +25,9 @@ the items the bucketing makes (each expert's tokens cut into chunks of the
 item size, experts in ascending order) every (item, row tile) is taken by
 exactly one block of the launch grid, whatever upper bound on the items the
 grid was sized for, and each XCD's run holds an expert's items side by side
-per row tile.
+per row tile; and k_bucket_fill, whose per-expert sums give the slot
+offsets, items and slot maps of an exclusive scan with a binary-search owner
+per slot.
 """
 import itertools
 
@@ -413,3 +415,62 @@ def test_xcd_work_order_covers_every_item_and_tile_once(case):
                 assert e1 <= e2
                 if e1 == e2:
                     assert (r1, i1) < (r2, i2)
+
+
+def bucket_fill(counts, lists, T, KS, ch):
+    """k_bucket_fill, transcribed: workgroup e sums the counts and item counts
+    of the experts before it, then writes its items and slot maps."""
+    NE = len(counts)
+    offs = [0] * (NE + 1)
+    items, slot_of, slot_tok = {}, {}, {}
+    n_items = 0
+    for e in range(NE):
+        so = sum(counts[:e])
+        io = sum((c + ch - 1) // ch for c in counts[:e])
+        c = counts[e]
+        ni = (c + ch - 1) // ch
+        offs[e] = so
+        if e == NE - 1:
+            offs[NE] = so + c
+            n_items = io + ni
+        for j in range(ni):
+            items[io + j] = (e, so + j * ch, min(ch, c - j * ch))
+        for p in range(c):
+            entry = lists[e][p]
+            slot_of[entry] = so + p
+            slot_tok[so + p] = entry // KS
+    return offs, [items[i] for i in range(n_items)], slot_of, slot_tok
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_bucket_fill_matches_the_scan_definition(seed):
+    import random
+    rng = random.Random(seed)
+    E, S = rng.choice([(16, 1), (256, 1), (5, 0), (64, 2)])
+    K = rng.randint(1, min(E, 8))
+    T = rng.choice([1, 3, 17, 300])
+    KS = K + S
+    ch = rng.choice([4, 32, 64])
+    # routing: K distinct experts per token; shared experts take every token
+    lists = [[] for _ in range(E + S)]
+    for t in range(T):
+        for k, e in enumerate(rng.sample(range(E), K)):
+            lists[e].append(t * KS + k)
+        for s in range(S):
+            lists[E + s].append(t * KS + K + s)
+    counts = [len(l) for l in lists]
+    offs, items, slot_of, slot_tok = bucket_fill(counts, lists, T, KS, ch)
+    # definition: exclusive scan of the counts; each slot's owner is the last
+    # expert whose offset is at or below it
+    scan = [0]
+    for c in counts:
+        scan.append(scan[-1] + c)
+    assert offs == scan
+    want_items = [(e, scan[e] + j * ch, min(ch, c - j * ch))
+                  for e, c in enumerate(counts) for j in range((c + ch - 1) // ch)]
+    assert items == want_items
+    for g in range(scan[-1]):
+        e = max(i for i in range(E + S) if scan[i] <= g and counts[i] > 0)
+        entry = lists[e][g - scan[e]]
+        assert slot_of[entry] == g and slot_tok[g] == entry // KS
+    assert sorted(slot_of) == sorted(x for l in lists for x in l)
