@@ -147,10 +147,12 @@ __global__ __launch_bounds__(256) void k_router_reduce(const double* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Sigmoid, correction bias and top-k: one wave per token, EPL candidates per
-// lane. K rounds of a wave arg-max under the total order (c desc, index asc);
-// lane k keeps the k-th choice. Gate values: unbiased sigmoid, normalised by
-// their sum (k ascending) when asked, times rho, rounded to fp32.
+// Sigmoid, correction bias and top-k for shapes beyond the wave selection of
+// k_topk_wave (more than 256 experts or K > 16): one wave per token, EPL
+// candidates per lane. K rounds of a wave arg-max under the total order (c
+// desc, index asc); lane k keeps the k-th choice. Gate values: unbiased
+// sigmoid, normalised by their sum (k ascending) when asked, times rho,
+// rounded to fp32.
 // ---------------------------------------------------------------------------
 template <int EPL>
 __global__ __launch_bounds__(256) void k_topk(const double* __restrict__ logits,
