@@ -91,13 +91,34 @@ __global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b) acc[a][b] = v4d{0.0, 0.0, 0.0, 0.0};
-    for (int k0 = kbeg; k0 < kbeg + kper; k0 += kRouterK) {
+    // this thread's two float4 of each operand chunk: rows li >> 3, columns
+    // 4 (li & 7) of the 64 x 32 tile; the next chunk is requested right after
+    // the current one is staged (unconditionally: the last chunk is requested
+    // again at the end), so its latency overlaps the MFMA work
+    const int kend = kbeg + kper;
+    const float* xrow[2];
+    const float* wrow[2];
+    bool xok[2], wok[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int li = tid * 2 + i, row = li >> 3, c4 = li & 7;
+        xok[i] = t0 + row < T;
+        wok[i] = e0 + row < E;
+        xrow[i] = x + (int64_t)min(t0 + row, T - 1) * H + c4 * 4;
+        wrow[i] = wr + (int64_t)min(e0 + row, E - 1) * H + c4 * 4;
+    }
+    float4 nv[2], nw[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        nv[i] = *reinterpret_cast<const float4*>(xrow[i] + kbeg);
+        nw[i] = *reinterpret_cast<const float4*>(wrow[i] + kbeg);
+    }
+    for (int k0 = kbeg; k0 < kend; k0 += kRouterK) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int li = tid * 2 + i, row = li >> 3, c4 = li & 7;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f), w = v;
-            if (t0 + row < T) v = *reinterpret_cast<const float4*>(x + (int64_t)(t0 + row) * H + k0 + c4 * 4);
-            if (e0 + row < E) w = *reinterpret_cast<const float4*>(wr + (int64_t)(e0 + row) * H + k0 + c4 * 4);
+            const float4 v = xok[i] ? nv[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 w = wok[i] ? nw[i] : make_float4(0.f, 0.f, 0.f, 0.f);
             xs[row][c4 * 4 + 0] = v.x;
             xs[row][c4 * 4 + 1] = v.y;
             xs[row][c4 * 4 + 2] = v.z;
@@ -108,6 +129,12 @@ __global__ __launch_bounds__(256) void k_router_gemm(const float* __restrict__ x
             ws[row][c4 * 4 + 3] = w.w;
         }
         __syncthreads();
+        const int kn = min(k0 + kRouterK, kend - kRouterK);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            nv[i] = *reinterpret_cast<const float4*>(xrow[i] + kn);
+            nw[i] = *reinterpret_cast<const float4*>(wrow[i] + kn);
+        }
 #pragma unroll
         for (int k = 0; k < kRouterK; k += 4) {
             double av[2], bv[2];
