@@ -132,11 +132,11 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
 }
 
 // Router + top-k into ws (shared by coli_moe_route and coli_moe_forward).
-// Slices of the hidden dimension for the many-token router GEMM: enough
-// workgroups to cover the GPU (~512), each slice a multiple of 32.
+// Slices of the hidden dimension for the many-token router GEMM: about 1024
+// workgroups (four per CU), each slice a multiple of 32.
 int router_ksplit(int H, int64_t T, int E) {
     const int64_t tiles = ((T + kRouterTile - 1) / kRouterTile) * ((E + kRouterTile - 1) / kRouterTile);
-    int ks = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxRouterSplit, 512 / std::max<int64_t>(tiles, 1)));
+    int ks = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxRouterSplit, 1024 / std::max<int64_t>(tiles, 1)));
     while (ks > 1 && H % (kRouterK * ks) != 0) --ks;
     return ks;
 }
