@@ -42,8 +42,8 @@ TRAFFIC = {
     # profiles/dec_kernels_decode_T1.txt
     ("dec_gateup", "decode T1 H6144 E256 K8 I2048"): (55669.1 * 2 + 38.4) * 1024,
     # profiles/dec_kernels_decode_T1_int8.txt, profiles/dec_kernels_decode_T1_int2.txt
-    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int8 weights"): (111687.3 * 2 + 38.4) * 1024,
-    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int2 weights"): (28007.7 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int8 weights"): (111685.5 * 2 + 38.4) * 1024,
+    ("dec_gateup", "decode T1 H6144 E256 K8 I2048 int2 weights"): (27999.9 * 2 + 38.4) * 1024,
     # profiles/dec_kernels_mtp_verify_T3.txt (mean over the counter run's steps)
     ("dec_gateup", "mtp-verify T3 correlated"): (95841.8 * 2 + 103.2) * 1024,
     # profiles/pf_kernels_prefill_T512.txt, profiles/pf_kernels_prefill_T512_int8.txt
