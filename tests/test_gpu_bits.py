@@ -3,7 +3,8 @@ layer: the fused few-token kernels up to four tokens, the grouped MFMA
 kernels above): packing bit-exact; Q8_0(x) codes in each width's element
 order, per-block gate dots bit-exact through the debug tap; Q8_0(h) codes
 equal; outputs within 1e-4 rel-L2 of the oracle (tiny workload on every
-token; full decode, MTP-verify and prefill shapes on sampled tokens)."""
+token, and on every token of layers whose experts take 64-token items; full
+decode, MTP-verify and prefill shapes on sampled tokens)."""
 import dataclasses
 
 import numpy as np
@@ -88,8 +89,9 @@ def _run(C, W, x):
         "tap_stride": int(L.tap_stride)}
 
 
-def _compare(ref, cfg, bits, x, y, taps, tokens):
-    OL = oracle_layer_for(ref, cfg, 0, x[tokens], bits=bits)
+def _compare(ref, cfg, bits, x, y, taps, tokens, OL=None, max_flips=None):
+    if OL is None:
+        OL = oracle_layer_for(ref, cfg, 0, x[tokens], bits=bits)
     xs = x[tokens]
     yo, to = OL.forward(xs, taps=True)
     np.testing.assert_array_equal(taps["qx"][tokens], to["qx"])
@@ -109,6 +111,8 @@ def _compare(ref, cfg, bits, x, y, taps, tokens):
     err = rel_l2(y[tokens], yo)
     _note("rel_l2", err, "q_h flips", flips)
     assert err <= TOL_REL_L2
+    if max_flips is not None:
+        assert flips <= max_flips
 
 
 @pytest.mark.parametrize("bits", [2, 8])
@@ -120,6 +124,72 @@ def test_tiny_layer_every_token(C, ref, bits, n_tok):
     x = layer_input(ref, cfg)
     y, taps = _run(C, W, x)
     _compare(ref, cfg, bits, x, y, taps, list(range(n_tok)))
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("shape", ["tiny T400", "mid T800"])
+def test_64_token_items_every_token(C, ref, bits, shape):
+    # routed experts averaging 48 tokens or more take 64-token items (the
+    # grouped kernels' KT = 64 instances at this width): every token against
+    # the oracle, and the untapped kernels bit for bit against the tapped ones
+    if shape == "tiny T400":  # 50 tokens per routed expert, 16-token tails
+        cfg = cs.with_tokens(cs.CONFIGS[0], 400)
+    else:  # zipf-skewed bias, 100 tokens per routed expert on average
+        cfg = dataclasses.replace(cs.CONFIGS[3], name="mid T800 H1024 E32 K4 I512", n_tok=800,
+                                  hidden=1024, n_experts=32, top_k=4, inter=512)
+    _note("items64", bits, cfg.name)
+    W = _layer(C, cfg, bits)
+    x = layer_input(ref, cfg)
+    y_plain = _run_plain(C, W, x)
+    y, taps = _run(C, W, x)
+    np.testing.assert_array_equal(y_plain, y)
+    _compare(ref, cfg, bits, x, y, taps, list(range(cfg.n_tok)))
+    del W
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bits", [2, 8])
+@pytest.mark.parametrize("n_tok", [40, 400])  # 32- and 64-token items
+def test_wide_scale_rows_take_the_fp64_epilogue(C, ref, bits, n_tok):
+    # Q8_0 block scales of one row spanning more than 2^7 have no 31-bit
+    # integer form, so such items take the fp64 epilogue: one block of input
+    # token 3 scaled by 1e-4 (x side), the shared expert's first 32 gate rows
+    # by 1e-5 (its h rows, down side); parity with the oracle on every token,
+    # with taps and without
+    cfg = dataclasses.replace(cs.CONFIGS[0], name=f"wide scales T{n_tok} H256 E16 K2 I128",
+                              n_tok=n_tok)
+    _note("wide", bits, cfg.name)
+    calls = [0]
+    shared_gate = 3 * cfg.n_experts  # build_layer packs gate, up, down of expert 0, 1, ...
+
+    def pack(w, qv, sv):
+        if calls[0] == shared_gate:
+            w[:32] *= np.float32(1e-5)
+        calls[0] += 1
+        C.coli_pack_weights(w, bits, qv, sv)
+    wr, b, q, s = cs.build_layer(cfg, 0, "cuda", pack, bits=bits)
+    W = C.LayerWeights(lib_cfg(C, cfg, bits=bits), wr, b, q, s)
+    x = layer_input(ref, cfg)
+    x[3, :32] *= np.float32(1e-4)
+    wro, bo = cs.router(cfg, 0, "cpu")
+    wro, bo = wro.numpy(), bo.numpy()
+    idx, _, _ = ref.route(x, wro, bo, cfg.top_k, cfg.norm_topk, cfg.rho)
+    OL = ref.OracleLayer(cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.n_shared,
+                         cfg.norm_topk, cfg.rho, wro, bo, {}, 1, 1, bits)
+    for e in sorted(set(int(v) for v in np.unique(idx)) | {cfg.n_experts}):
+        mats = [cs.expert_matrix(cfg, 0, e, m, "cpu").numpy().copy() for m in ("gate", "up", "down")]
+        if e == cfg.n_experts:
+            mats[0][:32] *= np.float32(1e-5)
+        OL.add_expert(e, ref.pack_expert(*mats, bits=bits))
+    y_plain = _run_plain(C, W, x)
+    y, taps = _run(C, W, x)
+    np.testing.assert_array_equal(y_plain, y)
+    # the scales really are wide: x of token 3, h of every shared slot
+    dx3 = taps["dx"][3]
+    assert dx3.max() / dx3[dx3 > 0].min() > 2.0 ** 8
+    dh = taps["dh"][taps["slot_of"][:, cfg.top_k]]
+    assert all(r.max() / r[r > 0].min() > 2.0 ** 8 for r in dh)
+    _compare(ref, cfg, bits, x, y, taps, list(range(n_tok)), OL=OL, max_flips=0)
 
 
 @pytest.mark.parametrize("bits", [2, 8])
