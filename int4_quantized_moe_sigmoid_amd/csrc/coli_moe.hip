@@ -31,6 +31,17 @@ constexpr int64_t kTapBudget = 1ll << 24;  // int32 entries of the block-dot tap
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Router GEMM partial sums: slices x tokens the split (router_ksplit) may use
+// at T tokens. The split is at most kMaxRouterSplit and, once it exceeds one,
+// at most 1024 / tiles with tiles >= (T / 64) ceil(E / 64), so slices x T <=
+// 65536 / ceil(E / 64); with one slice it is T. The bound never decreases as
+// T grows, and router_ksplit never exceeds it.
+int64_t router_part_slots(int64_t T, int E) {
+    const int64_t et = (E + kRouterTile - 1) / kRouterTile;
+    return std::min<int64_t>((int64_t)kMaxRouterSplit * T,
+                             std::max<int64_t>(T, 1024 * kRouterTile / et));
+}
+
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 int check_cfg(const coli_moe_cfg* c) {
@@ -102,7 +113,7 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
     L->items = take(3 * L->max_items * 4);
     L->n_items = take(4);
     L->uinfo = take(4 * (1 + 4 * dec::kMaxEntries + 64));
-    L->rpart = take(T > 8 ? (size_t)kMaxRouterSplit * T * E * 8 : 0);
+    L->rpart = take(T > 8 ? (size_t)router_part_slots(T, (int)E) * E * 8 : 0);
     // s and c of the few-token path; reserved for min(T, its token limit) at
     // every T so that the total never shrinks as T grows
     L->sig = take((size_t)2 * std::min<int64_t>(T, dec::kMaxTok) * E * 8);
@@ -137,6 +148,7 @@ void make_layout(const coli_moe_cfg& c, int64_t T, uint32_t flags, Layout* L) {
 int router_ksplit(int H, int64_t T, int E) {
     const int64_t tiles = ((T + kRouterTile - 1) / kRouterTile) * ((E + kRouterTile - 1) / kRouterTile);
     int ks = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxRouterSplit, 1024 / std::max<int64_t>(tiles, 1)));
+    while (ks > 1 && (int64_t)ks * T > router_part_slots(T, E)) --ks;  // the workspace holds these
     while (ks > 1 && H % (kRouterK * ks) != 0) --ks;
     return ks;
 }
