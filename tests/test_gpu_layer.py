@@ -167,6 +167,32 @@ def test_full_size_layers(C, ref, cid, n_tok):
     assert err <= TOL_REL_L2
 
 
+# decode at full size on many tokens: 24 one-token calls on consecutive tokens
+# of the decode input stream, each routed to its own experts (well over a
+# hundred of the 256 in all), through the kernels the bench times and the
+# tapped ones, every call against the oracle
+def test_decode_calls_on_many_tokens(C, ref):
+    n = 24
+    cfg1 = cs.with_tokens(cs.CONFIGS[1], 1)
+    cfgn = cs.with_tokens(cs.CONFIGS[1], n)
+    _note(cfgn.name, "one-token calls", n)
+    W = _layer(C, cfg1)
+    xs = layer_input(ref, cfgn)
+    OL = oracle_layer_for(ref, cfgn, 0, xs)  # every expert the n tokens select
+    used = set()
+    for t in range(n):
+        x = np.ascontiguousarray(xs[t:t + 1])
+        y_plain, _ = run_gpu(C, W, x, taps=False)
+        y, taps = run_gpu(C, W, x)
+        np.testing.assert_array_equal(y_plain, y)
+        err, flips = compare(ref, cfg1, OL, x, y, taps, [0])
+        assert flips == 0, (t, flips)
+        assert err <= TOL_REL_L2, (t, err)
+        used |= set(int(e) for e in taps["idx"][0])
+    _note("experts used", len(used))
+    assert len(used) > 100
+
+
 # the two ends of the several-token work split at full size (E256 K8, four
 # tokens): one token repeated four times (8 experts, each holding every token:
 # two work units each, one h-block per workgroup) and four independent tokens
