@@ -36,8 +36,8 @@ def _sample(ws, lay, cfg, rng):
     counts = _ws_i32(ws, lay.counts, E + S)
     offs = _ws_i32(ws, lay.offs, E + S + 1)
     slot_tok = _ws_i32(ws, lay.slot_tok, int(lay.n_slots))
-    toks = set(rng.choice(T, 4, replace=False).tolist()) | {0, T - 1}
-    for e in rng.choice(E, 5, replace=False):
+    toks = set(rng.choice(T, 48, replace=False).tolist()) | {0, T - 1}
+    for e in rng.choice(E, 8, replace=False):
         n = int(counts[e])
         if n == 0:
             continue
